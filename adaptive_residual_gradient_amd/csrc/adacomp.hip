@@ -1,0 +1,463 @@
+// C ABI of the AdaComp library (declared in include/adacomp.h): plan
+// management, argument checking and stream-ordered kernel launches.
+//
+// Method: "AdaComp (Adaptive Residual Gradient Compression)", AIMech curated
+// page, definition paragraph and Mechanism claim on local-bin soft threshold
+// and mean-g_max quantization (Algorithm 2); index word widths from its
+// Application claim (Table 2).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/adacomp.h"
+#include "kernels.hpp"
+#include "layout.hpp"
+
+using adacomp::Layout;
+using adacomp::SegDev;
+
+struct adacomp_plan {
+    Layout L;
+    int device = -1;
+    void* dmem = nullptr;
+    SegDev* d_segs = nullptr;
+    uint32_t* d_tile_seg = nullptr;
+    uint32_t* d_vtiles[2] = {nullptr, nullptr};
+    uint32_t* d_chunk_tile_begin = nullptr;
+    uint32_t* d_chunk_seg = nullptr;
+    uint32_t tile_lds[2] = {0, 0};
+};
+
+struct adacomp_timer {
+    struct Rec {
+        int stage;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> recs;
+    double ms[ADACOMP_NUM_STAGES] = {};
+    uint64_t n[ADACOMP_NUM_STAGES] = {};
+};
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+Range range_of(const void* p, uint64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+int check_device(const adacomp_plan* plan) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return ADACOMP_ERR_HIP;
+    return dev == plan->device ? ADACOMP_OK : ADACOMP_ERR_INVALID_ARGUMENT;
+}
+
+// Records one stage's events around a group of launches.
+struct StageTimer {
+    adacomp_timer* t;
+    hipStream_t s;
+    hipEvent_t a = nullptr, b = nullptr;
+    int stage;
+    StageTimer(adacomp_timer* timer, hipStream_t stream, int st) : t(timer), s(stream), stage(st) {
+        if (!t) return;
+        if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+            t = nullptr;
+            return;
+        }
+        (void)hipEventRecord(a, s);
+    }
+    void stop() {
+        if (!t) return;
+        (void)hipEventRecord(b, s);
+        t->recs.push_back({stage, a, b});
+        t = nullptr;
+    }
+    ~StageTimer() {
+        if (!t) return;   // a launch failed before stop(): drop the events
+        (void)hipEventDestroy(a);
+        (void)hipEventDestroy(b);
+    }
+};
+
+int launch_status() {
+    return hipGetLastError() == hipSuccess ? ADACOMP_OK : ADACOMP_ERR_HIP;
+}
+
+struct DecodeLayout {
+    uint64_t status, dcnt, doff, dchunk_cnt, dchunk_base, dseg_s, dseg_eoff, dvalid, total;
+};
+
+DecodeLayout decode_layout(const Layout& L, uint32_t K) {
+    DecodeLayout d{};
+    uint64_t w = 0;
+    auto take = [&w](uint64_t bytes) {
+        const uint64_t at = w;
+        w = adacomp::round_up(w + bytes, adacomp::kAlign);
+        return at;
+    };
+    const uint64_t T = L.ntiles, C = L.nchunks, S = L.nseg;
+    d.status = take(4);
+    d.dcnt = take(4 * K * T);
+    d.doff = take(4 * K * T);
+    d.dchunk_cnt = take(4 * K * C);
+    d.dchunk_base = take(4 * K * C);
+    d.dseg_s = take(4 * K * S);
+    d.dseg_eoff = take(8 * K * S);
+    d.dvalid = take(4 * uint64_t(K));
+    d.total = w;
+    return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* adacomp_status_str(int status) {
+    switch (status) {
+        case ADACOMP_OK: return "ok";
+        case ADACOMP_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case ADACOMP_ERR_UNSUPPORTED_BIN: return "unsupported bin length (1..32768)";
+        case ADACOMP_ERR_MISALIGNED: return "misaligned segment offset or buffer";
+        case ADACOMP_ERR_OVERLAP: return "segments overlap";
+        case ADACOMP_ERR_CAPACITY: return "buffer smaller than the plan requires";
+        case ADACOMP_ERR_HIP: return "HIP runtime error";
+        case ADACOMP_ERR_TOO_LARGE: return "segment table too large";
+        default: return "unknown status";
+    }
+}
+
+int adacomp_plan_query(const adacomp_segment* segs, uint32_t nseg, adacomp_plan_info* info) {
+    if (info == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+    try {
+        Layout L;
+        const int st = adacomp::build_layout(segs, nseg, L);
+        if (st != ADACOMP_OK) return st;
+        adacomp::fill_info(L, info);
+        return ADACOMP_OK;
+    } catch (...) {
+        return ADACOMP_ERR_INVALID_ARGUMENT;
+    }
+}
+
+int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan** out) {
+    if (out == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+    *out = nullptr;
+    adacomp_plan* p = nullptr;
+    try {
+        p = new adacomp_plan();
+        int st = adacomp::build_layout(segs, nseg, p->L);
+        if (st != ADACOMP_OK) {
+            delete p;
+            return st;
+        }
+        const Layout& L = p->L;
+        // Launch limits: total work-items of one launch must fit in 32 bits.
+        if (L.tiles_by_variant[0].size() * uint64_t(adacomp::kSmallThreads) >= (uint64_t(1) << 32) ||
+            L.tiles_by_variant[1].size() * uint64_t(adacomp::kLargeThreads) >= (uint64_t(1) << 32) ||
+            L.ntiles * 256ull >= (uint64_t(1) << 32) || L.nchunks * 256ull >= (uint64_t(1) << 32)) {
+            delete p;
+            return ADACOMP_ERR_TOO_LARGE;
+        }
+        if (hipGetDevice(&p->device) != hipSuccess) {
+            delete p;
+            return ADACOMP_ERR_HIP;
+        }
+        const uint64_t b_segs = adacomp::round_up(sizeof(SegDev) * L.nseg, 256);
+        const uint64_t b_ts = adacomp::round_up(4 * L.ntiles, 256);
+        const uint64_t b_v0 = adacomp::round_up(4 * L.tiles_by_variant[0].size() + 4, 256);
+        const uint64_t b_v1 = adacomp::round_up(4 * L.tiles_by_variant[1].size() + 4, 256);
+        const uint64_t b_ctb = adacomp::round_up(4 * (L.nchunks + 1), 256);
+        const uint64_t b_cs = adacomp::round_up(4 * L.nchunks + 4, 256);
+        const uint64_t total = b_segs + b_ts + b_v0 + b_v1 + b_ctb + b_cs;
+        std::vector<uint8_t> host(total, 0);
+        uint64_t at = 0;
+        auto put = [&](const void* src, uint64_t bytes, uint64_t room) {
+            if (bytes) std::memcpy(host.data() + at, src, bytes);
+            const uint64_t here = at;
+            at += room;
+            return here;
+        };
+        const uint64_t o_segs = put(L.segs.data(), sizeof(SegDev) * L.nseg, b_segs);
+        const uint64_t o_ts = put(L.tile_seg.data(), 4 * L.ntiles, b_ts);
+        const uint64_t o_v0 = put(L.tiles_by_variant[0].data(), 4 * L.tiles_by_variant[0].size(), b_v0);
+        const uint64_t o_v1 = put(L.tiles_by_variant[1].data(), 4 * L.tiles_by_variant[1].size(), b_v1);
+        const uint64_t o_ctb = put(L.chunk_tile_begin.data(), 4 * (L.nchunks + 1), b_ctb);
+        const uint64_t o_cs = put(L.chunk_seg.data(), 4 * L.nchunks, b_cs);
+        if (hipMalloc(&p->dmem, total) != hipSuccess) {
+            delete p;
+            return ADACOMP_ERR_HIP;
+        }
+        if (hipMemcpy(p->dmem, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipFree(p->dmem);
+            delete p;
+            return ADACOMP_ERR_HIP;
+        }
+        uint8_t* base = static_cast<uint8_t*>(p->dmem);
+        p->d_segs = reinterpret_cast<SegDev*>(base + o_segs);
+        p->d_tile_seg = reinterpret_cast<uint32_t*>(base + o_ts);
+        p->d_vtiles[0] = reinterpret_cast<uint32_t*>(base + o_v0);
+        p->d_vtiles[1] = reinterpret_cast<uint32_t*>(base + o_v1);
+        p->d_chunk_tile_begin = reinterpret_cast<uint32_t*>(base + o_ctb);
+        p->d_chunk_seg = reinterpret_cast<uint32_t*>(base + o_cs);
+        for (int v = 0; v < 2; ++v) p->tile_lds[v] = (2 * L.max_bpt[v] + 1) * 4;
+        *out = p;
+        return ADACOMP_OK;
+    } catch (...) {
+        if (p) {
+            if (p->dmem) (void)hipFree(p->dmem);
+            delete p;
+        }
+        return ADACOMP_ERR_INVALID_ARGUMENT;
+    }
+}
+
+int adacomp_plan_destroy(adacomp_plan* plan) {
+    if (plan == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+    int st = ADACOMP_OK;
+    if (plan->dmem && hipFree(plan->dmem) != hipSuccess) st = ADACOMP_ERR_HIP;
+    delete plan;
+    return st;
+}
+
+int adacomp_plan_get_info(const adacomp_plan* plan, adacomp_plan_info* info) {
+    if (plan == nullptr || info == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+    adacomp::fill_info(plan->L, info);
+    return ADACOMP_OK;
+}
+
+int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float* dW,
+                           uint64_t n_elems, void* msg, uint64_t msg_bytes, void* ws,
+                           uint64_t ws_bytes, float* bin_max_out, void* stream_,
+                           adacomp_timer* timer) {
+    if (plan == nullptr || residue == nullptr || dW == nullptr || msg == nullptr || ws == nullptr)
+        return ADACOMP_ERR_INVALID_ARGUMENT;
+    const Layout& L = plan->L;
+    if (!aligned16(residue) || !aligned16(dW) || !aligned16(msg) || !aligned16(ws))
+        return ADACOMP_ERR_MISALIGNED;
+    if (bin_max_out != nullptr && (reinterpret_cast<uintptr_t>(bin_max_out) & 3u) != 0)
+        return ADACOMP_ERR_MISALIGNED;
+    if (n_elems < L.span || msg_bytes < L.capacity || ws_bytes < L.ws_compress)
+        return ADACOMP_ERR_CAPACITY;
+    {
+        std::vector<Range> r = {range_of(residue, 4 * L.span), range_of(dW, 4 * L.span),
+                                range_of(msg, L.capacity), range_of(ws, L.ws_compress)};
+        if (bin_max_out) r.push_back(range_of(bin_max_out, 4 * L.total_bins));
+        for (size_t i = 0; i < r.size(); ++i)
+            for (size_t j = i + 1; j < r.size(); ++j)
+                if (overlaps(r[i], r[j])) return ADACOMP_ERR_INVALID_ARGUMENT;
+    }
+    int st = check_device(plan);
+    if (st != ADACOMP_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+
+    uint8_t* w8 = static_cast<uint8_t*>(ws);
+    uint2* stage = reinterpret_cast<uint2*>(w8 + L.ws_stage);
+    uint32_t* tile_cnt = reinterpret_cast<uint32_t*>(w8 + L.ws_tile_cnt);
+    double* tile_gsum = reinterpret_cast<double*>(w8 + L.ws_tile_gsum);
+    uint32_t* tile_off = reinterpret_cast<uint32_t*>(w8 + L.ws_tile_off);
+    uint32_t* chunk_cnt = reinterpret_cast<uint32_t*>(w8 + L.ws_chunk_cnt);
+    double* chunk_gsum = reinterpret_cast<double*>(w8 + L.ws_chunk_gsum);
+    uint32_t* chunk_base = reinterpret_cast<uint32_t*>(w8 + L.ws_chunk_base);
+    float* seg_s = reinterpret_cast<float*>(w8 + L.ws_seg_s);
+    uint32_t* seg_nsurv = reinterpret_cast<uint32_t*>(w8 + L.ws_seg_nsurv);
+    uint64_t* seg_eoff = reinterpret_cast<uint64_t*>(w8 + L.ws_seg_eoff);
+    uint8_t* m8 = static_cast<uint8_t*>(msg);
+
+    {
+        StageTimer tm(timer, stream, ADACOMP_STAGE_TILE_PASS);
+        const uint32_t n0 = static_cast<uint32_t>(L.tiles_by_variant[0].size());
+        const uint32_t n1 = static_cast<uint32_t>(L.tiles_by_variant[1].size());
+        if (n0)
+            hipLaunchKernelGGL((adacomp::k_tile_pass<adacomp::kSmallThreads, adacomp::kSmallVecs>),
+                               dim3(n0), dim3(adacomp::kSmallThreads), plan->tile_lds[0], stream,
+                               plan->d_segs, plan->d_tile_seg, plan->d_vtiles[0], residue, dW, m8,
+                               stage, tile_cnt, tile_gsum, bin_max_out);
+        if ((st = launch_status()) != ADACOMP_OK) return st;
+        if (n1)
+            hipLaunchKernelGGL((adacomp::k_tile_pass<adacomp::kLargeThreads, adacomp::kLargeVecs>),
+                               dim3(n1), dim3(adacomp::kLargeThreads), plan->tile_lds[1], stream,
+                               plan->d_segs, plan->d_tile_seg, plan->d_vtiles[1], residue, dW, m8,
+                               stage, tile_cnt, tile_gsum, bin_max_out);
+        if ((st = launch_status()) != ADACOMP_OK) return st;
+        tm.stop();
+    }
+    {
+        StageTimer tm(timer, stream, ADACOMP_STAGE_CHUNK_SCAN);
+        hipLaunchKernelGGL(adacomp::k_chunk_scan, dim3(static_cast<uint32_t>(L.nchunks)), dim3(256), 0,
+                           stream, plan->d_chunk_tile_begin, tile_cnt, tile_gsum, tile_off,
+                           chunk_cnt, chunk_gsum);
+        if ((st = launch_status()) != ADACOMP_OK) return st;
+        tm.stop();
+    }
+    {
+        StageTimer tm(timer, stream, ADACOMP_STAGE_FINALIZE);
+        hipLaunchKernelGGL(adacomp::k_finalize, dim3(1), dim3(256), 0, stream, plan->d_segs, L.nseg,
+                           L.plan_hash, L.entries_begin, chunk_cnt, chunk_gsum, chunk_base, seg_s,
+                           seg_nsurv, seg_eoff, m8);
+        if ((st = launch_status()) != ADACOMP_OK) return st;
+        tm.stop();
+    }
+    {
+        StageTimer tm(timer, stream, ADACOMP_STAGE_ENCODE);
+        hipLaunchKernelGGL(adacomp::k_encode, dim3(static_cast<uint32_t>(L.ntiles)), dim3(256), 0,
+                           stream, plan->d_segs, plan->d_tile_seg, stage, tile_cnt, tile_off,
+                           chunk_base, seg_s, seg_eoff, m8, residue);
+        if ((st = launch_status()) != ADACOMP_OK) return st;
+        tm.stop();
+    }
+    return ADACOMP_OK;
+}
+
+int adacomp_compress(const adacomp_plan* plan, float* residue, const float* dW, uint64_t n_elems,
+                     void* msg, uint64_t msg_bytes, void* ws, uint64_t ws_bytes,
+                     float* bin_max_out, void* stream) {
+    return adacomp_compress_timed(plan, residue, dW, n_elems, msg, msg_bytes, ws, ws_bytes,
+                                  bin_max_out, stream, nullptr);
+}
+
+int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                                    float* out, uint64_t n_elems, int accumulate, void* ws,
+                                    uint64_t ws_bytes, void* stream_, adacomp_timer* timer) {
+    if (plan == nullptr || msgs == nullptr || out == nullptr || ws == nullptr)
+        return ADACOMP_ERR_INVALID_ARGUMENT;
+    if (K == 0 || K > ADACOMP_MAX_MESSAGES) return ADACOMP_ERR_INVALID_ARGUMENT;
+    if (accumulate != 0 && accumulate != 1) return ADACOMP_ERR_INVALID_ARGUMENT;
+    const Layout& L = plan->L;
+    const DecodeLayout D = decode_layout(L, K);
+    if (!aligned16(out) || !aligned16(ws)) return ADACOMP_ERR_MISALIGNED;
+    if (n_elems < L.span || ws_bytes < D.total ||
+        ws_bytes < L.dws_fixed + uint64_t(K) * L.dws_per_msg)
+        return ADACOMP_ERR_CAPACITY;
+    const Range ro = range_of(out, 4 * L.span), rw = range_of(ws, D.total);
+    if (overlaps(ro, rw)) return ADACOMP_ERR_INVALID_ARGUMENT;
+    adacomp::MsgPtrs mp{};
+    for (uint32_t k = 0; k < K; ++k) {
+        if (msgs[k] == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+        if (!aligned16(msgs[k])) return ADACOMP_ERR_MISALIGNED;
+        const Range rm = range_of(msgs[k], 32 + 16 * uint64_t(L.nseg));
+        if (overlaps(rm, ro) || overlaps(rm, rw)) return ADACOMP_ERR_INVALID_ARGUMENT;
+        mp.p[k] = static_cast<const uint8_t*>(msgs[k]);
+    }
+    int st = check_device(plan);
+    if (st != ADACOMP_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+
+    uint8_t* w8 = static_cast<uint8_t*>(ws);
+    adacomp::DecodeWs dw;
+    dw.status = reinterpret_cast<uint32_t*>(w8 + D.status);
+    dw.dcnt = reinterpret_cast<uint32_t*>(w8 + D.dcnt);
+    dw.doff = reinterpret_cast<uint32_t*>(w8 + D.doff);
+    dw.dchunk_cnt = reinterpret_cast<uint32_t*>(w8 + D.dchunk_cnt);
+    dw.dchunk_base = reinterpret_cast<uint32_t*>(w8 + D.dchunk_base);
+    dw.dseg_s = reinterpret_cast<float*>(w8 + D.dseg_s);
+    dw.dseg_eoff = reinterpret_cast<uint64_t*>(w8 + D.dseg_eoff);
+    dw.dvalid = reinterpret_cast<uint32_t*>(w8 + D.dvalid);
+    const uint32_t T = static_cast<uint32_t>(L.ntiles), C = static_cast<uint32_t>(L.nchunks);
+
+    {
+        StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_COUNT);
+        hipLaunchKernelGGL(adacomp::k_decode_count, dim3(C, K), dim3(256), 0, stream, mp,
+                           plan->d_segs, plan->d_chunk_tile_begin, plan->d_chunk_seg, T, C,
+                           L.nseg, L.plan_hash, dw);
+        if ((st = launch_status()) != ADACOMP_OK) return st;
+        tm.stop();
+    }
+    {
+        StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_BASE);
+        hipLaunchKernelGGL(adacomp::k_decode_base, dim3(1), dim3(256), 0, stream, mp, K,
+                           plan->d_segs, L.nseg, L.plan_hash, C, dw);
+        if ((st = launch_status()) != ADACOMP_OK) return st;
+        tm.stop();
+    }
+    {
+        StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_APPLY);
+        const uint32_t n0 = static_cast<uint32_t>(L.tiles_by_variant[0].size());
+        const uint32_t n1 = static_cast<uint32_t>(L.tiles_by_variant[1].size());
+        if (n0) {
+            const uint32_t acc_words = L.max_span_vecs[0] * 4;
+            const uint32_t ps = L.max_bpt[0] + 1;
+            const uint32_t KG = std::max<uint32_t>(1, std::min<uint32_t>(K, adacomp::kPrefWords / ps));
+            const uint32_t lds = (acc_words + KG * ps) * 4;
+            hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, 4>), dim3(n0), dim3(256), lds,
+                               stream, mp, K, KG, plan->d_segs, plan->d_tile_seg,
+                               plan->d_vtiles[0], T, C, L.nseg, dw, out, accumulate, acc_words);
+            if ((st = launch_status()) != ADACOMP_OK) return st;
+        }
+        if (n1) {
+            const uint32_t ps = L.max_bpt[1] + 1;
+            const uint32_t KG = std::max<uint32_t>(1, std::min<uint32_t>(K, adacomp::kPrefWords / ps));
+            const uint32_t lds = KG * ps * 4;
+            hipLaunchKernelGGL((adacomp::k_decode_apply<1024, false, 2>), dim3(n1), dim3(1024), lds,
+                               stream, mp, K, KG, plan->d_segs, plan->d_tile_seg,
+                               plan->d_vtiles[1], T, C, L.nseg, dw, out, accumulate, 0u);
+            if ((st = launch_status()) != ADACOMP_OK) return st;
+        }
+        tm.stop();
+    }
+    return ADACOMP_OK;
+}
+
+int adacomp_decode_accumulate(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                              float* out, uint64_t n_elems, int accumulate, void* ws,
+                              uint64_t ws_bytes, void* stream) {
+    return adacomp_decode_accumulate_timed(plan, msgs, K, out, n_elems, accumulate, ws, ws_bytes,
+                                           stream, nullptr);
+}
+
+int adacomp_timer_create(adacomp_timer** timer) {
+    if (timer == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+    *timer = new (std::nothrow) adacomp_timer();
+    return *timer ? ADACOMP_OK : ADACOMP_ERR_INVALID_ARGUMENT;
+}
+
+int adacomp_timer_reset(adacomp_timer* timer) {
+    if (timer == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+    int st = ADACOMP_OK;
+    for (auto& r : timer->recs) {
+        if (hipEventSynchronize(r.b) != hipSuccess) st = ADACOMP_ERR_HIP;
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    timer->recs.clear();
+    for (int i = 0; i < ADACOMP_NUM_STAGES; ++i) {
+        timer->ms[i] = 0.0;
+        timer->n[i] = 0;
+    }
+    return st;
+}
+
+int adacomp_timer_destroy(adacomp_timer* timer) {
+    if (timer == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+    const int st = adacomp_timer_reset(timer);
+    delete timer;
+    return st;
+}
+
+int adacomp_timer_read(adacomp_timer* timer, double* ms, uint64_t* launches, uint32_t nstages) {
+    if (timer == nullptr || ms == nullptr || launches == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+    for (auto& r : timer->recs) {
+        if (hipEventSynchronize(r.b) != hipSuccess) return ADACOMP_ERR_HIP;
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return ADACOMP_ERR_HIP;
+        timer->ms[r.stage] += t;
+        timer->n[r.stage] += 1;
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    timer->recs.clear();
+    for (uint32_t i = 0; i < nstages && i < ADACOMP_NUM_STAGES; ++i) {
+        ms[i] = timer->ms[i];
+        launches[i] = timer->n[i];
+    }
+    return ADACOMP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,715 @@
+// HIP kernels of the AdaComp compressor and decode-accumulate for gfx950.
+//
+// Method: "AdaComp (Adaptive Residual Gradient Compression)", AIMech curated
+// page, definition paragraph and Mechanism claim on local-bin soft threshold
+// and mean-g_max quantization (Algorithm 2); word widths from its Application
+// claim (Table 2).
+//
+// The path is HBM-bandwidth bound (about 6 float32 operations per 12 bytes
+// moved), so the kernels are built around coalesced 16-byte accesses, whole
+// bins per workgroup and compaction in LDS; no matrix cores are involved.
+//
+// Compress, per call, four stream-ordered launches:
+//   tile pass   (dense, one workgroup per tile of whole bins): reads residue
+//               and dW once as float4, forms G and H, bin maxima by a
+//               segmented wavefront max-scan plus LDS atomics, the survivor
+//               test |H| >= g_max && G != 0, survivor ranks by ballot and
+//               popcount, writes residue = G for every element, the bin's
+//               count word into the message, and the tile's survivors as
+//               (tile offset | sign, G) pairs to a staging area;
+//   chunk scan  survivor offsets of tiles inside chunks of 1024 tiles and the
+//               chunk's float64 sum of bin maxima, in a fixed order;
+//   finalize    one workgroup: s per segment, entry region offsets, message
+//               header, directory and padding;
+//   encode      one workgroup per tile: entry words into the message and the
+//               residue of each survivor, G - sign(G) * s.
+// Decode, per call, three launches: per-tile counts of every message, chunk
+// bases and message validity, then the per-tile apply that sums the messages
+// in order in LDS (large tiles: directly in out) and writes each tile once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace adacomp {
+
+constexpr uint32_t kSentinel = 0xFFFFFFFFu;
+
+__device__ __forceinline__ uint64_t rup16(uint64_t x) { return (x + 15u) & ~uint64_t(15); }
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__device__ __forceinline__ void put_word(uint8_t* p, uint32_t wb, uint32_t v) {
+    if (wb == 1u) *p = static_cast<uint8_t>(v);
+    else *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(v);
+}
+
+__device__ __forceinline__ uint32_t get_word(const uint8_t* p, uint32_t wb) {
+    return wb == 1u ? uint32_t(*p) : uint32_t(*reinterpret_cast<const uint16_t*>(p));
+}
+
+// Exclusive scan of n <= 64*k values in LDS by one wavefront; returns total.
+__device__ __forceinline__ uint32_t wave_exclusive_scan_lds(const uint32_t* in, uint32_t* out,
+                                                            int n, int lane) {
+    uint32_t carry = 0;
+    for (int base = 0; base < n; base += 64) {
+        const int i = base + lane;
+        const uint32_t v = i < n ? in[i] : 0u;
+        uint32_t inc = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t t = __shfl_up(inc, d);
+            if (lane >= d) inc += t;
+        }
+        if (i < n) out[i] = carry + inc - v;
+        carry += __shfl(inc, 63);
+    }
+    return carry;
+}
+
+// ---------------------------------------------------------------------------
+// Compress, dense tile pass.
+// ---------------------------------------------------------------------------
+template <int THREADS, int VPT>
+__global__ void __launch_bounds__(THREADS)
+k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
+            const uint32_t* __restrict__ vtiles, float* __restrict__ residue,
+            const float* __restrict__ dW, uint8_t* __restrict__ msg,
+            uint2* __restrict__ stage, uint32_t* __restrict__ tile_cnt,
+            double* __restrict__ tile_gsum, float* __restrict__ bin_max_out) {
+    constexpr int NW = THREADS / 64;
+    constexpr int NCH = NW * VPT;   // wavefront chunks of 256 elements per tile
+    extern __shared__ uint32_t dyn[];
+    __shared__ uint32_t ch_tot[NCH];
+    __shared__ uint32_t ch_base[NCH];
+    __shared__ uint32_t s_total;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint32_t tile = vtiles[blockIdx.x];
+    const SegDev sg = segs[tile_seg[tile]];
+    const TileGeom tg = tile_geom(sg, tile);
+    const uint32_t lt = sg.lt, magic = sg.magic;
+    uint32_t* smax = dyn;                 // [bpt] bin maxima as float bits
+    uint32_t* sbound = dyn + sg.bpt;      // [bpt + 1] survivors before each bin
+
+    for (uint32_t b = tid; b < tg.nb; b += THREADS) smax[b] = 0u;
+
+    float g[VPT][4], dd[VPT][4];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int vi = v * THREADS + tid;
+        const int x0 = vi * 4 - int(tg.lead);
+        float rr[4] = {0.f, 0.f, 0.f, 0.f}, dw[4] = {0.f, 0.f, 0.f, 0.f};
+        if (vi < int(tg.nvec)) {
+            const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
+            if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
+                const float4 a = *reinterpret_cast<const float4*>(residue + e0);
+                const float4 b = *reinterpret_cast<const float4*>(dW + e0);
+                rr[0] = a.x; rr[1] = a.y; rr[2] = a.z; rr[3] = a.w;
+                dw[0] = b.x; dw[1] = b.y; dw[2] = b.z; dw[3] = b.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int x = x0 + c;
+                    if (x >= 0 && x < int(tg.tlen)) {
+                        rr[c] = residue[e0 + c];
+                        dw[c] = dW[e0 + c];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            g[v][c] = rr[c] + dw[c];     // G = residue + dW
+            dd[v][c] = dw[c];
+        }
+    }
+    __syncthreads();   // smax cleared
+
+    // ---- bin maxima: g_max(i) = max |G| over bin i ----
+    if (lt >= 4u) {
+        // A float4 then spans at most two bins: a head run and a tail run.
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int vi = v * THREADS + tid;
+            const int x0 = vi * 4 - int(tg.lead);
+            uint32_t hb = kSentinel, tb = kSentinel, mh = 0u, mt = 0u;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int x = x0 + c;
+                if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen)) {
+                    const uint32_t b = div_bin(uint32_t(x), lt, magic);
+                    const uint32_t m = __float_as_uint(fabsf(g[v][c]));
+                    if (hb == kSentinel) { hb = b; tb = b; mh = m; mt = m; }
+                    else if (b == hb) { mh = max(mh, m); mt = max(mt, m); }
+                    else if (b == tb) { mt = max(mt, m); }
+                    else { tb = b; mt = m; }
+                }
+            }
+            const bool two = hb != tb;
+            // The head run of a two-run lane continues the previous lane's
+            // tail run: fold it there; a lane whose head starts a wave emits it.
+            const uint32_t ptb = __shfl_up(tb, 1);
+            const bool covered = two && lane > 0 && ptb == hb;
+            if (two && !covered) atomicMax(&smax[hb], mh);
+            const uint32_t nhb = __shfl_down(hb, 1);
+            const uint32_t nmh = __shfl_down(mh, 1);
+            const uint32_t ntwo = __shfl_down(uint32_t(two), 1);
+            if (lane < 63 && ntwo && nhb == tb) mt = max(mt, nmh);
+            // Segmented inclusive max-scan of the tail runs (bins ascend
+            // along the lanes, so equal keys are contiguous).
+            uint32_t val = mt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t k2 = __shfl_up(tb, d);
+                const uint32_t v2 = __shfl_up(val, d);
+                if (lane >= d && k2 == tb) val = max(val, v2);
+            }
+            const uint32_t nkey = __shfl_down(tb, 1);
+            if ((lane == 63 || nkey != tb) && tb != kSentinel) atomicMax(&smax[tb], val);
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int vi = v * THREADS + tid;
+            const int x0 = vi * 4 - int(tg.lead);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int x = x0 + c;
+                if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen))
+                    atomicMax(&smax[div_bin(uint32_t(x), lt, magic)],
+                              __float_as_uint(fabsf(g[v][c])));
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- selection: |H| >= g_max of the bin and G != 0 ----
+    uint32_t sel[VPT];
+    uint32_t wrank[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int vi = v * THREADS + tid;
+        const int x0 = vi * 4 - int(tg.lead);
+        uint32_t m = 0u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int x = x0 + c;
+            if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen)) {
+                const float gm = __uint_as_float(smax[div_bin(uint32_t(x), lt, magic)]);
+                const float h = g[v][c] + dd[v][c];      // H = G + dW
+                if (fabsf(h) >= gm && g[v][c] != 0.0f) m |= 1u << c;
+            }
+        }
+        sel[v] = m;
+        const uint64_t lm = lanemask_lt(lane);
+        const uint64_t b0 = __ballot(m & 1u), b1 = __ballot(m & 2u);
+        const uint64_t b2 = __ballot(m & 4u), b3 = __ballot(m & 8u);
+        wrank[v] = __popcll(b0 & lm) + __popcll(b1 & lm) + __popcll(b2 & lm) + __popcll(b3 & lm);
+        if (lane == 0) ch_tot[v * NW + wv] = __popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3);
+    }
+    __syncthreads();
+    if (wv == 0) {
+        const uint32_t tot = wave_exclusive_scan_lds(ch_tot, ch_base, NCH, lane);
+        if (lane == 0) s_total = tot;
+    }
+    __syncthreads();
+    const uint32_t total = s_total;
+
+    // ---- survivors to staging, bin boundaries, residue <- G ----
+    uint2* st = stage + tg.t0;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const int vi = v * THREADS + tid;
+        const int x0 = vi * 4 - int(tg.lead);
+        if (vi >= int(tg.nvec)) continue;
+        uint32_t r = ch_base[v * NW + wv] + wrank[v];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int x = x0 + c;
+            if (x >= 0 && x < int(tg.tlen)) {
+                const uint32_t b = div_bin(uint32_t(x), lt, magic);
+                if (uint32_t(x) == b * lt) sbound[b] = r;
+                if (sel[v] & (1u << c)) {
+                    const uint32_t neg = g[v][c] < 0.0f ? 0x80000000u : 0u;
+                    st[r] = make_uint2(neg | uint32_t(x), __float_as_uint(g[v][c]));
+                    ++r;
+                }
+            }
+        }
+        const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
+        if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
+            *reinterpret_cast<float4*>(residue + e0) = make_float4(g[v][0], g[v][1], g[v][2], g[v][3]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int x = x0 + c;
+                if (x >= 0 && x < int(tg.tlen)) residue[e0 + c] = g[v][c];
+            }
+        }
+    }
+    if (tid == 0) sbound[tg.nb] = total;
+    __syncthreads();
+
+    // ---- per-bin count words, optional g_max export, tile totals ----
+    uint8_t* cw = msg + sg.count_off + uint64_t(tg.first_bin) * sg.wb;
+    for (uint32_t b = tid; b < tg.nb; b += THREADS) {
+        put_word(cw + uint64_t(b) * sg.wb, sg.wb, sbound[b + 1] - sbound[b]);
+        if (bin_max_out) bin_max_out[sg.bin_base + tg.first_bin + b] = __uint_as_float(smax[b]);
+    }
+    if (wv == 0) {
+        double acc = 0.0;
+        for (uint32_t b = lane; b < tg.nb; b += 64) acc += double(__uint_as_float(smax[b]));
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+        if (lane == 0) {
+            tile_gsum[tile] = acc;
+            tile_cnt[tile] = total;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive scan of one value per thread (256 threads).
+// ---------------------------------------------------------------------------
+template <int THREADS>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds_w,
+                                                         uint32_t* total) {
+    constexpr int NW = THREADS / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    uint32_t inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t t = __shfl_up(inc, d);
+        if (lane >= d) inc += t;
+    }
+    if (lane == 63) lds_w[wv] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t x = lds_w[w];
+        if (w < wv) before += x;
+        all += x;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - v;
+}
+
+// Chunk scan: tiles [chunk_tile_begin[c], chunk_tile_begin[c+1]) <= 1024.
+__global__ void __launch_bounds__(256)
+k_chunk_scan(const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ tile_cnt,
+             const double* __restrict__ tile_gsum, uint32_t* __restrict__ tile_off,
+             uint32_t* __restrict__ chunk_cnt, double* __restrict__ chunk_gsum) {
+    __shared__ uint32_t lw[4];
+    __shared__ double lg[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint32_t c = blockIdx.x;
+    const uint32_t tb = chunk_tile_begin[c], n = chunk_tile_begin[c + 1] - tb;
+    uint32_t cnt[4];
+    uint32_t mine = 0;
+    double gs = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = uint32_t(tid) * 4u + i;
+        cnt[i] = t < n ? tile_cnt[tb + t] : 0u;
+        if (t < n) gs += tile_gsum[tb + t];
+        mine += cnt[i];
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan<256>(mine, lw, &total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = uint32_t(tid) * 4u + i;
+        if (t < n) tile_off[tb + t] = run;
+        run += cnt[i];
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) gs += __shfl_xor(gs, d);
+    if (lane == 0) lg[wv] = gs;
+    __syncthreads();
+    if (tid == 0) {
+        chunk_cnt[c] = total;
+        chunk_gsum[c] = ((lg[0] + lg[1]) + lg[2]) + lg[3];
+    }
+}
+
+// Finalize: one block of 256 threads.
+__global__ void __launch_bounds__(256)
+k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
+           uint64_t entries_begin, const uint32_t* __restrict__ chunk_cnt,
+           const double* __restrict__ chunk_gsum, uint32_t* __restrict__ chunk_base,
+           float* __restrict__ seg_s, uint32_t* __restrict__ seg_nsurv,
+           uint64_t* __restrict__ seg_eoff, uint8_t* __restrict__ msg) {
+    __shared__ uint64_t lw[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // s and survivor totals per segment; chunk bases within the segment.
+    for (uint32_t l = tid; l < nseg; l += 256) {
+        const SegDev sg = segs[l];
+        double acc = 0.0;
+        uint32_t run = 0;
+        for (uint32_t c = 0; c < sg.nchunks; ++c) {
+            const uint32_t ci = sg.chunk_begin + c;
+            acc += chunk_gsum[ci];
+            chunk_base[ci] = run;
+            run += chunk_cnt[ci];
+        }
+        // s = mean of the bin maxima, rounded once to float32.
+        seg_s[l] = float(acc / double(sg.nbins));
+        seg_nsurv[l] = run;
+        // Zero the padding after the count region.
+        const uint64_t cend = sg.count_off + uint64_t(sg.nbins) * sg.wb;
+        for (uint64_t p = cend; p < rup16(cend); ++p) msg[p] = 0;
+    }
+    __syncthreads();
+    // Entry regions in table order, each 16-byte aligned.
+    uint64_t carry = 0, surv = 0;
+    for (uint32_t base = 0; base < nseg; base += 256) {
+        const uint32_t l = base + tid;
+        uint64_t sz = 0, ns = 0;
+        if (l < nseg) {
+            ns = seg_nsurv[l];
+            sz = rup16(ns * segs[l].wb);
+        }
+        uint64_t inc = sz, ninc = ns;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint64_t t = __shfl_up(inc, d);
+            const uint64_t t2 = __shfl_up(ninc, d);
+            if (lane >= d) { inc += t; ninc += t2; }
+        }
+        if (lane == 63) lw[wv] = inc;
+        __syncthreads();
+        uint64_t before = 0, all = 0;
+        for (int w = 0; w < 4; ++w) {
+            if (w < wv) before += lw[w];
+            all += lw[w];
+        }
+        __syncthreads();
+        if (lane == 63) lw[wv] = ninc;
+        __syncthreads();
+        uint64_t nall = 0;
+        for (int w = 0; w < 4; ++w) nall += lw[w];
+        __syncthreads();
+        if (l < nseg) {
+            const uint64_t eoff = entries_begin + carry + before + inc - sz;
+            seg_eoff[l] = eoff;
+            uint8_t* d = msg + 32 + 16 * uint64_t(l);
+            *reinterpret_cast<float*>(d) = seg_s[l];
+            *reinterpret_cast<uint32_t*>(d + 4) = uint32_t(ns);
+            *reinterpret_cast<uint64_t*>(d + 8) = eoff;
+            const uint64_t wend = eoff + ns * segs[l].wb;
+            for (uint64_t p = wend; p < eoff + sz; ++p) msg[p] = 0;
+        }
+        carry += all;
+        surv += nall;
+    }
+    if (tid == 0) {
+        *reinterpret_cast<uint32_t*>(msg) = 0x43414441u;
+        *reinterpret_cast<uint16_t*>(msg + 4) = 1;
+        *reinterpret_cast<uint16_t*>(msg + 6) = 0;
+        *reinterpret_cast<uint32_t*>(msg + 8) = nseg;
+        *reinterpret_cast<uint32_t*>(msg + 12) = plan_hash;
+        *reinterpret_cast<uint64_t*>(msg + 16) = entries_begin + carry;
+        *reinterpret_cast<uint64_t*>(msg + 24) = surv;
+    }
+}
+
+// Encode + residue fix-up: one 256-thread block per tile.
+__global__ void __launch_bounds__(256)
+k_encode(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
+         const uint2* __restrict__ stage, const uint32_t* __restrict__ tile_cnt,
+         const uint32_t* __restrict__ tile_off, const uint32_t* __restrict__ chunk_base,
+         const float* __restrict__ seg_s, const uint64_t* __restrict__ seg_eoff,
+         uint8_t* __restrict__ msg, float* __restrict__ residue) {
+    const uint32_t tile = blockIdx.x;
+    const uint32_t cnt = tile_cnt[tile];
+    if (cnt == 0) return;
+    const uint32_t si = tile_seg[tile];
+    const SegDev sg = segs[si];
+    const TileGeom tg = tile_geom(sg, tile);
+    const uint32_t chunk = sg.chunk_begin + (tile - sg.tile_begin) / kChunkTiles;
+    const uint64_t base = uint64_t(chunk_base[chunk]) + tile_off[tile];
+    const float s = seg_s[si];
+    uint8_t* ew = msg + seg_eoff[si] + base * sg.wb;
+    const uint2* st = stage + tg.t0;
+    const uint32_t topbit = sg.wb == 1u ? 7u : 15u;
+    for (uint32_t e = threadIdx.x; e < cnt; e += 256) {
+        const uint2 p = st[e];
+        const uint32_t x = p.x & 0x7FFFFFFFu;
+        const uint32_t neg = p.x >> 31;
+        const uint32_t b = div_bin(x, sg.lt, sg.magic);
+        put_word(ew + uint64_t(e) * sg.wb, sg.wb, (neg << topbit) | (x - b * sg.lt));
+        const float gv = __uint_as_float(p.y);
+        // residue <- G - G_q with G_q = sign(G) * s
+        residue[tg.t0 + x] = neg ? gv + s : gv - s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode-accumulate.
+// ---------------------------------------------------------------------------
+struct MsgPtrs {
+    const uint8_t* p[ADACOMP_MAX_MESSAGES];
+};
+
+struct DecodeWs {
+    uint32_t* status;     // [1]
+    uint32_t* dcnt;       // [K*T]
+    uint32_t* doff;       // [K*T]
+    uint32_t* dchunk_cnt; // [K*C]
+    uint32_t* dchunk_base;// [K*C]
+    float* dseg_s;        // [K*nseg]
+    uint64_t* dseg_eoff;  // [K*nseg]
+    uint32_t* dvalid;     // [K]
+};
+
+// Per (chunk, message): tile survivor counts from the count words, offsets
+// within the chunk, chunk totals.
+__device__ __forceinline__ bool header_matches(const uint8_t* m, uint32_t nseg, uint32_t plan_hash) {
+    return *reinterpret_cast<const uint32_t*>(m) == 0x43414441u &&
+           *reinterpret_cast<const uint16_t*>(m + 4) == 1 &&
+           *reinterpret_cast<const uint32_t*>(m + 8) == nseg &&
+           *reinterpret_cast<const uint32_t*>(m + 12) == plan_hash;
+}
+
+__global__ void __launch_bounds__(256)
+k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
+               const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ chunk_seg,
+               uint32_t T, uint32_t C, uint32_t nseg, uint32_t plan_hash, DecodeWs ws) {
+    __shared__ uint32_t lw[4];
+    const uint32_t c = blockIdx.x, k = blockIdx.y;
+    const uint8_t* m = msgs.p[k];
+    // A message made for another table is never read past its header.
+    const bool ok = header_matches(m, nseg, plan_hash);
+    const SegDev sg = segs[chunk_seg[c]];
+    const uint32_t tb = chunk_tile_begin[c], n = chunk_tile_begin[c + 1] - tb;
+    uint32_t cnt[4];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = threadIdx.x * 4u + i;
+        uint32_t s = 0;
+        if (ok && t < n) {
+            const uint32_t first_bin = (tb + t - sg.tile_begin) * sg.bpt;
+            const uint32_t nb = min(sg.bpt, sg.nbins - first_bin);
+            const uint8_t* cw = m + sg.count_off + uint64_t(first_bin) * sg.wb;
+            for (uint32_t b = 0; b < nb; ++b) s += get_word(cw + uint64_t(b) * sg.wb, sg.wb);
+        }
+        cnt[i] = s;
+        mine += s;
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan<256>(mine, lw, &total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = threadIdx.x * 4u + i;
+        if (t < n) {
+            ws.dcnt[uint64_t(k) * T + tb + t] = cnt[i];
+            ws.doff[uint64_t(k) * T + tb + t] = run;
+        }
+        run += cnt[i];
+    }
+    if (threadIdx.x == 0) ws.dchunk_cnt[uint64_t(k) * C + c] = total;
+}
+
+// One block: message validity, per-segment s and entry offsets, chunk bases.
+__global__ void __launch_bounds__(256)
+k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, uint32_t nseg,
+              uint32_t plan_hash, uint32_t C, DecodeWs ws) {
+    __shared__ uint32_t valid[ADACOMP_MAX_MESSAGES];
+    __shared__ uint32_t bad;
+    if (threadIdx.x == 0) bad = 0;
+    __syncthreads();
+    for (uint32_t k = threadIdx.x; k < K; k += 256) {
+        const bool ok = header_matches(msgs.p[k], nseg, plan_hash);
+        valid[k] = ok ? 1u : 0u;
+        ws.dvalid[k] = ok ? 1u : 0u;
+        if (!ok) atomicAdd(&bad, 1u);
+    }
+    __syncthreads();
+    for (uint64_t i = threadIdx.x; i < uint64_t(K) * nseg; i += 256) {
+        const uint32_t k = uint32_t(i / nseg), l = uint32_t(i % nseg);
+        float s = 0.0f;
+        uint64_t eoff = 0;
+        if (valid[k]) {
+            const uint8_t* d = msgs.p[k] + 32 + 16 * uint64_t(l);
+            s = *reinterpret_cast<const float*>(d);
+            eoff = *reinterpret_cast<const uint64_t*>(d + 8);
+        }
+        ws.dseg_s[i] = s;
+        ws.dseg_eoff[i] = eoff;
+        const SegDev sg = segs[l];
+        uint32_t run = 0;
+        for (uint32_t c = 0; c < sg.nchunks; ++c) {
+            const uint64_t ci = uint64_t(k) * C + sg.chunk_begin + c;
+            ws.dchunk_base[ci] = run;
+            run += ws.dchunk_cnt[ci];
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) *ws.status = bad;
+}
+
+// Per tile: out[j] = (accumulate ? out[j] : +0) + q_0[j] + q_1[j] + ... in
+// message order, only at transmitted j.  LDS_ACC keeps the tile in LDS;
+// otherwise the tile is accumulated in place in out (large tiles).
+template <int THREADS, bool LDS_ACC, int EPT>
+__global__ void __launch_bounds__(THREADS)
+k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__ segs,
+               const uint32_t* __restrict__ tile_seg, const uint32_t* __restrict__ vtiles,
+               uint32_t T, uint32_t C, uint32_t nseg, DecodeWs ws, float* __restrict__ out,
+               int accumulate, uint32_t acc_words) {
+    extern __shared__ uint32_t dyn[];
+    __shared__ uint32_t fk[ADACOMP_MAX_MESSAGES + 1];      // flat entry prefix over messages
+    __shared__ uint64_t ebase[ADACOMP_MAX_MESSAGES];       // byte offset of the tile's entries
+    __shared__ float ks[ADACOMP_MAX_MESSAGES];
+
+    const int tid = threadIdx.x;
+    const uint32_t tile = vtiles[blockIdx.x];
+    const uint32_t si = tile_seg[tile];
+    const SegDev sg = segs[si];
+    const TileGeom tg = tile_geom(sg, tile);
+    const uint32_t chunk = sg.chunk_begin + (tile - sg.tile_begin) / kChunkTiles;
+    float* acc = LDS_ACC ? reinterpret_cast<float*>(dyn) : out + tg.v0;
+    uint32_t* pref = dyn + (LDS_ACC ? acc_words : 0u);    // [KG][bpt + 1]
+    const uint32_t pstride = sg.bpt + 1;
+
+    // Initial values: +0, or out.
+    for (uint32_t vi = tid; vi < tg.nvec; vi += THREADS) {
+        const int x0 = int(vi * 4) - int(tg.lead);
+        const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
+        if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
+            if (LDS_ACC) {
+                float4 a = accumulate ? *reinterpret_cast<const float4*>(out + e0)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+                *reinterpret_cast<float4*>(acc + vi * 4) = a;
+            } else if (!accumulate) {
+                *reinterpret_cast<float4*>(out + e0) = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        } else {
+            for (int c = 0; c < 4; ++c) {
+                const int x = x0 + c;
+                if (x >= 0 && x < int(tg.tlen)) {
+                    if (LDS_ACC) acc[vi * 4 + c] = accumulate ? out[e0 + c] : 0.0f;
+                    else if (!accumulate) out[e0 + c] = 0.0f;
+                }
+            }
+        }
+    }
+
+    for (uint32_t k0 = 0; k0 < K; k0 += KG) {
+        const uint32_t kn = min(KG, K - k0);
+        __syncthreads();
+        // Count words of the tile's bins for this group of messages.
+        for (uint32_t i = tid; i < kn * tg.nb; i += THREADS) {
+            const uint32_t kk = i / tg.nb, b = i - kk * tg.nb;
+            const uint32_t k = k0 + kk;
+            uint32_t cw = 0;
+            if (ws.dvalid[k])
+                cw = get_word(msgs.p[k] + sg.count_off + uint64_t(tg.first_bin + b) * sg.wb, sg.wb);
+            pref[kk * pstride + b + 1] = cw;
+        }
+        if (tid < int(kn)) {
+            const uint32_t k = k0 + tid;
+            const uint64_t kt = uint64_t(k) * T + tile;
+            const uint64_t base = uint64_t(ws.dchunk_base[uint64_t(k) * C + chunk]) + ws.doff[kt];
+            ebase[tid] = ws.dseg_eoff[uint64_t(k) * nseg + si] + base * sg.wb;
+            ks[tid] = ws.dseg_s[uint64_t(k) * nseg + si];
+        }
+        __syncthreads();
+        if (tid < int(kn)) {
+            uint32_t* pr = pref + tid * pstride;
+            uint32_t run = 0;
+            pr[0] = 0;
+            for (uint32_t b = 0; b < tg.nb; ++b) {
+                run += pr[b + 1];
+                pr[b + 1] = run;
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t run = 0;
+            for (uint32_t kk = 0; kk < kn; ++kk) {
+                fk[kk] = run;
+                run += pref[kk * pstride + tg.nb];
+            }
+            fk[kn] = run;
+        }
+        __syncthreads();
+        const uint32_t E = fk[kn];
+        const uint32_t topbit = sg.wb == 1u ? 7u : 15u;
+        for (uint32_t w0 = 0; w0 < E; w0 += THREADS * EPT) {
+            uint32_t xk[EPT], kq[EPT];
+            float qv[EPT];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                const uint32_t i = w0 + j * THREADS + tid;
+                kq[j] = kSentinel;
+                if (i < E) {
+                    // message of flat entry i
+                    uint32_t lo = 0, hi = kn;   // fk[lo] <= i < fk[hi]
+                    while (hi - lo > 1) {
+                        const uint32_t mid = (lo + hi) >> 1;
+                        if (fk[mid] <= i) lo = mid; else hi = mid;
+                    }
+                    const uint32_t e = i - fk[lo];
+                    const uint32_t* pr = pref + lo * pstride;
+                    uint32_t bl = 0, bh = tg.nb;   // pr[bl] <= e < pr[bh]
+                    while (bh - bl > 1) {
+                        const uint32_t mid = (bl + bh) >> 1;
+                        if (pr[mid] <= e) bl = mid; else bh = mid;
+                    }
+                    const uint32_t word = get_word(msgs.p[k0 + lo] + ebase[lo] + uint64_t(e) * sg.wb, sg.wb);
+                    const uint32_t idx = word & ((1u << topbit) - 1u);
+                    const uint32_t x = bl * sg.lt + idx;
+                    if (idx < sg.lt && x < tg.tlen) {
+                        kq[j] = lo;
+                        xk[j] = x + tg.lead;
+                        qv[j] = (word >> topbit) ? -ks[lo] : ks[lo];
+                    }
+                }
+            }
+            // Apply in message order; within one message every index is distinct.
+            const uint32_t klo = [&] {
+                uint32_t lo = 0, hi = kn;
+                while (hi - lo > 1) { const uint32_t mid = (lo + hi) >> 1; if (fk[mid] <= w0) lo = mid; else hi = mid; }
+                return lo;
+            }();
+            const uint32_t last = min(E, w0 + THREADS * EPT) - 1;
+            const uint32_t khi = [&] {
+                uint32_t lo = 0, hi = kn;
+                while (hi - lo > 1) { const uint32_t mid = (lo + hi) >> 1; if (fk[mid] <= last) lo = mid; else hi = mid; }
+                return lo;
+            }();
+            for (uint32_t kk = klo; kk <= khi; ++kk) {
+#pragma unroll
+                for (int j = 0; j < EPT; ++j)
+                    if (kq[j] == kk) acc[xk[j]] = acc[xk[j]] + qv[j];
+                __syncthreads();
+            }
+        }
+    }
+    if (LDS_ACC) {
+        __syncthreads();
+        for (uint32_t vi = tid; vi < tg.nvec; vi += THREADS) {
+            const int x0 = int(vi * 4) - int(tg.lead);
+            const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
+            if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
+                *reinterpret_cast<float4*>(out + e0) = *reinterpret_cast<const float4*>(acc + vi * 4);
+            } else {
+                for (int c = 0; c < 4; ++c) {
+                    const int x = x0 + c;
+                    if (x >= 0 && x < int(tg.tlen)) out[e0 + c] = acc[vi * 4 + c];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace adacomp

@@ -1,0 +1,278 @@
+// Host-side plan layout for the AdaComp library: validation of a segment
+// table, work tiles, message layout and workspace layout.  No HIP calls here.
+//
+// Work decomposition.  Each segment (one layer) is cut into tiles of whole
+// bins, so that every bin maximum, survivor count and compaction is local to
+// one workgroup and no cross-workgroup combination is needed for a bin.
+//   - small tiles: 256 threads x 4 float4 per thread per array, at most 4096
+//     elements, for L_T <= 4093;
+//   - large tiles: 1024 threads x 9 float4, at most 36864 elements, for
+//     4093 < L_T <= 32768.
+// Bins per tile are chosen so that tile starts fall on 16-byte boundaries
+// whenever that fits, which keeps every load and store a whole float4 except
+// at the ends of segments.
+#pragma once
+
+#include <algorithm>
+#include <cstdint>
+#include <numeric>
+#include <vector>
+
+#include "../../include/adacomp.h"
+
+#if defined(__HIPCC__)
+#define ADACOMP_HD __host__ __device__
+#else
+#define ADACOMP_HD
+#endif
+
+namespace adacomp {
+
+constexpr uint32_t kSmallThreads = 256;
+constexpr uint32_t kSmallVecs = 4;
+constexpr uint32_t kSmallCap = kSmallThreads * kSmallVecs * 4;   // 4096 elements
+constexpr uint32_t kLargeThreads = 1024;
+constexpr uint32_t kLargeVecs = 9;
+constexpr uint32_t kLargeCap = kLargeThreads * kLargeVecs * 4;   // 36864 elements
+constexpr uint32_t kChunkTiles = 1024;  // tiles per scan chunk (4 per thread of a 256-thread block)
+constexpr uint32_t kPrefWords = 8192;   // LDS words for per-message bin prefixes in decode
+constexpr uint64_t kAlign = 256;        // workspace sub-buffer alignment
+
+// Per-segment parameters read by every kernel (80 bytes).
+struct SegDev {
+    uint64_t off;        // element offset in the flat buffers
+    uint64_t numel;
+    uint64_t bin_base;   // global index of the segment's first bin
+    uint64_t count_off;  // byte offset of the segment's count region in a message
+    uint32_t lt;         // bin length L_T
+    uint32_t magic;      // floor(2^32 / lt) + 1: exact x / lt for x < 2^16 (lt >= 2)
+    uint32_t nbins;
+    uint32_t bpt;        // bins per tile
+    uint32_t tile_begin; // first global tile of the segment
+    uint32_t ntiles;
+    uint32_t chunk_begin;
+    uint32_t nchunks;
+    uint32_t wb;         // index word bytes: 1 if lt < 64 else 2
+    uint32_t variant;    // 0 small tiles, 1 large tiles
+    uint32_t pad[2];
+};
+static_assert(sizeof(SegDev) == 80, "SegDev layout");
+
+// Exact x / lt for 0 <= x < 2^16 and 2 <= lt <= 2^16 with magic =
+// floor(2^32 / lt) + 1: the product overshoots x / lt by x * e / 2^32 with
+// 0 < e <= 1, which stays below 2^-16 <= 1/lt, so the floor is unchanged.
+ADACOMP_HD inline uint32_t div_bin(uint32_t x, uint32_t lt, uint32_t magic) {
+    return lt == 1u ? x : static_cast<uint32_t>((uint64_t(x) * magic) >> 32);
+}
+
+// Geometry of one tile: its bins, elements and the float4 it touches.
+struct TileGeom {
+    uint32_t first_bin;  // first bin of the tile within its segment
+    uint32_t nb;         // bins in the tile
+    uint32_t tlen;       // elements in the tile
+    uint32_t lead;       // t0 - v0 (0..3)
+    uint32_t nvec;       // float4 the tile touches
+    uint64_t t0;         // flat index of the tile's first element
+    uint64_t v0;         // t0 rounded down to a multiple of 4
+};
+
+ADACOMP_HD inline TileGeom tile_geom(const SegDev& sg, uint32_t tile) {
+    TileGeom g;
+    const uint32_t local = tile - sg.tile_begin;
+    g.first_bin = local * sg.bpt;
+    const uint32_t left = sg.nbins - g.first_bin;
+    g.nb = sg.bpt < left ? sg.bpt : left;
+    const uint64_t e0 = uint64_t(g.first_bin) * sg.lt;
+    const uint64_t rest = sg.numel - e0;
+    const uint64_t want = uint64_t(g.nb) * sg.lt;
+    g.tlen = static_cast<uint32_t>(want < rest ? want : rest);
+    g.t0 = sg.off + e0;
+    g.v0 = g.t0 & ~uint64_t(3);
+    g.lead = static_cast<uint32_t>(g.t0 - g.v0);
+    g.nvec = (g.lead + g.tlen + 3u) >> 2;
+    return g;
+}
+
+struct Layout {
+    uint32_t nseg = 0;
+    uint32_t plan_hash = 0;
+    std::vector<SegDev> segs;
+    std::vector<uint32_t> tile_seg;          // [T] segment of each tile
+    std::vector<uint32_t> tiles_by_variant[2];
+    std::vector<uint32_t> chunk_tile_begin;  // [C + 1]
+    std::vector<uint32_t> chunk_seg;         // [C]
+    uint32_t max_bpt[2] = {0, 0};
+    uint32_t max_span_vecs[2] = {0, 0};      // most float4 one tile touches
+    uint64_t total_numel = 0, span = 0, total_bins = 0;
+    uint64_t ntiles = 0, nchunks = 0;
+    uint64_t counts_begin = 0, entries_begin = 0, capacity = 0;
+
+    // Compress workspace (byte offsets).
+    uint64_t ws_stage = 0, ws_tile_cnt = 0, ws_tile_gsum = 0, ws_tile_off = 0;
+    uint64_t ws_chunk_cnt = 0, ws_chunk_gsum = 0, ws_chunk_base = 0;
+    uint64_t ws_seg_s = 0, ws_seg_nsurv = 0, ws_seg_eoff = 0, ws_compress = 0;
+
+    // Decode workspace: fixed part, then per-message arrays.
+    uint64_t dws_fixed = 0, dws_per_msg = 0;
+};
+
+inline uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// FNV-1a, 32 bit, over each segment's offset, numel (8 bytes each), bin_len
+// and flags (4 bytes each), little-endian, in table order.
+inline uint32_t table_hash(const adacomp_segment* s, uint32_t n) {
+    uint32_t h = 0x811C9DC5u;
+    auto mix = [&h](uint64_t v, int bytes) {
+        for (int i = 0; i < bytes; ++i) {
+            h ^= static_cast<uint32_t>((v >> (8 * i)) & 0xFFu);
+            h *= 0x01000193u;
+        }
+    };
+    for (uint32_t i = 0; i < n; ++i) {
+        mix(s[i].offset, 8);
+        mix(s[i].numel, 8);
+        mix(s[i].bin_len, 4);
+        mix(s[i].flags, 4);
+    }
+    return h;
+}
+
+// Bins per tile for bin length lt and tile capacity cap (elements): as many
+// whole bins as fit, rounded so that tiles start 16-byte aligned if possible;
+// otherwise leave room for the up-to-3-element lead of an unaligned start.
+inline uint32_t bins_per_tile(uint32_t lt, uint32_t cap, uint32_t nbins) {
+    uint32_t bpt = cap / lt;
+    if (bpt >= nbins) return nbins;   // one tile holds the segment; it starts aligned
+    const uint32_t a = 4u / std::gcd(lt, 4u);
+    if ((static_cast<uint64_t>(bpt) * lt) % 4 != 0) {
+        const uint32_t aligned = bpt / a * a;
+        bpt = aligned >= 1 ? aligned : (cap - 3) / lt;
+    }
+    return bpt;
+}
+
+inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
+    if (segs == nullptr || nseg == 0) return ADACOMP_ERR_INVALID_ARGUMENT;
+    for (uint32_t i = 0; i < nseg; ++i) {
+        const adacomp_segment& s = segs[i];
+        if (s.numel == 0 || s.flags != 0) return ADACOMP_ERR_INVALID_ARGUMENT;
+        if (s.bin_len == 0 || s.bin_len > ADACOMP_MAX_BIN_LEN) return ADACOMP_ERR_UNSUPPORTED_BIN;
+        if (s.offset % 4 != 0) return ADACOMP_ERR_MISALIGNED;
+        if (s.numel >= (uint64_t(1) << 32)) return ADACOMP_ERR_TOO_LARGE;
+        if (s.offset > (uint64_t(1) << 48)) return ADACOMP_ERR_TOO_LARGE;
+    }
+    {   // overlap check on the table sorted by offset
+        std::vector<uint32_t> ord(nseg);
+        std::iota(ord.begin(), ord.end(), 0u);
+        std::sort(ord.begin(), ord.end(),
+                  [&](uint32_t a, uint32_t b) { return segs[a].offset < segs[b].offset; });
+        for (uint32_t i = 1; i < nseg; ++i) {
+            const adacomp_segment& p = segs[ord[i - 1]];
+            if (p.offset + p.numel > segs[ord[i]].offset) return ADACOMP_ERR_OVERLAP;
+        }
+    }
+
+    L = Layout();
+    L.nseg = nseg;
+    L.plan_hash = table_hash(segs, nseg);
+    L.segs.resize(nseg);
+    L.counts_begin = round_up(32 + 16 * uint64_t(nseg), 16);
+    uint64_t count_at = L.counts_begin;
+    uint64_t tiles = 0, chunks = 0, bins = 0;
+    for (uint32_t i = 0; i < nseg; ++i) {
+        const adacomp_segment& s = segs[i];
+        SegDev& d = L.segs[i];
+        d = SegDev{};
+        d.off = s.offset;
+        d.numel = s.numel;
+        d.lt = s.bin_len;
+        d.magic = s.bin_len >= 2 ? static_cast<uint32_t>((uint64_t(1) << 32) / s.bin_len + 1) : 0u;
+        const uint64_t nb = (s.numel + s.bin_len - 1) / s.bin_len;
+        d.nbins = static_cast<uint32_t>(nb);
+        d.variant = s.bin_len <= kSmallCap - 3 ? 0u : 1u;
+        const uint32_t cap = d.variant == 0 ? kSmallCap : kLargeCap;
+        d.bpt = bins_per_tile(s.bin_len, cap, d.nbins);
+        d.ntiles = static_cast<uint32_t>((nb + d.bpt - 1) / d.bpt);
+        d.wb = s.bin_len < 64 ? 1u : 2u;
+        d.bin_base = bins;
+        d.count_off = count_at;
+        if (tiles + d.ntiles >= (uint64_t(1) << 31)) return ADACOMP_ERR_TOO_LARGE;
+        d.tile_begin = static_cast<uint32_t>(tiles);
+        d.nchunks = (d.ntiles + kChunkTiles - 1) / kChunkTiles;
+        d.chunk_begin = static_cast<uint32_t>(chunks);
+        // Most float4 any tile of this segment touches: an unaligned start
+        // adds up to 3 leading elements.
+        const uint64_t tile_elems = std::min<uint64_t>(uint64_t(d.bpt) * s.bin_len, s.numel);
+        const bool aligned = (uint64_t(d.bpt) * s.bin_len) % 4 == 0 || d.ntiles == 1;
+        const uint64_t vecs = (tile_elems + (aligned ? 0 : 3) + 3) / 4;
+        if (vecs * 4 > cap) return ADACOMP_ERR_UNSUPPORTED_BIN;
+        L.max_span_vecs[d.variant] = std::max<uint32_t>(L.max_span_vecs[d.variant], uint32_t(vecs));
+        L.max_bpt[d.variant] = std::max(L.max_bpt[d.variant], d.bpt);
+
+        for (uint32_t t = 0; t < d.ntiles; ++t) {
+            L.tile_seg.push_back(i);
+            L.tiles_by_variant[d.variant].push_back(static_cast<uint32_t>(tiles + t));
+        }
+        for (uint32_t c = 0; c < d.nchunks; ++c) {
+            L.chunk_tile_begin.push_back(static_cast<uint32_t>(tiles + uint64_t(c) * kChunkTiles));
+            L.chunk_seg.push_back(i);
+        }
+        tiles += d.ntiles;
+        chunks += d.nchunks;
+        bins += nb;
+        count_at = round_up(count_at + nb * d.wb, 16);
+        L.total_numel += s.numel;
+        L.span = std::max<uint64_t>(L.span, s.offset + s.numel);
+    }
+    L.chunk_tile_begin.push_back(static_cast<uint32_t>(tiles));
+    L.ntiles = tiles;
+    L.nchunks = chunks;
+    L.total_bins = bins;
+    L.entries_begin = count_at;
+    uint64_t cap = count_at;
+    for (uint32_t i = 0; i < nseg; ++i) cap = round_up(cap + L.segs[i].numel * L.segs[i].wb, 16);
+    L.capacity = cap;
+
+    // Compress workspace.
+    uint64_t w = 0;
+    auto take = [&w](uint64_t bytes) {
+        const uint64_t at = w;
+        w = round_up(w + bytes, kAlign);
+        return at;
+    };
+    L.ws_stage = take(8 * round_up(L.span, 4));     // (key, G) pair per possible survivor
+    L.ws_tile_cnt = take(4 * tiles);
+    L.ws_tile_gsum = take(8 * tiles);
+    L.ws_tile_off = take(4 * tiles);
+    L.ws_chunk_cnt = take(4 * chunks);
+    L.ws_chunk_gsum = take(8 * chunks);
+    L.ws_chunk_base = take(4 * chunks);
+    L.ws_seg_s = take(4 * uint64_t(nseg));
+    L.ws_seg_nsurv = take(4 * uint64_t(nseg));
+    L.ws_seg_eoff = take(8 * uint64_t(nseg));
+    L.ws_compress = w;
+
+    // Decode workspace for K messages: a status block, then arrays indexed by
+    // message: tile counts and offsets [K*T], chunk counts and bases [K*C],
+    // per-segment s and entry offsets [K*nseg], per-message validity [K].
+    // Each array is kAlign-aligned, so fixed covers the padding of all nine.
+    L.dws_fixed = 9 * kAlign;
+    L.dws_per_msg = round_up(8 * tiles + 8 * chunks + 12 * uint64_t(nseg) + 4, 16);
+    return ADACOMP_OK;
+}
+
+inline void fill_info(const Layout& L, adacomp_plan_info* info) {
+    info->nseg = L.nseg;
+    info->plan_hash = L.plan_hash;
+    info->total_numel = L.total_numel;
+    info->span = L.span;
+    info->total_bins = L.total_bins;
+    info->ntiles = L.ntiles;
+    info->header_bytes = 32 + 16 * uint64_t(L.nseg);
+    info->message_capacity = L.capacity;
+    info->compress_workspace_bytes = L.ws_compress;
+    info->decode_workspace_bytes_per_message = L.dws_per_msg;
+    info->decode_workspace_bytes_fixed = L.dws_fixed;
+}
+
+}  // namespace adacomp

@@ -1,0 +1,223 @@
+"""Benchmark of the AdaComp hot path on one MI355X.
+
+One step = one adacomp_compress of a learner's full gradient (the
+1.07-billion-element workload: 64 layers of 4096 x 4096, L_T = 500, 16-bit
+words, bursty N(0, 1e-3) gradients with 5% of bins scaled x100) followed by
+one adacomp_decode_accumulate of K = 16 learners' messages into a dense float32
+sum.  Every input is generated on the device before the timed region; the
+residue carries over from step to step.
+
+Printed: one JSON line.  ``value`` is compress throughput in Gelem/s (device
+time of the compress calls inside the timed steps); ``roofline`` rates the
+dominant kernel (the dense tile pass) against MI355X's 8 TB/s HBM peak;
+``cpu_baseline`` is the plain C oracle timed on this host's cores on a sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import pathlib
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "AdaComp compress Gelem/s & % of HBM roofline; compression ratio; decode GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "adaptive_residual_gradient_amd" / "csrc").glob("*")):
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per tile-pass launch measured with rocprofv3 counters, if the
+    kernel sources have not changed since they were taken."""
+    p = ROOT / "profiles" / f"tile_pass_{workload}_traffic.json"
+    if not p.exists():
+        return None
+    try:
+        rec = json.loads(p.read_text())
+    except ValueError:
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, dws_host_fn, seconds: float = 15.0):
+    """Time the oracle (single thread) on whole layers of the workload."""
+    import numpy as np
+    import oracle
+    segs = wl.segments
+    take = 4 if len(segs) >= 4 else len(segs)
+    sub, off = [], 0
+    for (_, n, lt) in segs[:take]:
+        sub.append((off, n, lt))
+        off += (n + 3) // 4 * 4
+    r = np.zeros(off, np.float32)
+    steps, elems, t_used = 0, 0, 0.0
+    while t_used < seconds and steps < 10:
+        d = dws_host_fn(steps, off)
+        t0 = time.perf_counter()
+        oracle.compress(sub, r, d)
+        t_used += time.perf_counter() - t0
+        steps += 1
+        elems += sum(n for _, n, _ in sub)
+    return {
+        "value": round(elems / t_used / 1e9, 4),
+        "unit": "Gelem/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{take} of {len(segs)} layers ({sum(n for _, n, _ in sub)} elements), "
+                  f"{steps} compress steps from zero residue on the benchmark's own gradients, "
+                  f"{t_used:.1f} s single-threaded",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="large")
+    ap.add_argument("--learners", type=int, default=16)
+    ap.add_argument("--learner-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build measures one GPU: the compressor runs per learner "
+                                   "on its own GPU; multi-GPU exchange is not built (run with --gpus 1)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import adaptive_residual_gradient_amd as A
+    import workloads as W
+    from adaptive_residual_gradient_amd import stats
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.workload(args.workload)
+    n_alloc = W.alloc_len(wl)
+    N = wl.numel
+    plan = A.Plan(wl.segments)
+    info = plan.info
+    log(f"workload {wl.name}: {N} elements, {len(wl.segments)} layers, {info.total_bins} bins")
+
+    # Decode inputs: K learners, each running its own steps from zero residue.
+    K = args.learners
+    msg = plan.message_buffer(dev)
+    ws = plan.compress_workspace(dev)
+    dbuf = torch.empty(n_alloc, dtype=torch.float32, device=dev)
+    learner_msgs, learner_bytes = [], []
+    for k in range(1, K + 1):
+        r = torch.zeros(n_alloc, dtype=torch.float32, device=dev)
+        for s in range(1, args.learner_steps + 1):
+            W.fill_dw(dbuf, wl, k, s)
+            A.compress(plan, r, dbuf, msg, ws)
+        total, _, _ = A.message_header(plan, msg)
+        learner_msgs.append(msg[:total].clone())
+        learner_bytes.append(total)
+        del r
+    log(f"built {K} learner messages, {sum(learner_bytes) / 1e6:.1f} MB in total")
+
+    # The benchmarked learner (learner 0): all step gradients resident in HBM.
+    nsteps = args.warmup + args.steps
+    dws = []
+    for s in range(1, nsteps + 1):
+        t = torch.empty(n_alloc, dtype=torch.float32, device=dev)
+        W.fill_dw(t, wl, 0, s)
+        dws.append(t)
+    residue = torch.zeros(n_alloc, dtype=torch.float32, device=dev)
+    out = torch.empty(n_alloc, dtype=torch.float32, device=dev)
+    dws_dec = plan.decode_workspace(K, dev)
+    timer = A.Timer()
+    torch.cuda.synchronize()
+
+    def step(i, tm):
+        A.compress(plan, residue, dws[i], msg, ws, timer=tm)
+        A.decode_accumulate(plan, learner_msgs, out, False, dws_dec, timer=tm)
+
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    timer.reset()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, nsteps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = timer.read()
+
+    # Message of the last timed step (for the compression ratio).
+    total, surv, dirs = A.message_header(plan, msg)
+    pr, wr, _, _ = stats.message_ratios(wl.segments, bytes(msg[: int(info.header_bytes)].cpu().numpy()))
+
+    ms = {k: v[0] / max(v[1], 1) for k, v in st.items()}
+    launches = {k: v[1] for k, v in st.items()}
+    compress_ms = ms["tile_pass"] + ms["chunk_scan"] + ms["finalize"] + ms["encode"]
+    decode_ms = ms["decode_count"] + ms["decode_base"] + ms["decode_apply"]
+    tile_bytes = 12.0 * N                       # read residue + dW, write residue
+    achieved = tile_bytes / (ms["tile_pass"] * 1e-3) / 1e9
+    compress_bytes = 12.0 * N + total
+    decode_bytes = float(sum(learner_bytes)) + 4.0 * N
+    traffic = traffic_from_profiles(args.workload)
+
+    res = {
+        "metric": METRIC,
+        "value": round(N / (compress_ms * 1e-3) / 1e9, 3),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": len(wl.segments), "numel": N,
+                   "bin_len": 500, "index_bits": 16, "decode_messages": K,
+                   "learner_steps": args.learner_steps},
+        "roofline": {"bound": "hbm", "kernel": "tile_pass",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+        "compress_ms": round(compress_ms, 4),
+        "compress_GBps": round(compress_bytes / (compress_ms * 1e-3) / 1e9, 1),
+        "compress_frac_of_peak": round(compress_bytes / (compress_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "decode_ms": round(decode_ms, 4),
+        "decode_GBps": round(decode_bytes / (decode_ms * 1e-3) / 1e9, 1),
+        "stage_ms": {k: round(v, 4) for k, v in ms.items()},
+        "stage_launches": launches,
+        "last_message": {"bytes": int(total), "survivors": int(surv),
+                         "payload_ratio": round(pr, 2), "wire_ratio": round(wr, 2)},
+    }
+    timer.close()
+
+    if not args.no_cpu_baseline:
+        def host_dw(step_idx, length):
+            # the benchmarked learner's gradient of step step_idx+1, first layers
+            return dws[min(step_idx, nsteps - 1)][:length].cpu().numpy().copy()
+        res["cpu_baseline"] = cpu_baseline(wl, host_dw)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * adacomp.h -- C ABI of the AdaComp compressor for AMD Instinct MI355X (gfx950).
+ *
+ * AdaComp ("AdaComp (Adaptive Residual Gradient Compression)", AIMech curated
+ * page, definition paragraph and the Mechanism claim on local-bin soft
+ * threshold and mean-g_max quantization, Algorithm 2) compresses each layer's
+ * gradient dW against a residue carried from step to step:
+ *
+ *   G = residue + dW,  H = G + dW                       (float32, no contraction)
+ *   bins of L_T consecutive elements; g_max(i) = max |G| over bin i
+ *   transmit every element with |H| >= g_max(its bin) and G != 0
+ *   s = mean of g_max over the layer's bins             (one scale per layer)
+ *   G_q = sign(G) * s for transmitted elements
+ *   residue <- G - G_q (transmitted), residue <- G (all others)
+ *
+ * The transmitted elements are packed as sparse-indexed ternary words, 8-bit
+ * when L_T < 64 and 16-bit otherwise (Application claim, Table 2; Curated
+ * Limitations), into a message whose length varies from step to step
+ * (Limitation claim).  decode_accumulate sums several such messages, one per
+ * learner of a data-parallel job, into a dense float32 gradient.
+ *
+ * Conventions common to every call:
+ *   - Every pointer named residue, dW, out, msg, msgs[k] or ws is a DEVICE
+ *     pointer on the device that was current when the plan was created; that
+ *     device must be current at the call.  Pointers to plain structs and to
+ *     the msgs array are HOST pointers.  The caller owns every buffer.
+ *   - The flat float32 buffers (residue, dW, out) hold every layer of the
+ *     segment table at its element offset; they must be 16-byte aligned and
+ *     hold at least info.span elements.  Elements outside every segment are
+ *     never read or written.
+ *   - msg and ws must be 16-byte aligned and at least as large as the plan
+ *     reports.  Buffers given to one call must not overlap.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *     stream) and return once the work is enqueued.  Argument errors are
+ *     detected on the host before anything is enqueued, and then nothing is
+ *     written.  Results are deterministic: the same inputs give the same bits.
+ *   - Return value: ADACOMP_OK (0) or a negative status; adacomp_status_str()
+ *     names it.  No C++ exception crosses this interface.
+ *
+ * Message layout (all little-endian, every region 16-byte aligned, padding
+ * bytes zero; w = 8 if L_T < 64 else 16):
+ *   header, 32 bytes: u32 magic 0x43414441 ("ADAC"), u16 version 1, u16 0,
+ *     u32 nseg, u32 plan_hash, u64 total_bytes, u64 total_survivors;
+ *   directory at byte 32: nseg x 16 bytes {f32 s, u32 nsurv, u64 entries_offset};
+ *   count regions, one per segment in table order, at positions fixed by the
+ *     plan: B words of w bits, the number of transmitted elements per bin;
+ *   entry regions, one per segment in table order, packed after the count
+ *     regions: nsurv words of w bits, bin-major with ascending in-bin index,
+ *     each word = sign << (w-1) | in_bin_index, sign = 1 iff G < 0.
+ */
+#ifndef ADACOMP_H
+#define ADACOMP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define ADACOMP_OK 0
+#define ADACOMP_ERR_INVALID_ARGUMENT (-1) /* null pointer, empty table, numel 0, flags != 0, wrong device, aliasing */
+#define ADACOMP_ERR_UNSUPPORTED_BIN (-2)  /* L_T = 0 or L_T > 32768 (a 16-bit word holds a 15-bit index) */
+#define ADACOMP_ERR_MISALIGNED (-3)       /* segment offset not a multiple of 4, or a buffer not 16-byte aligned */
+#define ADACOMP_ERR_OVERLAP (-4)          /* two segments share an element */
+#define ADACOMP_ERR_CAPACITY (-5)         /* a buffer is smaller than the plan requires */
+#define ADACOMP_ERR_HIP (-6)              /* a HIP runtime call or kernel launch failed */
+#define ADACOMP_ERR_TOO_LARGE (-7)        /* numel >= 2^32 in one segment, or the table exceeds launch limits */
+
+#define ADACOMP_MAX_BIN_LEN 32768u
+#define ADACOMP_MAX_MESSAGES 256u         /* most messages one decode_accumulate call sums */
+
+/* One layer: numel consecutive elements of the flat buffers starting at
+ * element `offset` (a multiple of 4), compressed with bins of bin_len = L_T
+ * elements over its flattened storage order.  flags must be 0. */
+typedef struct adacomp_segment {
+    uint64_t offset;
+    uint64_t numel;
+    uint32_t bin_len;
+    uint32_t flags;
+} adacomp_segment;
+
+/* Sizes a caller needs to allocate buffers for a segment table. */
+typedef struct adacomp_plan_info {
+    uint32_t nseg;
+    uint32_t plan_hash;                 /* FNV-1a 32 of the table, as in message headers */
+    uint64_t total_numel;               /* sum of numel */
+    uint64_t span;                      /* max(offset + numel): minimum length of residue, dW, out */
+    uint64_t total_bins;                /* sum over segments of ceil(numel / bin_len) */
+    uint64_t ntiles;                    /* work tiles (whole bins of one segment each) */
+    uint64_t header_bytes;              /* 32 + 16*nseg: read this much to learn a message's size */
+    uint64_t message_capacity;          /* largest possible message: every element transmitted */
+    uint64_t compress_workspace_bytes;
+    uint64_t decode_workspace_bytes_per_message;
+    uint64_t decode_workspace_bytes_fixed; /* decode ws for K messages = fixed + K * per_message */
+} adacomp_plan_info;
+
+typedef struct adacomp_plan adacomp_plan;   /* opaque, immutable once created */
+typedef struct adacomp_timer adacomp_timer; /* opaque per-kernel device timer */
+
+/* Host-only: validate a segment table and report the sizes its plan would
+ * have.  Touches no GPU.  Returns a status; fills *info on success. */
+int adacomp_plan_query(const adacomp_segment* segs, uint32_t nseg, adacomp_plan_info* info);
+
+/* Validate the table, build the work tiles and copy the small tile tables to
+ * the current device.  The plan owns that device memory until
+ * adacomp_plan_destroy.  An immutable plan may be used from several streams
+ * at once (with separate buffers). */
+int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan** plan);
+int adacomp_plan_destroy(adacomp_plan* plan);
+int adacomp_plan_get_info(const adacomp_plan* plan, adacomp_plan_info* info);
+
+/* One AdaComp compression step over every segment (the definition above).
+ *   residue  [span] float32, read and updated in place.
+ *   dW       [span] float32, read only.
+ *   n_elems  elements in residue and in dW (>= info.span).
+ *   msg      message output, msg_bytes >= info.message_capacity.  Its length
+ *            is the header's total_bytes (read it after the stream syncs).
+ *   ws       workspace, ws_bytes >= info.compress_workspace_bytes; no
+ *            initial contents required, contents undefined afterwards.
+ *   bin_max_out  nullable device float32[total_bins]: every g_max, segments
+ *            in table order, bins in order (a testing aid).
+ * Determinism: s is the bin maxima summed in float64 in a fixed order, divided
+ * by B in float64 and rounded once to float32; everything else is exact. */
+int adacomp_compress(const adacomp_plan* plan, float* residue, const float* dW,
+                     uint64_t n_elems, void* msg, uint64_t msg_bytes, void* ws,
+                     uint64_t ws_bytes, float* bin_max_out, void* stream);
+
+/* Sum K messages made by adacomp_compress with this same segment table into
+ * out, in message order: for k = 0..K-1 and every element j message k
+ * transmits, out[j] = out[j] + sign * s (float32, rounded each time).
+ *   msgs        HOST array of K device pointers; 1 <= K <= ADACOMP_MAX_MESSAGES.
+ *   out         [span] float32.  accumulate = 0: every element of every
+ *               segment starts from +0; accumulate = 1: starts from out.
+ *               An element no message transmits gets no addition.
+ *   ws          ws_bytes >= fixed + K * per_message (see plan info).
+ * A message whose header does not match the plan (magic, version, nseg,
+ * plan_hash) contributes nothing; the number of such messages is written as
+ * a uint32 at byte 0 of ws. */
+int adacomp_decode_accumulate(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                              float* out, uint64_t n_elems, int accumulate, void* ws,
+                              uint64_t ws_bytes, void* stream);
+
+/* Same calls with a timer: device time of each kernel stage is recorded with
+ * HIP events on `stream` and summed in the timer.  timer may be NULL. */
+int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float* dW,
+                           uint64_t n_elems, void* msg, uint64_t msg_bytes, void* ws,
+                           uint64_t ws_bytes, float* bin_max_out, void* stream,
+                           adacomp_timer* timer);
+int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const* msgs,
+                                    uint32_t K, float* out, uint64_t n_elems, int accumulate,
+                                    void* ws, uint64_t ws_bytes, void* stream,
+                                    adacomp_timer* timer);
+
+/* Kernel stages a timer reports, in this order. */
+#define ADACOMP_STAGE_TILE_PASS 0   /* dense pass: G, H, bin maxima, selection, counts */
+#define ADACOMP_STAGE_CHUNK_SCAN 1  /* per-chunk survivor offsets and scale partial sums */
+#define ADACOMP_STAGE_FINALIZE 2    /* s per segment, message header and directory */
+#define ADACOMP_STAGE_ENCODE 3      /* entry words and residue of transmitted elements */
+#define ADACOMP_STAGE_DECODE_COUNT 4
+#define ADACOMP_STAGE_DECODE_BASE 5
+#define ADACOMP_STAGE_DECODE_APPLY 6
+#define ADACOMP_NUM_STAGES 7
+
+int adacomp_timer_create(adacomp_timer** timer);
+int adacomp_timer_destroy(adacomp_timer* timer);
+/* Wait for every recorded event, then report per stage the summed
+ * milliseconds and the number of launches since the last reset. */
+int adacomp_timer_read(adacomp_timer* timer, double* ms, uint64_t* launches, uint32_t nstages);
+int adacomp_timer_reset(adacomp_timer* timer);
+
+const char* adacomp_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADACOMP_H */

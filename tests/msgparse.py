@@ -154,3 +154,28 @@ def sent_mask(msg: Message, segments, length: int) -> np.ndarray:
     for sm, (off, n, lt, *rest) in zip(msg.segs, segments):
         m[off + sm.index] = True
     return m
+
+
+def single_segment_message(buf, segments, i: int) -> bytes:
+    """Re-pack segment i of a message as a one-segment message for the table
+    [(0, numel_i, bin_len_i)] (used to check samples of very large messages
+    against the oracle segment by segment)."""
+    b = bytes(np.asarray(buf, dtype=np.uint8).tobytes())
+    msg = parse(b, segments, strict=False)
+    sm = msg.segs[i]
+    _, n, lt, *rest = segments[i]
+    wb = word_bytes(lt)
+    nb = (n + lt - 1) // lt
+    sub = [(0, n, lt)]
+    count_at = align16(32 + 16)
+    entry_at = align16(count_at + nb * wb)
+    dt = np.uint8 if wb == 1 else np.dtype("<u2")
+    counts = sm.counts.astype(dt).tobytes()
+    words = sm.words.astype(dt).tobytes()
+    total = align16(entry_at + len(words))
+    out = bytearray(total)
+    struct.pack_into("<IHHIIQQ", out, 0, MAGIC, 1, 0, 1, table_hash(sub), total, sm.nsurv)
+    struct.pack_into("<IIQ", out, 32, sm.s_bits, sm.nsurv, entry_at)
+    out[count_at:count_at + len(counts)] = counts
+    out[entry_at:entry_at + len(words)] = words
+    return bytes(out)

@@ -1,0 +1,144 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads and exports
+every function include/adacomp.h declares, segment-table validation, the plan
+sizes, and a CPU check of the tile geometry every kernel launch relies on."""
+import ctypes
+import pathlib
+import random
+import re
+import subprocess
+
+import pytest
+
+import adaptive_residual_gradient_amd as A
+import msgparse as mp
+import oracle
+import workloads as W
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "adacomp.h"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_built():
+    if not A.LIB_PATH.exists():
+        from adaptive_residual_gradient_amd import _build
+        _build.build()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(adacomp_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 13
+    h = ctypes.CDLL(str(A.LIB_PATH))
+    for n in names:
+        assert hasattr(h, n), f"{n} not exported"
+    assert set(names) == set(A.SIGNATURES), "binding and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", str(A.LIB_PATH)],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (adacomp_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    for st in range(0, -8, -1):
+        assert A.status_str(st) != "unknown status"
+    assert A.status_str(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("segs,status", [
+    ([], -1),
+    ([(0, 0, 50)], -1),
+    ([(0, 100, 0)], -2),
+    ([(0, 100, 32769)], -2),
+    ([(2, 100, 50)], -3),
+    ([(0, 100, 50), (96, 10, 50)], -4),
+    ([(100, 10, 50), (0, 101, 50)], -4),
+    ([(0, 1 << 32, 500)], -7),
+    ([(0, 100, 50, 1)], -1),
+])
+def test_plan_query_rejects(segs, status):
+    with pytest.raises(A.AdaCompError) as e:
+        A.plan_query(segs)
+    assert e.value.status == status
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_plan_info_matches_format(name):
+    wl = W.workload(name)
+    info = A.plan_query(wl.segments)
+    assert info.nseg == len(wl.segments)
+    assert info.total_numel == wl.numel and info.span == wl.span
+    assert info.total_bins == wl.bins
+    assert info.header_bytes == 32 + 16 * len(wl.segments)
+    assert info.plan_hash == mp.table_hash(wl.segments) == oracle.plan_hash(wl.segments)
+    assert info.message_capacity == oracle.message_capacity(wl.segments)
+
+
+def test_null_plan_calls_fail_cleanly():
+    L = A.lib()
+    assert L.adacomp_compress(None, None, None, 0, None, 0, None, 0, None, None) == -1
+    assert L.adacomp_decode_accumulate(None, None, 0, None, 0, 0, None, 0, None) == -1
+    assert L.adacomp_plan_destroy(None) == -1
+    assert L.adacomp_plan_get_info(None, None) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(A, "LIB_PATH", ROOT / "nonexistent" / "libadacomp.so")
+    monkeypatch.setattr(A, "_lib", None)
+    with pytest.raises(A.HipLibraryMissing):
+        A.plan_query([(0, 100, 50)])
+
+
+# --------------------------------------------------------------------------
+# Tile geometry, checked on the CPU with the library's own layout code.
+# --------------------------------------------------------------------------
+
+EDGE_BINS = [1, 2, 3, 4, 5, 7, 8, 50, 63, 64, 65, 127, 500, 1000, 4093, 4094, 4095,
+             4096, 5000, 8191, 32765, 32766, 32767, 32768]
+EDGE_NUMEL = [1, 2, 3, 4, 5, 7, 63, 64, 65, 4093, 4096, 4097, 36861, 65537, 100003]
+
+
+def geometry_tables():
+    tables = [(wl.segments, 0) for wl in (W.workload(n) for n in W.WORKLOADS)]
+    for lt in EDGE_BINS:
+        segs, off = [], 0
+        for n in EDGE_NUMEL:
+            segs.append((off, n, lt))
+            off += (n + 3) // 4 * 4 + 4
+        tables.append((segs, 0))
+    rng = random.Random(5)
+    for _ in range(40):
+        segs, off = [], 0
+        for _ in range(rng.randint(1, 12)):
+            n = rng.choice([rng.randint(1, 80), rng.randint(1, 20000), rng.randint(1, 300000)])
+            lt = rng.choice([rng.randint(1, 70), rng.randint(1, 5000), rng.randint(4000, 32768)])
+            segs.append((off, n, lt))
+            off += (n + 3) // 4 * 4 + 4 * rng.randint(0, 3)
+        tables.append((segs, 0))
+    tables.append(([(0, 100, 0)], -2))
+    tables.append(([(0, 10, 50), (4, 10, 50)], -4))
+    return tables
+
+
+def test_tile_geometry_on_cpu(tmp_path):
+    exe = tmp_path / "geometry_check"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-o", str(exe),
+                    str(ROOT / "tests" / "cpu" / "geometry_check.cpp")], check=True)
+    tables = geometry_tables()
+    lines = []
+    for segs, expect in tables:
+        lines.append(f"{len(segs)} {expect}")
+        lines += [f"{o} {n} {lt}" for o, n, lt in segs]
+    inp = tmp_path / "tables.txt"
+    inp.write_text("\n".join(lines) + "\n")
+    r = subprocess.run([str(exe), str(inp)], capture_output=True, text=True)
+    out = r.stdout.strip().splitlines()
+    assert len(out) == len(tables), r.stderr
+    fails = [(i, l) for i, l in enumerate(out) if not l.startswith("OK")]
+    assert not fails, fails[:5]
+    assert r.returncode == 0

@@ -1,0 +1,156 @@
+"""GPU parity of adacomp_decode_accumulate against the CPU oracle: bit-exact,
+messages summed in order, for K = 1..16 messages, both accumulate modes,
+edge-case tables, the full-size 1.07-billion-element workload (sampled
+segments), and messages whose header does not match the plan."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import adaptive_residual_gradient_amd as A
+import msgparse as mp
+import oracle
+import workloads as W
+from parity import bits
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def learner_messages(wl, plan, K, steps=2):
+    """K learners, each `steps` compress steps from a zero residue with its
+    own seeds; returns the device messages of the last step."""
+    n = W.alloc_len(wl)
+    ws = plan.compress_workspace(DEV)
+    d = torch.empty(n, dtype=torch.float32, device=DEV)
+    msgs = []
+    for k in range(K):
+        r = torch.zeros(n, dtype=torch.float32, device=DEV)
+        msg = plan.message_buffer(DEV)
+        for s in range(1, steps + 1):
+            W.fill_dw(d, wl, k, s)
+            A.compress(plan, r, d, msg, ws)
+        total, _, _ = A.message_header(plan, msg)
+        msgs.append(msg[:max(total, 16)].clone() if total < msg.numel() else msg)
+    return msgs
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,K", [("fc", 1), ("fc", 3), ("conv", 4), ("resnet50", 16),
+                                    ("fc_lstm", 2)])
+def test_decode_parity(name, K):
+    wl = W.workload(name)
+    plan = A.Plan(wl.segments)
+    n = W.alloc_len(wl)
+    msgs = learner_messages(wl, plan, K)
+    host_msgs = [host(m) for m in msgs]
+    ws = plan.decode_workspace(K, DEV)
+    rng = np.random.default_rng(K)
+    for accumulate in (False, True):
+        start = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        start[::5] = -0.0
+        out = torch.from_numpy(start.copy()).to(DEV)
+        say(f"  decode {name} K={K} accumulate={accumulate}")
+        A.decode_accumulate(plan, msgs, out, accumulate, ws)
+        got = host(out)
+        want = start.copy()
+        oracle.decode_accumulate(wl.segments, host_msgs, want, accumulate)
+        np.testing.assert_array_equal(bits(got), bits(want))
+        assert int(host(ws[:4]).view(np.uint32)[0]) == 0
+    plan.close()
+
+
+@pytest.mark.parametrize("lt", [1, 3, 7, 50, 64, 500, 4094, 32768])
+def test_decode_edge_tables(lt):
+    segs, off = [], 0
+    for n in (1, 5, 63, 4097, 40003):
+        segs.append((off, n, lt))
+        off += (n + 3) // 4 * 4 + 4
+    span = off
+    plan = A.Plan(segs)
+    rng = np.random.default_rng(lt)
+    cws = plan.compress_workspace(DEV)
+    msgs = []
+    for k in range(3):
+        r = torch.from_numpy((rng.standard_normal(span) * 1e-3).astype(np.float32)).to(DEV)
+        d = torch.from_numpy((rng.standard_normal(span) * 1e-3).astype(np.float32)).to(DEV)
+        m = plan.message_buffer(DEV)
+        A.compress(plan, r, d, m, cws)
+        msgs.append(m)
+    host_msgs = []
+    for m in msgs:
+        total, _, _ = A.message_header(plan, m)
+        host_msgs.append(host(m[:total]))
+    ws = plan.decode_workspace(3, DEV)
+    for accumulate in (False, True):
+        start = rng.standard_normal(span).astype(np.float32)
+        out = torch.from_numpy(start.copy()).to(DEV)
+        say(f"  decode L_T={lt} accumulate={accumulate}")
+        A.decode_accumulate(plan, msgs, out, accumulate, ws)
+        want = start.copy()
+        oracle.decode_accumulate(segs, host_msgs, want, accumulate)
+        np.testing.assert_array_equal(bits(host(out)), bits(want))
+    plan.close()
+
+
+def test_decode_skips_foreign_messages():
+    """A message made for another segment table contributes nothing and is
+    counted in the status word."""
+    segs = [(0, 5000, 50)]
+    other = [(0, 5000, 500)]
+    plan, plan2 = A.Plan(segs), A.Plan(other)
+    r = torch.zeros(5000, dtype=torch.float32, device=DEV)
+    d = torch.from_numpy((np.random.default_rng(0).standard_normal(5000) * 1e-3)
+                         .astype(np.float32)).to(DEV)
+    m1, m2 = plan.message_buffer(DEV), plan2.message_buffer(DEV)
+    A.compress(plan, r.clone(), d, m1, plan.compress_workspace(DEV))
+    A.compress(plan2, r.clone(), d, m2, plan2.compress_workspace(DEV))
+    ws = plan.decode_workspace(2, DEV)
+    out = torch.zeros(5000, dtype=torch.float32, device=DEV)
+    A.decode_accumulate(plan, [m1, m2], out, False, ws)
+    ref = torch.zeros(5000, dtype=torch.float32, device=DEV)
+    A.decode_accumulate(plan, [m1], ref, False, plan.decode_workspace(1, DEV))
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+    assert int(host(ws[:4]).view(np.uint32)[0]) == 1
+    plan.close()
+    plan2.close()
+
+
+def test_decode_large_workload_sampled():
+    """K = 16 learner messages of the 1.07-billion-element workload summed on
+    the GPU at full size; three sampled segments checked bit for bit."""
+    wl = W.workload("large")
+    plan = A.Plan(wl.segments)
+    K = 16
+    say("  building 16 learner messages at full size")
+    msgs = learner_messages(wl, plan, K, steps=2)
+    ws = plan.decode_workspace(K, DEV)
+    out = torch.empty(W.alloc_len(wl), dtype=torch.float32, device=DEV)
+    say("  decode K=16 full size")
+    A.decode_accumulate(plan, msgs, out, False, ws)
+    torch.cuda.synchronize()
+    host_msgs = []
+    for m in msgs:
+        total, _, _ = A.message_header(plan, m)
+        host_msgs.append(host(m[:total]))
+    for i in (0, 31, 63):
+        o, c, lt = wl.segments[i]
+        sub = [(0, c, lt)]
+        want = np.zeros(c, np.float32)
+        oracle.decode_accumulate(sub, [mp.single_segment_message(hm, wl.segments, i)
+                                       for hm in host_msgs], want, False)
+        np.testing.assert_array_equal(bits(host(out[o:o + c])), bits(want))
+        say(f"    segment {i} ok")
+    plan.close()
+    del msgs, out, ws
+    torch.cuda.empty_cache()
