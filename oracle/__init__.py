@@ -137,7 +137,8 @@ def decode_accumulate(segments, messages, out: np.ndarray, accumulate: bool) -> 
     span = max(int(s[0]) + int(s[1]) for s in segments)
     if out.size < span:
         raise ValueError("out shorter than the segment table's span")
-    keep = [np.ascontiguousarray(m, dtype=np.uint8) for m in messages]
+    keep = [np.frombuffer(bytes(m), dtype=np.uint8) if isinstance(m, (bytes, bytearray, memoryview))
+            else np.ascontiguousarray(m, dtype=np.uint8) for m in messages]
     ptrs = (ctypes.c_void_p * max(1, len(keep)))(*[m.ctypes.data for m in keep])
     st = _load().oracle_decode_accumulate(arr, n, ptrs, len(keep), out.ctypes.data,
                                           1 if accumulate else 0)

@@ -75,10 +75,16 @@ def _check(cond, what):
         raise FormatError(what)
 
 
+def as_bytes(buf) -> bytes:
+    if isinstance(buf, (bytes, bytearray, memoryview)):
+        return bytes(buf)
+    return np.ascontiguousarray(buf, dtype=np.uint8).tobytes()
+
+
 def parse(buf, segments: Sequence, strict: bool = True) -> Message:
     """Parse ``buf`` (bytes-like or uint8 array) against the segment table.
     With ``strict`` every structural rule is checked, padding included."""
-    b = bytes(np.asarray(buf, dtype=np.uint8).tobytes())
+    b = as_bytes(buf)
     _check(len(b) >= 32, "message shorter than its header")
     magic, ver, zero, nseg, phash, total, nsurv_all = struct.unpack_from("<IHHIIQQ", b, 0)
     _check(magic == MAGIC, f"bad magic {magic:#x}")
@@ -160,7 +166,7 @@ def single_segment_message(buf, segments, i: int) -> bytes:
     """Re-pack segment i of a message as a one-segment message for the table
     [(0, numel_i, bin_len_i)] (used to check samples of very large messages
     against the oracle segment by segment)."""
-    b = bytes(np.asarray(buf, dtype=np.uint8).tobytes())
+    b = as_bytes(buf)
     msg = parse(b, segments, strict=False)
     sm = msg.segs[i]
     _, n, lt, *rest = segments[i]

@@ -65,7 +65,7 @@ def compare_step(segments, r_in: np.ndarray, dW: np.ndarray, r_gpu: np.ndarray,
             assert rel <= S_RTOL, f"segment {i}: s {a.s!r} vs {b.s!r}"
             rep.notes.append(f"segment {i}: s differs by {rel:.2e} relative")
     rep.survivors = m_ref.total_survivors
-    g = np.asarray(msg_gpu, dtype=np.uint8)[: m_ref.total_bytes]
+    g = mp.as_bytes(msg_gpu)[: m_ref.total_bytes]
     rep.msg_identical = bytes(g) == bytes(msg_ref)
     if all_s_equal:
         assert rep.msg_identical, "message bytes differ although every s agrees"

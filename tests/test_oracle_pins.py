@@ -463,3 +463,25 @@ def test_sent_count_adapts_to_activity():
 def test_oracle_rejects_bad_tables(segs):
     with pytest.raises(oracle.OracleError):
         oracle.message_capacity(segs)
+
+
+def test_single_segment_repack_matches_full_decode():
+    """Test infrastructure: re-packing one segment of a message as a
+    one-segment message decodes to the same values as that segment of the
+    full message (used by the sampled checks of the largest workload)."""
+    rng = np.random.default_rng(31)
+    segs = [(0, 3000, 50), (3000, 5003, 500), (8004, 777, 7)]
+    span = 8784
+    msgs = []
+    for k in range(3):
+        r = (rng.standard_normal(span) * 1e-3).astype(np.float32)
+        d = (rng.standard_normal(span) * 1e-3).astype(np.float32)
+        msgs.append(bytes(oracle.compress(segs, r, d)[0]))
+    full = np.zeros(span, np.float32)
+    oracle.decode_accumulate(segs, msgs, full, False)
+    for i, (o, n, lt) in enumerate(segs):
+        sub = np.zeros(n, np.float32)
+        oracle.decode_accumulate([(0, n, lt)], [mp.single_segment_message(m, segs, i) for m in msgs],
+                                 sub, False)
+        np.testing.assert_array_equal(bits(sub), bits(full[o:o + n]))
+        mp.parse(mp.single_segment_message(msgs[0], segs, i), [(0, n, lt)])
