@@ -56,19 +56,19 @@ def traffic_from_profiles(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, dws_host_fn, seconds: float = 15.0):
+def cpu_baseline(wl, dws_host_fn, max_steps: int, seconds: float = 15.0):
     """Time the oracle (single thread) on whole layers of the workload."""
     import numpy as np
     import oracle
     segs = wl.segments
-    take = 4 if len(segs) >= 4 else len(segs)
+    take = min(24, len(segs))
     sub, off = [], 0
     for (_, n, lt) in segs[:take]:
         sub.append((off, n, lt))
         off += (n + 3) // 4 * 4
     r = np.zeros(off, np.float32)
     steps, elems, t_used = 0, 0, 0.0
-    while t_used < seconds and steps < 10:
+    while t_used < seconds and steps < max_steps:
         d = dws_host_fn(steps, off)
         t0 = time.perf_counter()
         oracle.compress(sub, r, d)
@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--learners", type=int, default=16)
     ap.add_argument("--learner-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain device copy of 1 GiB (a known-size reference "
+                         "for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -111,6 +114,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = W.workload(args.workload)
     n_alloc = W.alloc_len(wl)
     N = wl.numel
@@ -213,7 +222,7 @@ def main():
         def host_dw(step_idx, length):
             # the benchmarked learner's gradient of step step_idx+1, first layers
             return dws[min(step_idx, nsteps - 1)][:length].cpu().numpy().copy()
-        res["cpu_baseline"] = cpu_baseline(wl, host_dw)
+        res["cpu_baseline"] = cpu_baseline(wl, host_dw, nsteps)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
