@@ -25,11 +25,25 @@ struct adacomp_plan {
     void* dmem = nullptr;
     SegDev* d_segs = nullptr;
     uint32_t* d_tile_seg = nullptr;
-    uint32_t* d_vtiles[2] = {nullptr, nullptr};
+    uint32_t* d_vtiles[adacomp::kVariants] = {nullptr, nullptr, nullptr};
     uint32_t* d_chunk_tile_begin = nullptr;
     uint32_t* d_chunk_seg = nullptr;
-    uint32_t tile_lds[2] = {0, 0};
+    uint32_t tile_lds_words[adacomp::kVariants] = {0, 0, 0};  // one tile's LDS words
 };
+
+namespace adacomp {
+template <int V>
+hipError_t launch_tile_pass(const adacomp_plan* plan, hipStream_t stream, float* residue,
+                            const float* dW, uint8_t* msg, uint2* stage, uint32_t* tile_cnt,
+                            double* tile_gsum, float* bin_max_out) {
+    const uint32_t n = static_cast<uint32_t>(plan->L.tiles_by_variant[V].size());
+    hipLaunchKernelGGL((k_tile_pass<kVarThreads[V], kVarVecs[V]>), dim3(n), dim3(kVarThreads[V]),
+                       plan->tile_lds_words[V] * 4, stream, plan->d_segs, plan->d_tile_seg,
+                       plan->d_vtiles[V], residue, dW, msg, stage, tile_cnt, tile_gsum,
+                       bin_max_out);
+    return hipGetLastError();
+}
+}  // namespace adacomp
 
 struct adacomp_timer {
     struct Rec {
@@ -160,9 +174,12 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
         }
         const Layout& L = p->L;
         // Launch limits: total work-items of one launch must fit in 32 bits.
-        if (L.tiles_by_variant[0].size() * uint64_t(adacomp::kSmallThreads) >= (uint64_t(1) << 32) ||
-            L.tiles_by_variant[1].size() * uint64_t(adacomp::kLargeThreads) >= (uint64_t(1) << 32) ||
-            L.ntiles * 256ull >= (uint64_t(1) << 32) || L.nchunks * 256ull >= (uint64_t(1) << 32)) {
+        bool too_large = L.ntiles * 256ull >= (uint64_t(1) << 32) ||
+                         L.nchunks * 256ull >= (uint64_t(1) << 32);
+        for (int v = 0; v < adacomp::kVariants; ++v)
+            too_large |= L.tiles_by_variant[v].size() * uint64_t(adacomp::kVarThreads[v]) >=
+                         (uint64_t(1) << 32);
+        if (too_large) {
             delete p;
             return ADACOMP_ERR_TOO_LARGE;
         }
@@ -172,11 +189,13 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
         }
         const uint64_t b_segs = adacomp::round_up(sizeof(SegDev) * L.nseg, 256);
         const uint64_t b_ts = adacomp::round_up(4 * L.ntiles, 256);
-        const uint64_t b_v0 = adacomp::round_up(4 * L.tiles_by_variant[0].size() + 4, 256);
-        const uint64_t b_v1 = adacomp::round_up(4 * L.tiles_by_variant[1].size() + 4, 256);
+        uint64_t b_v[adacomp::kVariants];
+        for (int v = 0; v < adacomp::kVariants; ++v)
+            b_v[v] = adacomp::round_up(4 * L.tiles_by_variant[v].size() + 4, 256);
         const uint64_t b_ctb = adacomp::round_up(4 * (L.nchunks + 1), 256);
         const uint64_t b_cs = adacomp::round_up(4 * L.nchunks + 4, 256);
-        const uint64_t total = b_segs + b_ts + b_v0 + b_v1 + b_ctb + b_cs;
+        uint64_t total = b_segs + b_ts + b_ctb + b_cs;
+        for (int v = 0; v < adacomp::kVariants; ++v) total += b_v[v];
         std::vector<uint8_t> host(total, 0);
         uint64_t at = 0;
         auto put = [&](const void* src, uint64_t bytes, uint64_t room) {
@@ -187,8 +206,9 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
         };
         const uint64_t o_segs = put(L.segs.data(), sizeof(SegDev) * L.nseg, b_segs);
         const uint64_t o_ts = put(L.tile_seg.data(), 4 * L.ntiles, b_ts);
-        const uint64_t o_v0 = put(L.tiles_by_variant[0].data(), 4 * L.tiles_by_variant[0].size(), b_v0);
-        const uint64_t o_v1 = put(L.tiles_by_variant[1].data(), 4 * L.tiles_by_variant[1].size(), b_v1);
+        uint64_t o_v[adacomp::kVariants];
+        for (int v = 0; v < adacomp::kVariants; ++v)
+            o_v[v] = put(L.tiles_by_variant[v].data(), 4 * L.tiles_by_variant[v].size(), b_v[v]);
         const uint64_t o_ctb = put(L.chunk_tile_begin.data(), 4 * (L.nchunks + 1), b_ctb);
         const uint64_t o_cs = put(L.chunk_seg.data(), 4 * L.nchunks, b_cs);
         if (hipMalloc(&p->dmem, total) != hipSuccess) {
@@ -203,11 +223,11 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
         uint8_t* base = static_cast<uint8_t*>(p->dmem);
         p->d_segs = reinterpret_cast<SegDev*>(base + o_segs);
         p->d_tile_seg = reinterpret_cast<uint32_t*>(base + o_ts);
-        p->d_vtiles[0] = reinterpret_cast<uint32_t*>(base + o_v0);
-        p->d_vtiles[1] = reinterpret_cast<uint32_t*>(base + o_v1);
+        for (int v = 0; v < adacomp::kVariants; ++v)
+            p->d_vtiles[v] = reinterpret_cast<uint32_t*>(base + o_v[v]);
         p->d_chunk_tile_begin = reinterpret_cast<uint32_t*>(base + o_ctb);
         p->d_chunk_seg = reinterpret_cast<uint32_t*>(base + o_cs);
-        for (int v = 0; v < 2; ++v) p->tile_lds[v] = (2 * L.max_bpt[v] + 1) * 4;
+        for (int v = 0; v < adacomp::kVariants; ++v) p->tile_lds_words[v] = 2 * L.max_bpt[v] + 1;
         *out = p;
         return ADACOMP_OK;
     } catch (...) {
@@ -273,20 +293,20 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
 
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_TILE_PASS);
-        const uint32_t n0 = static_cast<uint32_t>(L.tiles_by_variant[0].size());
-        const uint32_t n1 = static_cast<uint32_t>(L.tiles_by_variant[1].size());
-        if (n0)
-            hipLaunchKernelGGL((adacomp::k_tile_pass<adacomp::kSmallThreads, adacomp::kSmallVecs>),
-                               dim3(n0), dim3(adacomp::kSmallThreads), plan->tile_lds[0], stream,
-                               plan->d_segs, plan->d_tile_seg, plan->d_vtiles[0], residue, dW, m8,
-                               stage, tile_cnt, tile_gsum, bin_max_out);
-        if ((st = launch_status()) != ADACOMP_OK) return st;
-        if (n1)
-            hipLaunchKernelGGL((adacomp::k_tile_pass<adacomp::kLargeThreads, adacomp::kLargeVecs>),
-                               dim3(n1), dim3(adacomp::kLargeThreads), plan->tile_lds[1], stream,
-                               plan->d_segs, plan->d_tile_seg, plan->d_vtiles[1], residue, dW, m8,
-                               stage, tile_cnt, tile_gsum, bin_max_out);
-        if ((st = launch_status()) != ADACOMP_OK) return st;
+        for (int v = 0; v < adacomp::kVariants; ++v) {
+            if (L.tiles_by_variant[v].empty()) continue;
+            hipError_t e;
+            if (v == 0)
+                e = adacomp::launch_tile_pass<0>(plan, stream, residue, dW, m8, stage, tile_cnt,
+                                                 tile_gsum, bin_max_out);
+            else if (v == 1)
+                e = adacomp::launch_tile_pass<1>(plan, stream, residue, dW, m8, stage, tile_cnt,
+                                                 tile_gsum, bin_max_out);
+            else
+                e = adacomp::launch_tile_pass<2>(plan, stream, residue, dW, m8, stage, tile_cnt,
+                                                 tile_gsum, bin_max_out);
+            if (e != hipSuccess) return ADACOMP_ERR_HIP;
+        }
         tm.stop();
     }
     {
@@ -307,9 +327,12 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     }
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_ENCODE);
-        hipLaunchKernelGGL(adacomp::k_encode, dim3(static_cast<uint32_t>(L.ntiles)), dim3(256), 0,
-                           stream, plan->d_segs, plan->d_tile_seg, stage, tile_cnt, tile_off,
-                           chunk_base, seg_s, seg_eoff, m8, residue);
+        hipLaunchKernelGGL(adacomp::k_encode,
+                           dim3(static_cast<uint32_t>((L.ntiles + 4 * adacomp::kEncTiles - 1) /
+                                                      (4 * adacomp::kEncTiles))),
+                           dim3(256),
+                           0, stream, plan->d_segs, plan->d_tile_seg, stage, tile_cnt, tile_off,
+                           chunk_base, seg_s, seg_eoff, m8, residue, static_cast<uint32_t>(L.ntiles));
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.stop();
     }
@@ -379,25 +402,23 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
     }
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_APPLY);
-        const uint32_t n0 = static_cast<uint32_t>(L.tiles_by_variant[0].size());
-        const uint32_t n1 = static_cast<uint32_t>(L.tiles_by_variant[1].size());
-        if (n0) {
-            const uint32_t acc_words = L.max_span_vecs[0] * 4;
-            const uint32_t ps = L.max_bpt[0] + 1;
+        for (int v = 0; v < adacomp::kVariants; ++v) {
+            const uint32_t n = static_cast<uint32_t>(L.tiles_by_variant[v].size());
+            if (n == 0) continue;
+            const uint32_t ps = L.max_bpt[v] + 1;
             const uint32_t KG = std::max<uint32_t>(1, std::min<uint32_t>(K, adacomp::kPrefWords / ps));
-            const uint32_t lds = (acc_words + KG * ps) * 4;
-            hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, 4>), dim3(n0), dim3(256), lds,
-                               stream, mp, K, KG, plan->d_segs, plan->d_tile_seg,
-                               plan->d_vtiles[0], T, C, L.nseg, dw, out, accumulate, acc_words);
-            if ((st = launch_status()) != ADACOMP_OK) return st;
-        }
-        if (n1) {
-            const uint32_t ps = L.max_bpt[1] + 1;
-            const uint32_t KG = std::max<uint32_t>(1, std::min<uint32_t>(K, adacomp::kPrefWords / ps));
-            const uint32_t lds = KG * ps * 4;
-            hipLaunchKernelGGL((adacomp::k_decode_apply<1024, false, 2>), dim3(n1), dim3(1024), lds,
-                               stream, mp, K, KG, plan->d_segs, plan->d_tile_seg,
-                               plan->d_vtiles[1], T, C, L.nseg, dw, out, accumulate, 0u);
+            if (v < 2) {   // the tile fits in LDS
+                const uint32_t acc_words = L.max_span_vecs[v] * 4;
+                const uint32_t lds = (acc_words + KG * ps) * 4;
+                hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, 4>), dim3(n), dim3(256), lds,
+                                   stream, mp, K, KG, plan->d_segs, plan->d_tile_seg,
+                                   plan->d_vtiles[v], T, C, L.nseg, dw, out, accumulate, acc_words);
+            } else {       // large tiles accumulate in place in out
+                const uint32_t lds = KG * ps * 4;
+                hipLaunchKernelGGL((adacomp::k_decode_apply<1024, false, 2>), dim3(n), dim3(1024), lds,
+                                   stream, mp, K, KG, plan->d_segs, plan->d_tile_seg,
+                                   plan->d_vtiles[v], T, C, L.nseg, dw, out, accumulate, 0u);
+            }
             if ((st = launch_status()) != ADACOMP_OK) return st;
         }
         tm.stop();

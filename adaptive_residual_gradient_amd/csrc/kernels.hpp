@@ -37,11 +37,33 @@ namespace adacomp {
 
 constexpr uint32_t kSentinel = 0xFFFFFFFFu;
 
-__device__ __forceinline__ uint64_t rup16(uint64_t x) { return (x + 15u) & ~uint64_t(15); }
+#ifndef ADACOMP_NT_DW
+#define ADACOMP_NT_DW 1
+#endif
+#ifndef ADACOMP_NT_R
+#define ADACOMP_NT_R 1
+#endif
+#ifndef ADACOMP_NT_ST
+#define ADACOMP_NT_ST 1
+#endif
 
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
-    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming float4 access.  residue and dW are read once and the residue
+// written once per call, so all three use non-temporal accesses (measured
+// fastest on MI355X for this read-read-write stream).
+template <bool NT>
+__device__ __forceinline__ f32x4 load4(const float* p) {
+    if (NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return *reinterpret_cast<const f32x4*>(p);
 }
+template <bool NT>
+__device__ __forceinline__ void store4(float* p, f32x4 v) {
+    if (NT) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+    else *reinterpret_cast<f32x4*>(p) = v;
+}
+
+__device__ __forceinline__ uint64_t rup16(uint64_t x) { return (x + 15u) & ~uint64_t(15); }
 
 __device__ __forceinline__ void put_word(uint8_t* p, uint32_t wb, uint32_t v) {
     if (wb == 1u) *p = static_cast<uint8_t>(v);
@@ -52,82 +74,112 @@ __device__ __forceinline__ uint32_t get_word(const uint8_t* p, uint32_t wb) {
     return wb == 1u ? uint32_t(*p) : uint32_t(*reinterpret_cast<const uint16_t*>(p));
 }
 
-// Exclusive scan of n <= 64*k values in LDS by one wavefront; returns total.
-__device__ __forceinline__ uint32_t wave_exclusive_scan_lds(const uint32_t* in, uint32_t* out,
-                                                            int n, int lane) {
-    uint32_t carry = 0;
-    for (int base = 0; base < n; base += 64) {
-        const int i = base + lane;
-        const uint32_t v = i < n ? in[i] : 0u;
-        uint32_t inc = v;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t t = __shfl_up(inc, d);
-            if (lane >= d) inc += t;
-        }
-        if (i < n) out[i] = carry + inc - v;
-        carry += __shfl(inc, 63);
-    }
-    return carry;
-}
-
 // ---------------------------------------------------------------------------
 // Compress, dense tile pass.
 // ---------------------------------------------------------------------------
+constexpr uint32_t kNoKey = 0xFFFFFFFEu;   // never a bin index nor kSentinel
+
+// DPP lane moves (VALU, no LDS round trip).  Lanes without a source, and
+// lanes of rows masked off, receive `old`.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROWS, 0xf, false));
+}
+// lane l receives lane l+1 (wave_shl:1); lane 63 receives old
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t old, uint32_t v) { return dpp_u32<0x130>(old, v); }
+// lane l receives lane l-1 (wave_shr:1); lane 0 receives old
+__device__ __forceinline__ uint32_t from_prev_lane(uint32_t old, uint32_t v) { return dpp_u32<0x138>(old, v); }
+
+// Segmented inclusive max-scan across a wavefront: segments are runs of equal
+// key, keys ascending along the lanes.  Each lane gets the max of val over
+// lanes [start of its run, lane].  Row shifts 1, 2, 4, 8 scan within rows of
+// 16 lanes; the row broadcasts of lanes 15/47 and then 31 carry across rows.
+__device__ __forceinline__ uint32_t seg_max_scan(uint32_t key, uint32_t val) {
+#define ADACOMP_SEG_STEP(CTRL, ROWS)                                   \
+    {                                                                   \
+        const uint32_t k2 = dpp_u32<CTRL, ROWS>(kNoKey, key);          \
+        const uint32_t v2 = dpp_u32<CTRL, ROWS>(0u, val);              \
+        if (k2 == key) val = max(val, v2);                              \
+    }
+    ADACOMP_SEG_STEP(0x111, 0xf)
+    ADACOMP_SEG_STEP(0x112, 0xf)
+    ADACOMP_SEG_STEP(0x114, 0xf)
+    ADACOMP_SEG_STEP(0x118, 0xf)
+    ADACOMP_SEG_STEP(0x142, 0xa)
+    ADACOMP_SEG_STEP(0x143, 0xc)
+#undef ADACOMP_SEG_STEP
+    return val;
+}
+
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// One tile's inputs held in registers: residue and dW of VPT float4 per thread.
+template <int VPT>
+struct TileRegs {
+    TileGeom tg;
+    uint32_t tile;
+    float rr[VPT][4];
+    float dw[VPT][4];
+};
+
+// Issues the tile's loads without branches, so that the compiler can keep a
+// prefetched tile in flight: every lane loads whole float4 (lanes past the
+// tile reload its last float4).  Elements outside the tile are loaded but
+// masked later; the flat buffers are padded to a multiple of 4 elements, so
+// every float4 is inside them.
 template <int THREADS, int VPT>
-__global__ void __launch_bounds__(THREADS)
-k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
-            const uint32_t* __restrict__ vtiles, float* __restrict__ residue,
-            const float* __restrict__ dW, uint8_t* __restrict__ msg,
-            uint2* __restrict__ stage, uint32_t* __restrict__ tile_cnt,
-            double* __restrict__ tile_gsum, float* __restrict__ bin_max_out) {
+__device__ __forceinline__ void load_tile(TileRegs<VPT>& t, const SegDev* __restrict__ segs,
+                                          const uint32_t* __restrict__ tile_seg,
+                                          const uint32_t* __restrict__ vtiles, uint32_t it,
+                                          const float* __restrict__ residue,
+                                          const float* __restrict__ dW) {
+    const int tid = threadIdx.x;
+    t.tile = vtiles[it];
+    const SegDev& sg = segs[tile_seg[t.tile]];
+    t.tg = tile_geom(sg, t.tile);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const uint32_t vi = min(uint32_t(v * THREADS + tid), t.tg.nvec - 1u);
+        const uint64_t e0 = t.tg.v0 + uint64_t(vi) * 4u;
+        const f32x4 a = load4<ADACOMP_NT_R>(residue + e0);
+        const f32x4 b = load4<ADACOMP_NT_DW>(dW + e0);
+        t.rr[v][0] = a.x; t.rr[v][1] = a.y; t.rr[v][2] = a.z; t.rr[v][3] = a.w;
+        t.dw[v][0] = b.x; t.dw[v][1] = b.y; t.dw[v][2] = b.z; t.dw[v][3] = b.w;
+    }
+}
+
+// Everything a tile does after its inputs arrived.  lds: this tile's
+// [2*bpt_max+1] words (bin maxima, then bin boundaries).
+template <int THREADS, int VPT>
+__device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* lds,
+                                             const SegDev* __restrict__ segs,
+                                             const uint32_t* __restrict__ tile_seg,
+                                             float* __restrict__ residue, uint8_t* __restrict__ msg,
+                                             uint2* __restrict__ stage,
+                                             uint32_t* __restrict__ tile_cnt,
+                                             double* __restrict__ tile_gsum,
+                                             float* __restrict__ bin_max_out,
+                                             uint32_t* ch_tot) {
     constexpr int NW = THREADS / 64;
     constexpr int NCH = NW * VPT;   // wavefront chunks of 256 elements per tile
-    extern __shared__ uint32_t dyn[];
-    __shared__ uint32_t ch_tot[NCH];
-    __shared__ uint32_t ch_base[NCH];
-    __shared__ uint32_t s_total;
-
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const uint32_t tile = vtiles[blockIdx.x];
-    const SegDev sg = segs[tile_seg[tile]];
-    const TileGeom tg = tile_geom(sg, tile);
+    const TileGeom& tg = in.tg;
+    const SegDev sg = segs[tile_seg[in.tile]];
     const uint32_t lt = sg.lt, magic = sg.magic;
-    uint32_t* smax = dyn;                 // [bpt] bin maxima as float bits
-    uint32_t* sbound = dyn + sg.bpt;      // [bpt + 1] survivors before each bin
+    uint32_t* smax = lds;                 // [bpt] bin maxima as float bits
+    uint32_t* sbound = lds + sg.bpt;      // [bpt + 1] survivors before each bin
 
     for (uint32_t b = tid; b < tg.nb; b += THREADS) smax[b] = 0u;
 
-    float g[VPT][4], dd[VPT][4];
+    float g[VPT][4];
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-        const int vi = v * THREADS + tid;
-        const int x0 = vi * 4 - int(tg.lead);
-        float rr[4] = {0.f, 0.f, 0.f, 0.f}, dw[4] = {0.f, 0.f, 0.f, 0.f};
-        if (vi < int(tg.nvec)) {
-            const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
-            if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
-                const float4 a = *reinterpret_cast<const float4*>(residue + e0);
-                const float4 b = *reinterpret_cast<const float4*>(dW + e0);
-                rr[0] = a.x; rr[1] = a.y; rr[2] = a.z; rr[3] = a.w;
-                dw[0] = b.x; dw[1] = b.y; dw[2] = b.z; dw[3] = b.w;
-            } else {
+    for (int v = 0; v < VPT; ++v)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int x = x0 + c;
-                    if (x >= 0 && x < int(tg.tlen)) {
-                        rr[c] = residue[e0 + c];
-                        dw[c] = dW[e0 + c];
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            g[v][c] = rr[c] + dw[c];     // G = residue + dW
-            dd[v][c] = dw[c];
-        }
-    }
+        for (int c = 0; c < 4; ++c) g[v][c] = in.rr[v][c] + in.dw[v][c];   // G = residue + dW
     __syncthreads();   // smax cleared
 
     // ---- bin maxima: g_max(i) = max |G| over bin i ----
@@ -152,25 +204,15 @@ k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_s
             }
             const bool two = hb != tb;
             // The head run of a two-run lane continues the previous lane's
-            // tail run: fold it there; a lane whose head starts a wave emits it.
-            const uint32_t ptb = __shfl_up(tb, 1);
-            const bool covered = two && lane > 0 && ptb == hb;
-            if (two && !covered) atomicMax(&smax[hb], mh);
-            const uint32_t nhb = __shfl_down(hb, 1);
-            const uint32_t nmh = __shfl_down(mh, 1);
-            const uint32_t ntwo = __shfl_down(uint32_t(two), 1);
-            if (lane < 63 && ntwo && nhb == tb) mt = max(mt, nmh);
-            // Segmented inclusive max-scan of the tail runs (bins ascend
-            // along the lanes, so equal keys are contiguous).
-            uint32_t val = mt;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const uint32_t k2 = __shfl_up(tb, d);
-                const uint32_t v2 = __shfl_up(val, d);
-                if (lane >= d && k2 == tb) val = max(val, v2);
-            }
-            const uint32_t nkey = __shfl_down(tb, 1);
-            if ((lane == 63 || nkey != tb) && tb != kSentinel) atomicMax(&smax[tb], val);
+            // tail run: fold it there; otherwise the lane emits it itself.
+            const uint32_t ptb = from_prev_lane(kNoKey, tb);
+            if (two && ptb != hb) atomicMax(&smax[hb], mh);
+            const uint32_t nhb = from_next_lane(kNoKey, two ? hb : kNoKey);
+            const uint32_t nmh = from_next_lane(0u, mh);
+            if (nhb == tb) mt = max(mt, nmh);
+            const uint32_t val = seg_max_scan(tb, mt);
+            const uint32_t nkey = from_next_lane(kNoKey, tb);
+            if (nkey != tb && tb != kSentinel) atomicMax(&smax[tb], val);
         }
     } else {
 #pragma unroll
@@ -201,24 +243,29 @@ k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_s
             const int x = x0 + c;
             if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen)) {
                 const float gm = __uint_as_float(smax[div_bin(uint32_t(x), lt, magic)]);
-                const float h = g[v][c] + dd[v][c];      // H = G + dW
+                const float h = g[v][c] + in.dw[v][c];      // H = G + dW
                 if (fabsf(h) >= gm && g[v][c] != 0.0f) m |= 1u << c;
             }
         }
         sel[v] = m;
-        const uint64_t lm = lanemask_lt(lane);
         const uint64_t b0 = __ballot(m & 1u), b1 = __ballot(m & 2u);
         const uint64_t b2 = __ballot(m & 4u), b3 = __ballot(m & 8u);
-        wrank[v] = __popcll(b0 & lm) + __popcll(b1 & lm) + __popcll(b2 & lm) + __popcll(b3 & lm);
+        wrank[v] = mbcnt64(b0) + mbcnt64(b1) + mbcnt64(b2) + mbcnt64(b3);
         if (lane == 0) ch_tot[v * NW + wv] = __popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3);
     }
     __syncthreads();
-    if (wv == 0) {
-        const uint32_t tot = wave_exclusive_scan_lds(ch_tot, ch_base, NCH, lane);
-        if (lane == 0) s_total = tot;
+    uint32_t total = 0;
+    uint32_t cbase[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) cbase[v] = 0;
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+        const uint32_t t = ch_tot[q];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+            if (q < v * NW + wv) cbase[v] += t;
+        total += t;
     }
-    __syncthreads();
-    const uint32_t total = s_total;
 
     // ---- survivors to staging, bin boundaries, residue <- G ----
     uint2* st = stage + tg.t0;
@@ -227,7 +274,7 @@ k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_s
         const int vi = v * THREADS + tid;
         const int x0 = vi * 4 - int(tg.lead);
         if (vi >= int(tg.nvec)) continue;
-        uint32_t r = ch_base[v * NW + wv] + wrank[v];
+        uint32_t r = cbase[v] + wrank[v];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int x = x0 + c;
@@ -243,7 +290,9 @@ k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_s
         }
         const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
         if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
-            *reinterpret_cast<float4*>(residue + e0) = make_float4(g[v][0], g[v][1], g[v][2], g[v][3]);
+            f32x4 o;
+            o.x = g[v][0]; o.y = g[v][1]; o.z = g[v][2]; o.w = g[v][3];
+            store4<ADACOMP_NT_ST>(residue + e0, o);
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -261,16 +310,39 @@ k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_s
         put_word(cw + uint64_t(b) * sg.wb, sg.wb, sbound[b + 1] - sbound[b]);
         if (bin_max_out) bin_max_out[sg.bin_base + tg.first_bin + b] = __uint_as_float(smax[b]);
     }
-    if (wv == 0) {
+    if (wv == NW - 1) {
+        // float64 sum of the tile's bin maxima in a fixed order
         double acc = 0.0;
-        for (uint32_t b = lane; b < tg.nb; b += 64) acc += double(__uint_as_float(smax[b]));
+        if (tg.nb <= 64) {
+            if (lane == 0)
+                for (uint32_t b = 0; b < tg.nb; ++b) acc += double(__uint_as_float(smax[b]));
+        } else {
+            for (uint32_t b = lane; b < tg.nb; b += 64) acc += double(__uint_as_float(smax[b]));
 #pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+            for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+        }
         if (lane == 0) {
-            tile_gsum[tile] = acc;
-            tile_cnt[tile] = total;
+            tile_gsum[in.tile] = acc;
+            tile_cnt[in.tile] = total;
         }
     }
+}
+
+// One workgroup per tile.
+template <int THREADS, int VPT>
+__global__ void __launch_bounds__(THREADS)
+k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
+            const uint32_t* __restrict__ vtiles, float* __restrict__ residue,
+            const float* __restrict__ dW, uint8_t* __restrict__ msg, uint2* __restrict__ stage,
+            uint32_t* __restrict__ tile_cnt, double* __restrict__ tile_gsum,
+            float* __restrict__ bin_max_out) {
+    constexpr int NCH = (THREADS / 64) * VPT;
+    extern __shared__ uint32_t dyn[];
+    __shared__ uint32_t ch_tot[NCH];
+    TileRegs<VPT> a;
+    load_tile<THREADS, VPT>(a, segs, tile_seg, vtiles, blockIdx.x, residue, dW);
+    process_tile<THREADS, VPT>(a, dyn, segs, tile_seg, residue, msg, stage, tile_cnt, tile_gsum,
+                               bin_max_out, ch_tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -420,34 +492,71 @@ k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
     }
 }
 
-// Encode + residue fix-up: one 256-thread block per tile.
+// Encode + residue fix-up.  Each wavefront covers 64 consecutive tiles: lane
+// i reads tile i's metadata, a wavefront scan of the survivor counts flattens
+// the 64 tiles' survivors, and the lanes then walk them 64 at a time, so one
+// round of metadata latency serves ~64 tiles.
+constexpr uint32_t kEncTiles = 64;
+
 __global__ void __launch_bounds__(256)
 k_encode(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
          const uint2* __restrict__ stage, const uint32_t* __restrict__ tile_cnt,
          const uint32_t* __restrict__ tile_off, const uint32_t* __restrict__ chunk_base,
          const float* __restrict__ seg_s, const uint64_t* __restrict__ seg_eoff,
-         uint8_t* __restrict__ msg, float* __restrict__ residue) {
-    const uint32_t tile = blockIdx.x;
-    const uint32_t cnt = tile_cnt[tile];
-    if (cnt == 0) return;
-    const uint32_t si = tile_seg[tile];
-    const SegDev sg = segs[si];
-    const TileGeom tg = tile_geom(sg, tile);
-    const uint32_t chunk = sg.chunk_begin + (tile - sg.tile_begin) / kChunkTiles;
-    const uint64_t base = uint64_t(chunk_base[chunk]) + tile_off[tile];
-    const float s = seg_s[si];
-    uint8_t* ew = msg + seg_eoff[si] + base * sg.wb;
-    const uint2* st = stage + tg.t0;
-    const uint32_t topbit = sg.wb == 1u ? 7u : 15u;
-    for (uint32_t e = threadIdx.x; e < cnt; e += 256) {
-        const uint2 p = st[e];
+         uint8_t* __restrict__ msg, float* __restrict__ residue, uint32_t ntiles) {
+    __shared__ uint32_t pre[4][kEncTiles + 1];
+    __shared__ uint64_t t0s[4][kEncTiles];
+    __shared__ uint64_t eat[4][kEncTiles];     // byte offset of the tile's first entry word
+    __shared__ float ss[4][kEncTiles];
+    __shared__ uint32_t lts[4][kEncTiles], mags[4][kEncTiles], wbs[4][kEncTiles];
+    const uint32_t lane = threadIdx.x & 63u, wv = threadIdx.x >> 6;
+    const uint32_t tile = (blockIdx.x * 4u + wv) * kEncTiles + lane;
+    uint32_t cnt = 0;
+    if (tile < ntiles) {
+        cnt = tile_cnt[tile];
+        if (cnt) {
+            const uint32_t si = tile_seg[tile];
+            const SegDev sg = segs[si];
+            const TileGeom tg = tile_geom(sg, tile);
+            const uint32_t chunk = sg.chunk_begin + (tile - sg.tile_begin) / kChunkTiles;
+            const uint64_t base = uint64_t(chunk_base[chunk]) + tile_off[tile];
+            t0s[wv][lane] = tg.t0;
+            eat[wv][lane] = seg_eoff[si] + base * sg.wb;
+            ss[wv][lane] = seg_s[si];
+            lts[wv][lane] = sg.lt;
+            mags[wv][lane] = sg.magic;
+            wbs[wv][lane] = sg.wb;
+        }
+    }
+    uint32_t inc = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t t = __shfl_up(inc, d);
+        if (lane >= uint32_t(d)) inc += t;
+    }
+    pre[wv][lane + 1] = inc;
+    if (lane == 0) pre[wv][0] = 0;
+    __syncthreads();
+    const uint32_t E = pre[wv][kEncTiles];
+    for (uint32_t e = lane; e < E; e += 64) {
+        uint32_t lo = 0, hi = kEncTiles;   // pre[lo] <= e < pre[hi]
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (pre[wv][mid] <= e) lo = mid; else hi = mid;
+        }
+        const uint32_t r = e - pre[wv][lo];
+        const uint64_t t0 = t0s[wv][lo];
+        const uint32_t lt = lts[wv][lo], wb = wbs[wv][lo];
+        const uint2 p = stage[t0 + r];
         const uint32_t x = p.x & 0x7FFFFFFFu;
         const uint32_t neg = p.x >> 31;
-        const uint32_t b = div_bin(x, sg.lt, sg.magic);
-        put_word(ew + uint64_t(e) * sg.wb, sg.wb, (neg << topbit) | (x - b * sg.lt));
+        const uint32_t b = div_bin(x, lt, mags[wv][lo]);
+        const uint32_t topbit = wb == 1u ? 7u : 15u;
+        put_word(msg + eat[wv][lo] + uint64_t(r) * wb, wb, (neg << topbit) | (x - b * lt));
         const float gv = __uint_as_float(p.y);
+        const float s = ss[wv][lo];
         // residue <- G - G_q with G_q = sign(G) * s
-        residue[tg.t0 + x] = neg ? gv + s : gv - s;
+        residue[t0 + x] = neg ? gv + s : gv - s;
     }
 }
 

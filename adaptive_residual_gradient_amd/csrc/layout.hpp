@@ -4,10 +4,12 @@
 // Work decomposition.  Each segment (one layer) is cut into tiles of whole
 // bins, so that every bin maximum, survivor count and compaction is local to
 // one workgroup and no cross-workgroup combination is needed for a bin.
-//   - small tiles: 256 threads x 4 float4 per thread per array, at most 4096
-//     elements, for L_T <= 4093;
+//   - narrow tiles: 256 threads x 1 float4 per thread per array, at most 1024
+//     elements (two bins of 500, twenty bins of 50), for L_T <= 1021;
+//   - medium tiles: 256 threads x 4 float4, at most 4096 elements, for
+//     L_T <= 4093;
 //   - large tiles: 1024 threads x 9 float4, at most 36864 elements, for
-//     4093 < L_T <= 32768.
+//     L_T <= 32768.
 // Bins per tile are chosen so that tile starts fall on 16-byte boundaries
 // whenever that fits, which keeps every load and store a whole float4 except
 // at the ends of segments.
@@ -28,12 +30,21 @@
 
 namespace adacomp {
 
-constexpr uint32_t kSmallThreads = 256;
-constexpr uint32_t kSmallVecs = 4;
-constexpr uint32_t kSmallCap = kSmallThreads * kSmallVecs * 4;   // 4096 elements
-constexpr uint32_t kLargeThreads = 1024;
-constexpr uint32_t kLargeVecs = 9;
-constexpr uint32_t kLargeCap = kLargeThreads * kLargeVecs * 4;   // 36864 elements
+// Tile shapes (threads per workgroup x float4 per thread per array).  A
+// layer uses the first shape whose capacity holds one bin plus the up-to-3
+// leading elements of an unaligned tile start.
+#ifndef ADACOMP_NARROW_VECS
+#define ADACOMP_NARROW_VECS 2
+#endif
+#ifndef ADACOMP_NARROW_THREADS
+#define ADACOMP_NARROW_THREADS 256
+#endif
+constexpr int kVariants = 3;
+constexpr uint32_t kVarThreads[kVariants] = {ADACOMP_NARROW_THREADS, 256, 1024};
+constexpr uint32_t kVarVecs[kVariants] = {ADACOMP_NARROW_VECS, 4, 9};
+constexpr uint32_t var_cap(int v) { return kVarThreads[v] * kVarVecs[v] * 4; }
+constexpr uint32_t kMaxCap = 1024 * 9 * 4;   // 36864 elements
+static_assert(var_cap(2) == kMaxCap, "largest tile shape");
 constexpr uint32_t kChunkTiles = 1024;  // tiles per scan chunk (4 per thread of a 256-thread block)
 constexpr uint32_t kPrefWords = 8192;   // LDS words for per-message bin prefixes in decode
 constexpr uint64_t kAlign = 256;        // workspace sub-buffer alignment
@@ -53,7 +64,7 @@ struct SegDev {
     uint32_t chunk_begin;
     uint32_t nchunks;
     uint32_t wb;         // index word bytes: 1 if lt < 64 else 2
-    uint32_t variant;    // 0 small tiles, 1 large tiles
+    uint32_t variant;    // tile shape index
     uint32_t pad[2];
 };
 static_assert(sizeof(SegDev) == 80, "SegDev layout");
@@ -98,12 +109,13 @@ struct Layout {
     uint32_t plan_hash = 0;
     std::vector<SegDev> segs;
     std::vector<uint32_t> tile_seg;          // [T] segment of each tile
-    std::vector<uint32_t> tiles_by_variant[2];
+    std::vector<uint32_t> tiles_by_variant[kVariants];
     std::vector<uint32_t> chunk_tile_begin;  // [C + 1]
     std::vector<uint32_t> chunk_seg;         // [C]
-    uint32_t max_bpt[2] = {0, 0};
-    uint32_t max_span_vecs[2] = {0, 0};      // most float4 one tile touches
-    uint64_t total_numel = 0, span = 0, total_bins = 0;
+    uint32_t max_bpt[kVariants] = {0, 0, 0};
+    uint32_t max_span_vecs[kVariants] = {0, 0, 0};   // most float4 one tile touches
+    uint64_t total_numel = 0, total_bins = 0;
+    uint64_t span = 0;   // max(offset + numel) rounded up to 4: the flat buffers' minimum length
     uint64_t ntiles = 0, nchunks = 0;
     uint64_t counts_begin = 0, entries_begin = 0, capacity = 0;
 
@@ -189,8 +201,10 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
         d.magic = s.bin_len >= 2 ? static_cast<uint32_t>((uint64_t(1) << 32) / s.bin_len + 1) : 0u;
         const uint64_t nb = (s.numel + s.bin_len - 1) / s.bin_len;
         d.nbins = static_cast<uint32_t>(nb);
-        d.variant = s.bin_len <= kSmallCap - 3 ? 0u : 1u;
-        const uint32_t cap = d.variant == 0 ? kSmallCap : kLargeCap;
+        d.variant = kVariants - 1;
+        for (int v = kVariants - 1; v >= 0; --v)
+            if (s.bin_len + 3 <= var_cap(v)) d.variant = uint32_t(v);
+        const uint32_t cap = var_cap(int(d.variant));
         d.bpt = bins_per_tile(s.bin_len, cap, d.nbins);
         d.ntiles = static_cast<uint32_t>((nb + d.bpt - 1) / d.bpt);
         d.wb = s.bin_len < 64 ? 1u : 2u;
@@ -222,7 +236,7 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
         bins += nb;
         count_at = round_up(count_at + nb * d.wb, 16);
         L.total_numel += s.numel;
-        L.span = std::max<uint64_t>(L.span, s.offset + s.numel);
+        L.span = std::max<uint64_t>(L.span, round_up(s.offset + s.numel, 4));
     }
     L.chunk_tile_begin.push_back(static_cast<uint32_t>(tiles));
     L.ntiles = tiles;
@@ -240,7 +254,7 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
         w = round_up(w + bytes, kAlign);
         return at;
     };
-    L.ws_stage = take(8 * round_up(L.span, 4));     // (key, G) pair per possible survivor
+    L.ws_stage = take(8 * L.span);     // (key, G) pair per possible survivor
     L.ws_tile_cnt = take(4 * tiles);
     L.ws_tile_gsum = take(8 * tiles);
     L.ws_tile_off = take(4 * tiles);

@@ -26,8 +26,9 @@
  *     the msgs array are HOST pointers.  The caller owns every buffer.
  *   - The flat float32 buffers (residue, dW, out) hold every layer of the
  *     segment table at its element offset; they must be 16-byte aligned and
- *     hold at least info.span elements.  Elements outside every segment are
- *     never read or written.
+ *     hold at least info.span elements (the end of the last layer rounded up
+ *     to a multiple of 4).  Elements outside every segment may be read but
+ *     are never written.
  *   - msg and ws must be 16-byte aligned and at least as large as the plan
  *     reports.  Buffers given to one call must not overlap.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
@@ -85,7 +86,8 @@ typedef struct adacomp_plan_info {
     uint32_t nseg;
     uint32_t plan_hash;                 /* FNV-1a 32 of the table, as in message headers */
     uint64_t total_numel;               /* sum of numel */
-    uint64_t span;                      /* max(offset + numel): minimum length of residue, dW, out */
+    uint64_t span;                      /* max(offset + numel) rounded up to a multiple of 4:
+                                           the minimum length of residue, dW and out */
     uint64_t total_bins;                /* sum over segments of ceil(numel / bin_len) */
     uint64_t ntiles;                    /* work tiles (whole bins of one segment each) */
     uint64_t header_bytes;              /* 32 + 16*nseg: read this much to learn a message's size */

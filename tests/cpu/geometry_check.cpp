@@ -22,9 +22,6 @@ static std::string check(const std::vector<adacomp_segment>& segs, int expect_st
     const int st = build_layout(segs.data(), static_cast<uint32_t>(segs.size()), L);
     if (st != expect_status) return "FAIL status " + std::to_string(st);
     if (st != ADACOMP_OK) return "OK rejected";
-    const uint32_t caps[2] = {kSmallCap, kLargeCap};
-    const uint32_t threads[2] = {kSmallThreads, kLargeThreads};
-    const uint32_t vecs[2] = {kSmallVecs, kLargeVecs};
     uint64_t tiles_seen = 0;
     for (uint32_t s = 0; s < L.nseg; ++s) {
         const SegDev& d = L.segs[s];
@@ -38,8 +35,14 @@ static std::string check(const std::vector<adacomp_segment>& segs, int expect_st
             if (g.nb == 0 || g.nb > d.bpt || g.tlen == 0) return "FAIL empty tile";
             if (g.t0 + g.tlen > d.off + d.numel) return "FAIL tile past segment end";
             if (g.t0 + g.tlen > L.span) return "FAIL tile past span";
-            if (g.nvec > threads[d.variant] * vecs[d.variant]) return "FAIL vectors exceed threads";
-            if (uint64_t(g.nvec) * 4 > caps[d.variant]) return "FAIL vectors exceed cap";
+            // whole-float4 loads (lanes past the tile reload its last float4)
+            if (g.v0 + 4 * uint64_t(g.nvec) > L.span) return "FAIL float4 past padded span";
+            if (L.span % 4 != 0) return "FAIL span not padded";
+            if (g.nvec > kVarThreads[d.variant] * kVarVecs[d.variant]) return "FAIL vectors exceed threads";
+            if (uint64_t(g.nvec) * 4 > var_cap(int(d.variant))) return "FAIL vectors exceed cap";
+            // the first shape that holds the bin is used
+            for (uint32_t v = 0; v < d.variant; ++v)
+                if (d.lt + 3 <= var_cap(int(v))) return "FAIL shape not the smallest";
             if (g.nvec > L.max_span_vecs[d.variant]) return "FAIL decode LDS too small";
             if (g.lead + g.tlen >= 65536u) return "FAIL offsets exceed 16 bits";
             if ((g.t0 & 3) != g.lead || g.v0 % 4 != 0) return "FAIL lead";
@@ -67,18 +70,25 @@ static std::string check(const std::vector<adacomp_segment>& segs, int expect_st
         }
     }
     if (tiles_seen != L.ntiles || L.chunk_tile_begin.back() != L.ntiles) return "FAIL tile count";
-    if (L.tiles_by_variant[0].size() + L.tiles_by_variant[1].size() != L.ntiles) return "FAIL variants";
     // worst-case message fits its capacity
     uint64_t at = L.entries_begin;
     for (const SegDev& d : L.segs) at = round_up(at + d.numel * d.wb, 16);
     if (at != L.capacity) return "FAIL capacity";
     // staging: survivor slots t0 + rank < t0 + tlen <= span, inside the stage buffer
     if (L.ws_tile_cnt - L.ws_stage < 8 * L.span) return "FAIL stage size";
-    // decode LDS per workgroup (bytes) stays within 64 KiB for the small variant
-    const uint32_t ps = L.max_bpt[0] + 1;
-    const uint32_t kg = std::max<uint32_t>(1, std::min<uint32_t>(ADACOMP_MAX_MESSAGES, kPrefWords / ps));
-    if (L.tiles_by_variant[0].size() && (L.max_span_vecs[0] * 4 + kg * ps) * 4 > 65536) return "FAIL decode LDS";
-    if ((2 * L.max_bpt[0] + 1) * 4 > 65536 || (2 * L.max_bpt[1] + 1) * 4 > 65536) return "FAIL tile LDS";
+    // LDS per workgroup (bytes) stays within 64 KiB: decode keeps narrow and
+    // medium tiles in LDS; the tile pass holds 2*bpt+1 words.
+    uint64_t tiles_in_variants = 0;
+    for (int v = 0; v < kVariants; ++v) {
+        tiles_in_variants += L.tiles_by_variant[v].size();
+        if (L.tiles_by_variant[v].empty()) continue;
+        const uint32_t ps = L.max_bpt[v] + 1;
+        const uint32_t kg = std::max<uint32_t>(1, std::min<uint32_t>(ADACOMP_MAX_MESSAGES, kPrefWords / ps));
+        if (v < 2 && (L.max_span_vecs[v] * 4 + kg * ps) * 4 > 65536) return "FAIL decode LDS";
+        if (v == 2 && kg * ps * 4 > 65536) return "FAIL decode LDS";
+        if ((2 * L.max_bpt[v] + 1) * 4 > 65536) return "FAIL tile LDS";
+    }
+    if (tiles_in_variants != L.ntiles) return "FAIL variants";
     return "OK tiles=" + std::to_string(L.ntiles) + " chunks=" + std::to_string(L.nchunks);
 }
 

@@ -72,7 +72,7 @@ def test_plan_info_matches_format(name):
     wl = W.workload(name)
     info = A.plan_query(wl.segments)
     assert info.nseg == len(wl.segments)
-    assert info.total_numel == wl.numel and info.span == wl.span
+    assert info.total_numel == wl.numel and info.span == W.alloc_len(wl)
     assert info.total_bins == wl.bins
     assert info.header_bytes == 32 + 16 * len(wl.segments)
     assert info.plan_hash == mp.table_hash(wl.segments) == oracle.plan_hash(wl.segments)
@@ -98,7 +98,7 @@ def test_binding_fails_loudly_without_library(monkeypatch):
 # Tile geometry, checked on the CPU with the library's own layout code.
 # --------------------------------------------------------------------------
 
-EDGE_BINS = [1, 2, 3, 4, 5, 7, 8, 50, 63, 64, 65, 127, 500, 1000, 4093, 4094, 4095,
+EDGE_BINS = [1, 2, 3, 4, 5, 7, 8, 50, 63, 64, 65, 127, 500, 1000, 1021, 1022, 1023, 4093, 4094, 4095,
              4096, 5000, 8191, 32765, 32766, 32767, 32768]
 EDGE_NUMEL = [1, 2, 3, 4, 5, 7, 63, 64, 65, 4093, 4096, 4097, 36861, 65537, 100003]
 
