@@ -19,15 +19,20 @@
 using adacomp::Layout;
 using adacomp::SegDev;
 
+// Device copies of one tiling's tables.
+struct DevTiling {
+    uint32_t* tile_seg = nullptr;
+    uint32_t* vtiles[adacomp::kVariants] = {nullptr, nullptr, nullptr};
+    uint32_t* chunk_tile_begin = nullptr;
+    uint32_t* chunk_seg = nullptr;
+};
+
 struct adacomp_plan {
     Layout L;
     int device = -1;
     void* dmem = nullptr;
     SegDev* d_segs = nullptr;
-    uint32_t* d_tile_seg = nullptr;
-    uint32_t* d_vtiles[adacomp::kVariants] = {nullptr, nullptr, nullptr};
-    uint32_t* d_chunk_tile_begin = nullptr;
-    uint32_t* d_chunk_seg = nullptr;
+    DevTiling dct, ddt;                                        // compress and decode tiles
     uint32_t tile_lds_words[adacomp::kVariants] = {0, 0, 0};  // one tile's LDS words
 };
 
@@ -36,10 +41,10 @@ template <int V>
 hipError_t launch_tile_pass(const adacomp_plan* plan, hipStream_t stream, float* residue,
                             const float* dW, uint8_t* msg, uint2* stage, uint32_t* tile_cnt,
                             double* tile_gsum, float* bin_max_out) {
-    const uint32_t n = static_cast<uint32_t>(plan->L.tiles_by_variant[V].size());
+    const uint32_t n = static_cast<uint32_t>(plan->L.ct.by_variant[V].size());
     hipLaunchKernelGGL((k_tile_pass<kVarThreads[V], kVarVecs[V]>), dim3(n), dim3(kVarThreads[V]),
-                       plan->tile_lds_words[V] * 4, stream, plan->d_segs, plan->d_tile_seg,
-                       plan->d_vtiles[V], residue, dW, msg, stage, tile_cnt, tile_gsum,
+                       plan->tile_lds_words[V] * 4, stream, plan->d_segs, plan->dct.tile_seg,
+                       plan->dct.vtiles[V], residue, dW, msg, stage, tile_cnt, tile_gsum,
                        bin_max_out);
     return hipGetLastError();
 }
@@ -117,7 +122,7 @@ DecodeLayout decode_layout(const Layout& L, uint32_t K) {
         w = adacomp::round_up(w + bytes, adacomp::kAlign);
         return at;
     };
-    const uint64_t T = L.ntiles, C = L.nchunks, S = L.nseg;
+    const uint64_t T = L.dt.ntiles, C = L.dt.nchunks, S = L.nseg;
     d.status = take(4);
     d.dcnt = take(4 * K * T);
     d.doff = take(4 * K * T);
@@ -174,10 +179,14 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
         }
         const Layout& L = p->L;
         // Launch limits: total work-items of one launch must fit in 32 bits.
-        bool too_large = L.ntiles * 256ull >= (uint64_t(1) << 32) ||
-                         L.nchunks * 256ull >= (uint64_t(1) << 32);
+        bool too_large = L.ct.ntiles * 256ull >= (uint64_t(1) << 32) ||
+                         L.ct.nchunks * 256ull >= (uint64_t(1) << 32) ||
+                         L.dt.nchunks * 256ull >= (uint64_t(1) << 32);
         for (int v = 0; v < adacomp::kVariants; ++v)
-            too_large |= L.tiles_by_variant[v].size() * uint64_t(adacomp::kVarThreads[v]) >=
+            too_large |= L.ct.by_variant[v].size() * uint64_t(adacomp::kVarThreads[v]) >=
+                         (uint64_t(1) << 32);
+        for (int v = 0; v < adacomp::kDecVariants; ++v)
+            too_large |= L.dt.by_variant[v].size() * uint64_t(adacomp::kDecThreads[v]) >=
                          (uint64_t(1) << 32);
         if (too_large) {
             delete p;
@@ -187,47 +196,50 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
             delete p;
             return ADACOMP_ERR_HIP;
         }
-        const uint64_t b_segs = adacomp::round_up(sizeof(SegDev) * L.nseg, 256);
-        const uint64_t b_ts = adacomp::round_up(4 * L.ntiles, 256);
-        uint64_t b_v[adacomp::kVariants];
-        for (int v = 0; v < adacomp::kVariants; ++v)
-            b_v[v] = adacomp::round_up(4 * L.tiles_by_variant[v].size() + 4, 256);
-        const uint64_t b_ctb = adacomp::round_up(4 * (L.nchunks + 1), 256);
-        const uint64_t b_cs = adacomp::round_up(4 * L.nchunks + 4, 256);
-        uint64_t total = b_segs + b_ts + b_ctb + b_cs;
-        for (int v = 0; v < adacomp::kVariants; ++v) total += b_v[v];
-        std::vector<uint8_t> host(total, 0);
-        uint64_t at = 0;
-        auto put = [&](const void* src, uint64_t bytes, uint64_t room) {
+        // One device allocation holds every table.
+        std::vector<uint8_t> host;
+        auto put = [&host](const void* src, uint64_t bytes) {
+            const uint64_t at = host.size();
+            host.resize(adacomp::round_up(at + bytes + 4, 256), 0);
             if (bytes) std::memcpy(host.data() + at, src, bytes);
-            const uint64_t here = at;
-            at += room;
-            return here;
+            return at;
         };
-        const uint64_t o_segs = put(L.segs.data(), sizeof(SegDev) * L.nseg, b_segs);
-        const uint64_t o_ts = put(L.tile_seg.data(), 4 * L.ntiles, b_ts);
-        uint64_t o_v[adacomp::kVariants];
-        for (int v = 0; v < adacomp::kVariants; ++v)
-            o_v[v] = put(L.tiles_by_variant[v].data(), 4 * L.tiles_by_variant[v].size(), b_v[v]);
-        const uint64_t o_ctb = put(L.chunk_tile_begin.data(), 4 * (L.nchunks + 1), b_ctb);
-        const uint64_t o_cs = put(L.chunk_seg.data(), 4 * L.nchunks, b_cs);
-        if (hipMalloc(&p->dmem, total) != hipSuccess) {
+        struct TilingOffsets {
+            uint64_t ts, v[adacomp::kVariants], ctb, cs;
+        };
+        auto put_tiling = [&](const adacomp::Tiling& T) {
+            TilingOffsets o{};
+            o.ts = put(T.tile_seg.data(), 4 * T.tile_seg.size());
+            for (int v = 0; v < adacomp::kVariants; ++v)
+                o.v[v] = put(T.by_variant[v].data(), 4 * T.by_variant[v].size());
+            o.ctb = put(T.chunk_tile_begin.data(), 4 * T.chunk_tile_begin.size());
+            o.cs = put(T.chunk_seg.data(), 4 * T.chunk_seg.size());
+            return o;
+        };
+        const uint64_t o_segs = put(L.segs.data(), sizeof(SegDev) * L.nseg);
+        const TilingOffsets oc = put_tiling(L.ct), od = put_tiling(L.dt);
+        if (hipMalloc(&p->dmem, host.size()) != hipSuccess) {
+            p->dmem = nullptr;
             delete p;
             return ADACOMP_ERR_HIP;
         }
-        if (hipMemcpy(p->dmem, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+        if (hipMemcpy(p->dmem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
             (void)hipFree(p->dmem);
             delete p;
             return ADACOMP_ERR_HIP;
         }
         uint8_t* base = static_cast<uint8_t*>(p->dmem);
         p->d_segs = reinterpret_cast<SegDev*>(base + o_segs);
-        p->d_tile_seg = reinterpret_cast<uint32_t*>(base + o_ts);
-        for (int v = 0; v < adacomp::kVariants; ++v)
-            p->d_vtiles[v] = reinterpret_cast<uint32_t*>(base + o_v[v]);
-        p->d_chunk_tile_begin = reinterpret_cast<uint32_t*>(base + o_ctb);
-        p->d_chunk_seg = reinterpret_cast<uint32_t*>(base + o_cs);
-        for (int v = 0; v < adacomp::kVariants; ++v) p->tile_lds_words[v] = 2 * L.max_bpt[v] + 1;
+        auto bind = [base](DevTiling& d, const TilingOffsets& o) {
+            d.tile_seg = reinterpret_cast<uint32_t*>(base + o.ts);
+            for (int v = 0; v < adacomp::kVariants; ++v)
+                d.vtiles[v] = reinterpret_cast<uint32_t*>(base + o.v[v]);
+            d.chunk_tile_begin = reinterpret_cast<uint32_t*>(base + o.ctb);
+            d.chunk_seg = reinterpret_cast<uint32_t*>(base + o.cs);
+        };
+        bind(p->dct, oc);
+        bind(p->ddt, od);
+        for (int v = 0; v < adacomp::kVariants; ++v) p->tile_lds_words[v] = 2 * L.ct.max_bpt[v] + 1;
         *out = p;
         return ADACOMP_OK;
     } catch (...) {
@@ -294,7 +306,7 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_TILE_PASS);
         for (int v = 0; v < adacomp::kVariants; ++v) {
-            if (L.tiles_by_variant[v].empty()) continue;
+            if (L.ct.by_variant[v].empty()) continue;
             hipError_t e;
             if (v == 0)
                 e = adacomp::launch_tile_pass<0>(plan, stream, residue, dW, m8, stage, tile_cnt,
@@ -311,8 +323,8 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     }
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_CHUNK_SCAN);
-        hipLaunchKernelGGL(adacomp::k_chunk_scan, dim3(static_cast<uint32_t>(L.nchunks)), dim3(256), 0,
-                           stream, plan->d_chunk_tile_begin, tile_cnt, tile_gsum, tile_off,
+        hipLaunchKernelGGL(adacomp::k_chunk_scan, dim3(static_cast<uint32_t>(L.ct.nchunks)), dim3(256),
+                           0, stream, plan->dct.chunk_tile_begin, tile_cnt, tile_gsum, tile_off,
                            chunk_cnt, chunk_gsum);
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.stop();
@@ -328,11 +340,11 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_ENCODE);
         hipLaunchKernelGGL(adacomp::k_encode,
-                           dim3(static_cast<uint32_t>((L.ntiles + 4 * adacomp::kEncTiles - 1) /
+                           dim3(static_cast<uint32_t>((L.ct.ntiles + 4 * adacomp::kEncTiles - 1) /
                                                       (4 * adacomp::kEncTiles))),
                            dim3(256),
-                           0, stream, plan->d_segs, plan->d_tile_seg, stage, tile_cnt, tile_off,
-                           chunk_base, seg_s, seg_eoff, m8, residue, static_cast<uint32_t>(L.ntiles));
+                           0, stream, plan->d_segs, plan->dct.tile_seg, stage, tile_cnt, tile_off,
+                           chunk_base, seg_s, seg_eoff, m8, residue, static_cast<uint32_t>(L.ct.ntiles));
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.stop();
     }
@@ -383,12 +395,12 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
     dw.dseg_s = reinterpret_cast<float*>(w8 + D.dseg_s);
     dw.dseg_eoff = reinterpret_cast<uint64_t*>(w8 + D.dseg_eoff);
     dw.dvalid = reinterpret_cast<uint32_t*>(w8 + D.dvalid);
-    const uint32_t T = static_cast<uint32_t>(L.ntiles), C = static_cast<uint32_t>(L.nchunks);
+    const uint32_t DT = static_cast<uint32_t>(L.dt.ntiles), DC = static_cast<uint32_t>(L.dt.nchunks);
 
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_COUNT);
-        hipLaunchKernelGGL(adacomp::k_decode_count, dim3(C, K), dim3(256), 0, stream, mp,
-                           plan->d_segs, plan->d_chunk_tile_begin, plan->d_chunk_seg, T, C,
+        hipLaunchKernelGGL(adacomp::k_decode_count, dim3(DC, K), dim3(256), 0, stream, mp,
+                           plan->d_segs, plan->ddt.chunk_tile_begin, plan->ddt.chunk_seg, DT, DC,
                            L.nseg, L.plan_hash, dw);
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.stop();
@@ -396,28 +408,29 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_BASE);
         hipLaunchKernelGGL(adacomp::k_decode_base, dim3(1), dim3(256), 0, stream, mp, K,
-                           plan->d_segs, L.nseg, L.plan_hash, C, dw);
+                           plan->d_segs, L.nseg, L.plan_hash, DC, dw);
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.stop();
     }
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_APPLY);
-        for (int v = 0; v < adacomp::kVariants; ++v) {
-            const uint32_t n = static_cast<uint32_t>(L.tiles_by_variant[v].size());
+        for (int v = 0; v < adacomp::kDecVariants; ++v) {
+            const uint32_t n = static_cast<uint32_t>(L.dt.by_variant[v].size());
             if (n == 0) continue;
-            const uint32_t ps = L.max_bpt[v] + 1;
+            const uint32_t ps = L.dt.max_bpt[v] + 1;
             const uint32_t KG = std::max<uint32_t>(1, std::min<uint32_t>(K, adacomp::kPrefWords / ps));
-            if (v < 2) {   // the tile fits in LDS
-                const uint32_t acc_words = L.max_span_vecs[v] * 4;
+            if (v == 0) {   // the tile fits in LDS
+                const uint32_t acc_words = L.dt.max_span_vecs[0] * 4;
                 const uint32_t lds = (acc_words + KG * ps) * 4;
                 hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, 4>), dim3(n), dim3(256), lds,
-                                   stream, mp, K, KG, plan->d_segs, plan->d_tile_seg,
-                                   plan->d_vtiles[v], T, C, L.nseg, dw, out, accumulate, acc_words);
-            } else {       // large tiles accumulate in place in out
+                                   stream, mp, K, KG, plan->d_segs, plan->ddt.tile_seg,
+                                   plan->ddt.vtiles[0], DT, DC, L.nseg, dw, out, accumulate,
+                                   acc_words);
+            } else {        // one long bin per tile, accumulated in place in out
                 const uint32_t lds = KG * ps * 4;
                 hipLaunchKernelGGL((adacomp::k_decode_apply<1024, false, 2>), dim3(n), dim3(1024), lds,
-                                   stream, mp, K, KG, plan->d_segs, plan->d_tile_seg,
-                                   plan->d_vtiles[v], T, C, L.nseg, dw, out, accumulate, 0u);
+                                   stream, mp, K, KG, plan->d_segs, plan->ddt.tile_seg,
+                                   plan->ddt.vtiles[1], DT, DC, L.nseg, dw, out, accumulate, 0u);
             }
             if ((st = launch_status()) != ADACOMP_OK) return st;
         }

@@ -140,7 +140,7 @@ __device__ __forceinline__ void load_tile(TileRegs<VPT>& t, const SegDev* __rest
     const int tid = threadIdx.x;
     t.tile = vtiles[it];
     const SegDev& sg = segs[tile_seg[t.tile]];
-    t.tg = tile_geom(sg, t.tile);
+    t.tg = tile_geom(sg, sg.ct, t.tile);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const uint32_t vi = min(uint32_t(v * THREADS + tid), t.tg.nvec - 1u);
@@ -171,7 +171,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
     const SegDev sg = segs[tile_seg[in.tile]];
     const uint32_t lt = sg.lt, magic = sg.magic;
     uint32_t* smax = lds;                 // [bpt] bin maxima as float bits
-    uint32_t* sbound = lds + sg.bpt;      // [bpt + 1] survivors before each bin
+    uint32_t* sbound = lds + sg.ct.bpt;      // [bpt + 1] survivors before each bin
 
     for (uint32_t b = tid; b < tg.nb; b += THREADS) smax[b] = 0u;
 
@@ -425,8 +425,8 @@ k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
         const SegDev sg = segs[l];
         double acc = 0.0;
         uint32_t run = 0;
-        for (uint32_t c = 0; c < sg.nchunks; ++c) {
-            const uint32_t ci = sg.chunk_begin + c;
+        for (uint32_t c = 0; c < sg.ct.nchunks; ++c) {
+            const uint32_t ci = sg.ct.chunk_begin + c;
             acc += chunk_gsum[ci];
             chunk_base[ci] = run;
             run += chunk_cnt[ci];
@@ -517,8 +517,8 @@ k_encode(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
         if (cnt) {
             const uint32_t si = tile_seg[tile];
             const SegDev sg = segs[si];
-            const TileGeom tg = tile_geom(sg, tile);
-            const uint32_t chunk = sg.chunk_begin + (tile - sg.tile_begin) / kChunkTiles;
+            const TileGeom tg = tile_geom(sg, sg.ct, tile);
+            const uint32_t chunk = sg.ct.chunk_begin + (tile - sg.ct.tile_begin) / kChunkTiles;
             const uint64_t base = uint64_t(chunk_base[chunk]) + tile_off[tile];
             t0s[wv][lane] = tg.t0;
             eat[wv][lane] = seg_eoff[si] + base * sg.wb;
@@ -561,7 +561,7 @@ k_encode(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
 }
 
 // ---------------------------------------------------------------------------
-// Decode-accumulate.
+// Decode-accumulate, over decode tiles (TileSpec dt of each layer).
 // ---------------------------------------------------------------------------
 struct MsgPtrs {
     const uint8_t* p[ADACOMP_MAX_MESSAGES];
@@ -569,17 +569,15 @@ struct MsgPtrs {
 
 struct DecodeWs {
     uint32_t* status;     // [1]
-    uint32_t* dcnt;       // [K*T]
-    uint32_t* doff;       // [K*T]
-    uint32_t* dchunk_cnt; // [K*C]
-    uint32_t* dchunk_base;// [K*C]
+    uint32_t* dcnt;       // [K*DT]
+    uint32_t* doff;       // [K*DT]
+    uint32_t* dchunk_cnt; // [K*DC]
+    uint32_t* dchunk_base;// [K*DC]
     float* dseg_s;        // [K*nseg]
     uint64_t* dseg_eoff;  // [K*nseg]
     uint32_t* dvalid;     // [K]
 };
 
-// Per (chunk, message): tile survivor counts from the count words, offsets
-// within the chunk, chunk totals.
 __device__ __forceinline__ bool header_matches(const uint8_t* m, uint32_t nseg, uint32_t plan_hash) {
     return *reinterpret_cast<const uint32_t*>(m) == 0x43414441u &&
            *reinterpret_cast<const uint16_t*>(m + 4) == 1 &&
@@ -587,10 +585,12 @@ __device__ __forceinline__ bool header_matches(const uint8_t* m, uint32_t nseg, 
            *reinterpret_cast<const uint32_t*>(m + 12) == plan_hash;
 }
 
+// Per (chunk of decode tiles, message): survivors of each decode tile from
+// the count words, offsets within the chunk, chunk totals.
 __global__ void __launch_bounds__(256)
 k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
                const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ chunk_seg,
-               uint32_t T, uint32_t C, uint32_t nseg, uint32_t plan_hash, DecodeWs ws) {
+               uint32_t DT, uint32_t DC, uint32_t nseg, uint32_t plan_hash, DecodeWs ws) {
     __shared__ uint32_t lw[4];
     const uint32_t c = blockIdx.x, k = blockIdx.y;
     const uint8_t* m = msgs.p[k];
@@ -605,8 +605,8 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
         const uint32_t t = threadIdx.x * 4u + i;
         uint32_t s = 0;
         if (ok && t < n) {
-            const uint32_t first_bin = (tb + t - sg.tile_begin) * sg.bpt;
-            const uint32_t nb = min(sg.bpt, sg.nbins - first_bin);
+            const uint32_t first_bin = (tb + t - sg.dt.tile_begin) * sg.dt.bpt;
+            const uint32_t nb = min(sg.dt.bpt, sg.nbins - first_bin);
             const uint8_t* cw = m + sg.count_off + uint64_t(first_bin) * sg.wb;
             for (uint32_t b = 0; b < nb; ++b) s += get_word(cw + uint64_t(b) * sg.wb, sg.wb);
         }
@@ -619,18 +619,18 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
     for (int i = 0; i < 4; ++i) {
         const uint32_t t = threadIdx.x * 4u + i;
         if (t < n) {
-            ws.dcnt[uint64_t(k) * T + tb + t] = cnt[i];
-            ws.doff[uint64_t(k) * T + tb + t] = run;
+            ws.dcnt[uint64_t(k) * DT + tb + t] = cnt[i];
+            ws.doff[uint64_t(k) * DT + tb + t] = run;
         }
         run += cnt[i];
     }
-    if (threadIdx.x == 0) ws.dchunk_cnt[uint64_t(k) * C + c] = total;
+    if (threadIdx.x == 0) ws.dchunk_cnt[uint64_t(k) * DC + c] = total;
 }
 
 // One block: message validity, per-segment s and entry offsets, chunk bases.
 __global__ void __launch_bounds__(256)
 k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, uint32_t nseg,
-              uint32_t plan_hash, uint32_t C, DecodeWs ws) {
+              uint32_t plan_hash, uint32_t DC, DecodeWs ws) {
     __shared__ uint32_t valid[ADACOMP_MAX_MESSAGES];
     __shared__ uint32_t bad;
     if (threadIdx.x == 0) bad = 0;
@@ -655,8 +655,8 @@ k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, uint32_
         ws.dseg_eoff[i] = eoff;
         const SegDev sg = segs[l];
         uint32_t run = 0;
-        for (uint32_t c = 0; c < sg.nchunks; ++c) {
-            const uint64_t ci = uint64_t(k) * C + sg.chunk_begin + c;
+        for (uint32_t c = 0; c < sg.dt.nchunks; ++c) {
+            const uint64_t ci = uint64_t(k) * DC + sg.dt.chunk_begin + c;
             ws.dchunk_base[ci] = run;
             run += ws.dchunk_cnt[ci];
         }
@@ -665,41 +665,62 @@ k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, uint32_
     if (threadIdx.x == 0) *ws.status = bad;
 }
 
-// Per tile: out[j] = (accumulate ? out[j] : +0) + q_0[j] + q_1[j] + ... in
-// message order, only at transmitted j.  LDS_ACC keeps the tile in LDS;
-// otherwise the tile is accumulated in place in out (large tiles).
+// Index word at byte address a (w = 8 or 16 bits), read as the aligned
+// 16-bit word that contains it; messages are 16-byte aligned and padded to a
+// multiple of 16 bytes, so the read stays inside the message.
+__device__ __forceinline__ uint32_t word_at(uint64_t a, uint32_t wb) {
+    const uint32_t w16 = *reinterpret_cast<const uint16_t*>(a & ~uint64_t(1));
+    return wb == 1u ? (w16 >> (8u * uint32_t(a & 1u))) & 0xFFu : w16;
+}
+
+// Per decode tile: out[j] = (accumulate ? out[j] : +0) + q_0[j] + q_1[j] + ...
+// in message order, only at transmitted j.  LDS_ACC keeps the tile in LDS;
+// otherwise (bins longer than 4093) the tile is accumulated in place in out.
+// Messages are taken in groups of KG (their bin prefixes fill the LDS words
+// given at launch); each group's entries are gathered in windows of
+// THREADS*EPT: addresses first, then all loads, then the additions, message
+// by message, with a barrier between messages.
 template <int THREADS, bool LDS_ACC, int EPT>
 __global__ void __launch_bounds__(THREADS)
 k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__ segs,
                const uint32_t* __restrict__ tile_seg, const uint32_t* __restrict__ vtiles,
-               uint32_t T, uint32_t C, uint32_t nseg, DecodeWs ws, float* __restrict__ out,
+               uint32_t DT, uint32_t DC, uint32_t nseg, DecodeWs ws, float* __restrict__ out,
                int accumulate, uint32_t acc_words) {
+    constexpr int NW = THREADS / 64;
     extern __shared__ uint32_t dyn[];
-    __shared__ uint32_t fk[ADACOMP_MAX_MESSAGES + 1];      // flat entry prefix over messages
-    __shared__ uint64_t ebase[ADACOMP_MAX_MESSAGES];       // byte offset of the tile's entries
+    __shared__ uint64_t mbase[ADACOMP_MAX_MESSAGES];      // message base addresses
+    __shared__ uint64_t eaddr[ADACOMP_MAX_MESSAGES];      // address of the tile's first entry
+    __shared__ uint32_t fk[ADACOMP_MAX_MESSAGES + 1];     // flat entry prefix over messages
     __shared__ float ks[ADACOMP_MAX_MESSAGES];
+    __shared__ uint32_t kvalid[ADACOMP_MAX_MESSAGES];
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint32_t tile = vtiles[blockIdx.x];
     const uint32_t si = tile_seg[tile];
     const SegDev sg = segs[si];
-    const TileGeom tg = tile_geom(sg, tile);
-    const uint32_t chunk = sg.chunk_begin + (tile - sg.tile_begin) / kChunkTiles;
+    const TileGeom tg = tile_geom(sg, sg.dt, tile);
+    const uint32_t chunk = sg.dt.chunk_begin + (tile - sg.dt.tile_begin) / kChunkTiles;
     float* acc = LDS_ACC ? reinterpret_cast<float*>(dyn) : out + tg.v0;
     uint32_t* pref = dyn + (LDS_ACC ? acc_words : 0u);    // [KG][bpt + 1]
-    const uint32_t pstride = sg.bpt + 1;
+    const uint32_t pstride = sg.dt.bpt + 1;
+    const uint32_t wb = sg.wb, lt = sg.lt;
+    const uint32_t topbit = wb == 1u ? 7u : 15u;
 
+    for (uint32_t k = tid; k < K; k += THREADS) {
+        mbase[k] = reinterpret_cast<uint64_t>(msgs.p[k]);
+        kvalid[k] = ws.dvalid[k];
+    }
     // Initial values: +0, or out.
     for (uint32_t vi = tid; vi < tg.nvec; vi += THREADS) {
         const int x0 = int(vi * 4) - int(tg.lead);
         const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
         if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
             if (LDS_ACC) {
-                float4 a = accumulate ? *reinterpret_cast<const float4*>(out + e0)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
-                *reinterpret_cast<float4*>(acc + vi * 4) = a;
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                if (accumulate) a = load4<true>(out + e0);
+                *reinterpret_cast<f32x4*>(acc + vi * 4) = a;
             } else if (!accumulate) {
-                *reinterpret_cast<float4*>(out + e0) = make_float4(0.f, 0.f, 0.f, 0.f);
+                store4<false>(out + e0, f32x4{0.f, 0.f, 0.f, 0.f});
             }
         } else {
             for (int c = 0; c < 4; ++c) {
@@ -720,48 +741,69 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__
             const uint32_t kk = i / tg.nb, b = i - kk * tg.nb;
             const uint32_t k = k0 + kk;
             uint32_t cw = 0;
-            if (ws.dvalid[k])
-                cw = get_word(msgs.p[k] + sg.count_off + uint64_t(tg.first_bin + b) * sg.wb, sg.wb);
+            if (kvalid[k]) {
+                const uint64_t a = mbase[k] + sg.count_off + uint64_t(tg.first_bin + b) * wb;
+                cw = word_at(a, wb);
+            }
             pref[kk * pstride + b + 1] = cw;
         }
         if (tid < int(kn)) {
             const uint32_t k = k0 + tid;
-            const uint64_t kt = uint64_t(k) * T + tile;
-            const uint64_t base = uint64_t(ws.dchunk_base[uint64_t(k) * C + chunk]) + ws.doff[kt];
-            ebase[tid] = ws.dseg_eoff[uint64_t(k) * nseg + si] + base * sg.wb;
+            const uint64_t kt = uint64_t(k) * DT + tile;
+            const uint64_t base = uint64_t(ws.dchunk_base[uint64_t(k) * DC + chunk]) + ws.doff[kt];
+            eaddr[tid] = mbase[k] + ws.dseg_eoff[uint64_t(k) * nseg + si] + base * wb;
             ks[tid] = ws.dseg_s[uint64_t(k) * nseg + si];
         }
         __syncthreads();
-        if (tid < int(kn)) {
-            uint32_t* pr = pref + tid * pstride;
-            uint32_t run = 0;
-            pr[0] = 0;
-            for (uint32_t b = 0; b < tg.nb; ++b) {
-                run += pr[b + 1];
-                pr[b + 1] = run;
+        // Per-message exclusive prefix over the tile's bins: one wavefront
+        // per message, 64 bins at a time.
+        for (uint32_t kk = wv; kk < kn; kk += NW) {
+            uint32_t* pr = pref + kk * pstride;
+            uint32_t carry = 0;
+            for (uint32_t b0 = 0; b0 < tg.nb; b0 += 64) {
+                const uint32_t b = b0 + lane;
+                const uint32_t v = b < tg.nb ? pr[b + 1] : 0u;
+                uint32_t inc = v;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const uint32_t t = __shfl_up(inc, d);
+                    if (lane >= d) inc += t;
+                }
+                if (b < tg.nb) pr[b + 1] = carry + inc;
+                carry += __shfl(inc, 63);
             }
+            if (lane == 0) pr[0] = 0;
         }
         __syncthreads();
-        if (tid == 0) {
-            uint32_t run = 0;
-            for (uint32_t kk = 0; kk < kn; ++kk) {
-                fk[kk] = run;
-                run += pref[kk * pstride + tg.nb];
+        if (wv == 0) {
+            uint32_t carry = 0;
+            for (uint32_t k1 = 0; k1 < kn; k1 += 64) {
+                const uint32_t kk = k1 + lane;
+                const uint32_t v = kk < kn ? pref[kk * pstride + tg.nb] : 0u;
+                uint32_t inc = v;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const uint32_t t = __shfl_up(inc, d);
+                    if (lane >= d) inc += t;
+                }
+                if (kk < kn) fk[kk] = carry + inc - v;
+                carry += __shfl(inc, 63);
             }
-            fk[kn] = run;
+            if (lane == 0) fk[kn] = carry;
         }
         __syncthreads();
         const uint32_t E = fk[kn];
-        const uint32_t topbit = sg.wb == 1u ? 7u : 15u;
         for (uint32_t w0 = 0; w0 < E; w0 += THREADS * EPT) {
-            uint32_t xk[EPT], kq[EPT];
-            float qv[EPT];
+            uint64_t ad[EPT];
+            uint32_t kq[EPT], xb[EPT];
+            // (a) addresses: message and bin of each flat entry
 #pragma unroll
             for (int j = 0; j < EPT; ++j) {
                 const uint32_t i = w0 + j * THREADS + tid;
                 kq[j] = kSentinel;
+                xb[j] = 0;
+                ad[j] = mbase[k0];   // any readable address for idle slots
                 if (i < E) {
-                    // message of flat entry i
                     uint32_t lo = 0, hi = kn;   // fk[lo] <= i < fk[hi]
                     while (hi - lo > 1) {
                         const uint32_t mid = (lo + hi) >> 1;
@@ -774,28 +816,34 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__
                         const uint32_t mid = (bl + bh) >> 1;
                         if (pr[mid] <= e) bl = mid; else bh = mid;
                     }
-                    const uint32_t word = get_word(msgs.p[k0 + lo] + ebase[lo] + uint64_t(e) * sg.wb, sg.wb);
-                    const uint32_t idx = word & ((1u << topbit) - 1u);
-                    const uint32_t x = bl * sg.lt + idx;
-                    if (idx < sg.lt && x < tg.tlen) {
-                        kq[j] = lo;
-                        xk[j] = x + tg.lead;
-                        qv[j] = (word >> topbit) ? -ks[lo] : ks[lo];
-                    }
+                    kq[j] = lo;
+                    xb[j] = bl * lt;
+                    ad[j] = eaddr[lo] + uint64_t(e) * wb;
                 }
             }
+            // (b) all loads, then (c) positions and values
+            uint32_t wd[EPT];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) wd[j] = word_at(ad[j], wb);
+            uint32_t xk[EPT];
+            float qv[EPT];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                const uint32_t idx = wd[j] & ((1u << topbit) - 1u);
+                const uint32_t x = xb[j] + idx;
+                xk[j] = x + tg.lead;
+                const float s = kq[j] != kSentinel ? ks[kq[j]] : 0.0f;
+                qv[j] = (wd[j] >> topbit) ? -s : s;
+                if (kq[j] != kSentinel && !(idx < lt && x < tg.tlen)) kq[j] = kSentinel;
+            }
             // Apply in message order; within one message every index is distinct.
-            const uint32_t klo = [&] {
+            auto msg_of = [&](uint32_t i) {
                 uint32_t lo = 0, hi = kn;
-                while (hi - lo > 1) { const uint32_t mid = (lo + hi) >> 1; if (fk[mid] <= w0) lo = mid; else hi = mid; }
+                while (hi - lo > 1) { const uint32_t mid = (lo + hi) >> 1; if (fk[mid] <= i) lo = mid; else hi = mid; }
                 return lo;
-            }();
-            const uint32_t last = min(E, w0 + THREADS * EPT) - 1;
-            const uint32_t khi = [&] {
-                uint32_t lo = 0, hi = kn;
-                while (hi - lo > 1) { const uint32_t mid = (lo + hi) >> 1; if (fk[mid] <= last) lo = mid; else hi = mid; }
-                return lo;
-            }();
+            };
+            const uint32_t klo = msg_of(w0);
+            const uint32_t khi = msg_of(min(E, w0 + THREADS * EPT) - 1);
             for (uint32_t kk = klo; kk <= khi; ++kk) {
 #pragma unroll
                 for (int j = 0; j < EPT; ++j)
@@ -810,7 +858,7 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__
             const int x0 = int(vi * 4) - int(tg.lead);
             const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
             if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
-                *reinterpret_cast<float4*>(out + e0) = *reinterpret_cast<const float4*>(acc + vi * 4);
+                store4<true>(out + e0, *reinterpret_cast<const f32x4*>(acc + vi * 4));
             } else {
                 for (int c = 0; c < 4; ++c) {
                     const int x = x0 + c;

@@ -49,7 +49,17 @@ constexpr uint32_t kChunkTiles = 1024;  // tiles per scan chunk (4 per thread of
 constexpr uint32_t kPrefWords = 8192;   // LDS words for per-message bin prefixes in decode
 constexpr uint64_t kAlign = 256;        // workspace sub-buffer alignment
 
-// Per-segment parameters read by every kernel (80 bytes).
+// How one layer is cut into tiles of whole bins.
+struct TileSpec {
+    uint32_t bpt;         // bins per tile
+    uint32_t tile_begin;  // first global tile of the layer
+    uint32_t ntiles;
+    uint32_t chunk_begin; // first scan chunk (kChunkTiles tiles each) of the layer
+    uint32_t nchunks;
+    uint32_t variant;     // tile shape index
+};
+
+// Per-segment parameters read by every kernel (96 bytes).
 struct SegDev {
     uint64_t off;        // element offset in the flat buffers
     uint64_t numel;
@@ -58,16 +68,11 @@ struct SegDev {
     uint32_t lt;         // bin length L_T
     uint32_t magic;      // floor(2^32 / lt) + 1: exact x / lt for x < 2^16 (lt >= 2)
     uint32_t nbins;
-    uint32_t bpt;        // bins per tile
-    uint32_t tile_begin; // first global tile of the segment
-    uint32_t ntiles;
-    uint32_t chunk_begin;
-    uint32_t nchunks;
     uint32_t wb;         // index word bytes: 1 if lt < 64 else 2
-    uint32_t variant;    // tile shape index
-    uint32_t pad[2];
+    TileSpec ct;         // compress tiles
+    TileSpec dt;         // decode tiles
 };
-static_assert(sizeof(SegDev) == 80, "SegDev layout");
+static_assert(sizeof(SegDev) == 96, "SegDev layout");
 
 // Exact x / lt for 0 <= x < 2^16 and 2 <= lt <= 2^16 with magic =
 // floor(2^32 / lt) + 1: the product overshoots x / lt by x * e / 2^32 with
@@ -87,12 +92,12 @@ struct TileGeom {
     uint64_t v0;         // t0 rounded down to a multiple of 4
 };
 
-ADACOMP_HD inline TileGeom tile_geom(const SegDev& sg, uint32_t tile) {
+ADACOMP_HD inline TileGeom tile_geom(const SegDev& sg, const TileSpec& ts, uint32_t tile) {
     TileGeom g;
-    const uint32_t local = tile - sg.tile_begin;
-    g.first_bin = local * sg.bpt;
+    const uint32_t local = tile - ts.tile_begin;
+    g.first_bin = local * ts.bpt;
     const uint32_t left = sg.nbins - g.first_bin;
-    g.nb = sg.bpt < left ? sg.bpt : left;
+    g.nb = ts.bpt < left ? ts.bpt : left;
     const uint64_t e0 = uint64_t(g.first_bin) * sg.lt;
     const uint64_t rest = sg.numel - e0;
     const uint64_t want = uint64_t(g.nb) * sg.lt;
@@ -104,19 +109,31 @@ ADACOMP_HD inline TileGeom tile_geom(const SegDev& sg, uint32_t tile) {
     return g;
 }
 
+// The tiles of one kind over the whole table.
+struct Tiling {
+    std::vector<uint32_t> tile_seg;          // [T] segment of each tile
+    std::vector<uint32_t> by_variant[3];     // tile ids of each shape, in order
+    std::vector<uint32_t> chunk_tile_begin;  // [C + 1]
+    std::vector<uint32_t> chunk_seg;         // [C]
+    uint32_t max_bpt[3] = {0, 0, 0};
+    uint32_t max_span_vecs[3] = {0, 0, 0};   // most float4 one tile touches
+    uint64_t ntiles = 0, nchunks = 0;
+};
+
+// Decode tiles: accumulated in LDS up to kDecCap elements (L_T <= 4093),
+// otherwise one bin per tile accumulated in place in out.
+constexpr uint32_t kDecCap = 4096;
+constexpr int kDecVariants = 2;
+constexpr uint32_t kDecThreads[kDecVariants] = {256, 1024};
+
 struct Layout {
     uint32_t nseg = 0;
     uint32_t plan_hash = 0;
     std::vector<SegDev> segs;
-    std::vector<uint32_t> tile_seg;          // [T] segment of each tile
-    std::vector<uint32_t> tiles_by_variant[kVariants];
-    std::vector<uint32_t> chunk_tile_begin;  // [C + 1]
-    std::vector<uint32_t> chunk_seg;         // [C]
-    uint32_t max_bpt[kVariants] = {0, 0, 0};
-    uint32_t max_span_vecs[kVariants] = {0, 0, 0};   // most float4 one tile touches
+    Tiling ct;                               // compress tiles
+    Tiling dt;                               // decode tiles
     uint64_t total_numel = 0, total_bins = 0;
     uint64_t span = 0;   // max(offset + numel) rounded up to 4: the flat buffers' minimum length
-    uint64_t ntiles = 0, nchunks = 0;
     uint64_t counts_begin = 0, entries_begin = 0, capacity = 0;
 
     // Compress workspace (byte offsets).
@@ -190,7 +207,37 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
     L.segs.resize(nseg);
     L.counts_begin = round_up(32 + 16 * uint64_t(nseg), 16);
     uint64_t count_at = L.counts_begin;
-    uint64_t tiles = 0, chunks = 0, bins = 0;
+    uint64_t bins = 0;
+    // Cut layer i into tiles of spec ts (shape v, capacity cap elements).
+    auto cut = [&](Tiling& T, TileSpec& ts, uint32_t i, uint32_t v, uint32_t cap) -> int {
+        const SegDev& d = L.segs[i];
+        ts.variant = v;
+        ts.bpt = bins_per_tile(d.lt, cap, d.nbins);
+        ts.ntiles = (d.nbins + ts.bpt - 1) / ts.bpt;
+        if (T.ntiles + ts.ntiles >= (uint64_t(1) << 31)) return ADACOMP_ERR_TOO_LARGE;
+        ts.tile_begin = static_cast<uint32_t>(T.ntiles);
+        ts.nchunks = (ts.ntiles + kChunkTiles - 1) / kChunkTiles;
+        ts.chunk_begin = static_cast<uint32_t>(T.nchunks);
+        // Most float4 any tile touches: an unaligned start adds up to 3
+        // leading elements.
+        const uint64_t tile_elems = std::min<uint64_t>(uint64_t(ts.bpt) * d.lt, d.numel);
+        const bool aligned = (uint64_t(ts.bpt) * d.lt) % 4 == 0 || ts.ntiles == 1;
+        const uint64_t vecs = (tile_elems + (aligned ? 0 : 3) + 3) / 4;
+        if (vecs * 4 > cap) return ADACOMP_ERR_UNSUPPORTED_BIN;
+        T.max_span_vecs[v] = std::max<uint32_t>(T.max_span_vecs[v], uint32_t(vecs));
+        T.max_bpt[v] = std::max(T.max_bpt[v], ts.bpt);
+        for (uint32_t t = 0; t < ts.ntiles; ++t) {
+            T.tile_seg.push_back(i);
+            T.by_variant[v].push_back(static_cast<uint32_t>(T.ntiles + t));
+        }
+        for (uint32_t c = 0; c < ts.nchunks; ++c) {
+            T.chunk_tile_begin.push_back(static_cast<uint32_t>(T.ntiles + uint64_t(c) * kChunkTiles));
+            T.chunk_seg.push_back(i);
+        }
+        T.ntiles += ts.ntiles;
+        T.nchunks += ts.nchunks;
+        return ADACOMP_OK;
+    };
     for (uint32_t i = 0; i < nseg; ++i) {
         const adacomp_segment& s = segs[i];
         SegDev& d = L.segs[i];
@@ -201,51 +248,30 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
         d.magic = s.bin_len >= 2 ? static_cast<uint32_t>((uint64_t(1) << 32) / s.bin_len + 1) : 0u;
         const uint64_t nb = (s.numel + s.bin_len - 1) / s.bin_len;
         d.nbins = static_cast<uint32_t>(nb);
-        d.variant = kVariants - 1;
-        for (int v = kVariants - 1; v >= 0; --v)
-            if (s.bin_len + 3 <= var_cap(v)) d.variant = uint32_t(v);
-        const uint32_t cap = var_cap(int(d.variant));
-        d.bpt = bins_per_tile(s.bin_len, cap, d.nbins);
-        d.ntiles = static_cast<uint32_t>((nb + d.bpt - 1) / d.bpt);
         d.wb = s.bin_len < 64 ? 1u : 2u;
         d.bin_base = bins;
         d.count_off = count_at;
-        if (tiles + d.ntiles >= (uint64_t(1) << 31)) return ADACOMP_ERR_TOO_LARGE;
-        d.tile_begin = static_cast<uint32_t>(tiles);
-        d.nchunks = (d.ntiles + kChunkTiles - 1) / kChunkTiles;
-        d.chunk_begin = static_cast<uint32_t>(chunks);
-        // Most float4 any tile of this segment touches: an unaligned start
-        // adds up to 3 leading elements.
-        const uint64_t tile_elems = std::min<uint64_t>(uint64_t(d.bpt) * s.bin_len, s.numel);
-        const bool aligned = (uint64_t(d.bpt) * s.bin_len) % 4 == 0 || d.ntiles == 1;
-        const uint64_t vecs = (tile_elems + (aligned ? 0 : 3) + 3) / 4;
-        if (vecs * 4 > cap) return ADACOMP_ERR_UNSUPPORTED_BIN;
-        L.max_span_vecs[d.variant] = std::max<uint32_t>(L.max_span_vecs[d.variant], uint32_t(vecs));
-        L.max_bpt[d.variant] = std::max(L.max_bpt[d.variant], d.bpt);
-
-        for (uint32_t t = 0; t < d.ntiles; ++t) {
-            L.tile_seg.push_back(i);
-            L.tiles_by_variant[d.variant].push_back(static_cast<uint32_t>(tiles + t));
-        }
-        for (uint32_t c = 0; c < d.nchunks; ++c) {
-            L.chunk_tile_begin.push_back(static_cast<uint32_t>(tiles + uint64_t(c) * kChunkTiles));
-            L.chunk_seg.push_back(i);
-        }
-        tiles += d.ntiles;
-        chunks += d.nchunks;
+        uint32_t cv = kVariants - 1;
+        for (int v = kVariants - 1; v >= 0; --v)
+            if (s.bin_len + 3 <= var_cap(v)) cv = uint32_t(v);
+        int st = cut(L.ct, d.ct, i, cv, var_cap(int(cv)));
+        if (st != ADACOMP_OK) return st;
+        const uint32_t dv = s.bin_len + 3 <= kDecCap ? 0u : 1u;
+        st = cut(L.dt, d.dt, i, dv, dv == 0 ? kDecCap : kMaxCap);
+        if (st != ADACOMP_OK) return st;
         bins += nb;
         count_at = round_up(count_at + nb * d.wb, 16);
         L.total_numel += s.numel;
         L.span = std::max<uint64_t>(L.span, round_up(s.offset + s.numel, 4));
     }
-    L.chunk_tile_begin.push_back(static_cast<uint32_t>(tiles));
-    L.ntiles = tiles;
-    L.nchunks = chunks;
+    L.ct.chunk_tile_begin.push_back(static_cast<uint32_t>(L.ct.ntiles));
+    L.dt.chunk_tile_begin.push_back(static_cast<uint32_t>(L.dt.ntiles));
     L.total_bins = bins;
     L.entries_begin = count_at;
     uint64_t cap = count_at;
     for (uint32_t i = 0; i < nseg; ++i) cap = round_up(cap + L.segs[i].numel * L.segs[i].wb, 16);
     L.capacity = cap;
+    const uint64_t tiles = L.ct.ntiles, chunks = L.ct.nchunks;
 
     // Compress workspace.
     uint64_t w = 0;
@@ -267,11 +293,11 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
     L.ws_compress = w;
 
     // Decode workspace for K messages: a status block, then arrays indexed by
-    // message: tile counts and offsets [K*T], chunk counts and bases [K*C],
-    // per-segment s and entry offsets [K*nseg], per-message validity [K].
-    // Each array is kAlign-aligned, so fixed covers the padding of all nine.
+    // message: decode-tile counts and offsets [K*DT], chunk counts and bases
+    // [K*DC], per-segment s and entry offsets [K*nseg], per-message validity
+    // [K].  Each array is kAlign-aligned, so fixed covers the padding of all.
     L.dws_fixed = 9 * kAlign;
-    L.dws_per_msg = round_up(8 * tiles + 8 * chunks + 12 * uint64_t(nseg) + 4, 16);
+    L.dws_per_msg = round_up(8 * L.dt.ntiles + 8 * L.dt.nchunks + 12 * uint64_t(nseg) + 4, 16);
     return ADACOMP_OK;
 }
 
@@ -281,7 +307,7 @@ inline void fill_info(const Layout& L, adacomp_plan_info* info) {
     info->total_numel = L.total_numel;
     info->span = L.span;
     info->total_bins = L.total_bins;
-    info->ntiles = L.ntiles;
+    info->ntiles = L.ct.ntiles;
     info->header_bytes = 32 + 16 * uint64_t(L.nseg);
     info->message_capacity = L.capacity;
     info->compress_workspace_bytes = L.ws_compress;

@@ -1,13 +1,14 @@
 // Host-side check of the work decomposition the HIP kernels rely on, using
 // the library's own layout code (layout.hpp is plain C++).  For every segment
-// table read from the input file it verifies, tile by tile, that every access
-// the kernels derive from the tile geometry stays inside its buffer and its
-// LDS allocation, that the tiles partition each segment exactly, and that the
-// multiply-high bin division is exact for every in-tile offset.
+// table read from the input file it verifies, tile by tile and for both the
+// compress tiles and the decode tiles, that every access the kernels derive
+// from the tile geometry stays inside its buffer and its LDS allocation, that
+// the tiles partition each segment exactly, and that the multiply-high bin
+// division is exact for every in-tile offset.
 //
-// Input: blocks of "nseg" followed by nseg lines "offset numel bin_len".
-// Output: one line per table, "OK ..." or "FAIL <reason>"; exit status 1 if
-// any table fails.
+// Input: blocks of "nseg expected_status" followed by nseg lines
+// "offset numel bin_len".  Output: one line per table, "OK ..." or
+// "FAIL <reason>"; exit status 1 if any table fails.
 #include <cstdio>
 #include <cstdint>
 #include <string>
@@ -17,79 +18,99 @@
 
 using namespace adacomp;
 
+// capacity and threads x float4-per-thread of shape v of a tiling
+struct Shapes {
+    uint32_t cap[3];
+    uint32_t lanes_vecs[3];
+    int n;
+};
+
+static std::string check_tiling(const Layout& L, const Tiling& T, bool decode, const Shapes& sh) {
+    uint64_t seen = 0;
+    for (uint32_t s = 0; s < L.nseg; ++s) {
+        const SegDev& d = L.segs[s];
+        const TileSpec& ts = decode ? d.dt : d.ct;
+        if (int(ts.variant) >= sh.n) return "FAIL variant";
+        if (ts.bpt == 0 || ts.bpt > T.max_bpt[ts.variant]) return "FAIL bpt";
+        for (uint32_t v = 0; v < ts.variant; ++v)
+            if (d.lt + 3 <= sh.cap[v]) return "FAIL shape not the smallest";
+        uint64_t next = d.off;
+        uint32_t next_bin = 0;
+        for (uint32_t t = ts.tile_begin; t < ts.tile_begin + ts.ntiles; ++t) {
+            if (T.tile_seg[t] != s) return "FAIL tile_seg";
+            const TileGeom g = tile_geom(d, ts, t);
+            if (g.t0 != next || g.first_bin != next_bin) return "FAIL partition";
+            if (g.nb == 0 || g.nb > ts.bpt || g.tlen == 0) return "FAIL empty tile";
+            if (g.t0 + g.tlen > d.off + d.numel) return "FAIL tile past segment end";
+            if (g.v0 + 4 * uint64_t(g.nvec) > L.span) return "FAIL float4 past padded span";
+            if (g.nvec > sh.lanes_vecs[ts.variant]) return "FAIL vectors exceed threads";
+            if (uint64_t(g.nvec) * 4 > sh.cap[ts.variant]) return "FAIL vectors exceed cap";
+            if (g.nvec > T.max_span_vecs[ts.variant]) return "FAIL LDS tile too small";
+            if (g.lead + g.tlen >= 65536u) return "FAIL offsets exceed 16 bits";
+            if ((g.t0 & 3) != g.lead || g.v0 % 4 != 0) return "FAIL lead";
+            if (g.first_bin + g.nb < d.nbins && g.tlen != uint64_t(g.nb) * d.lt) return "FAIL partial bin";
+            for (uint32_t x = 0; x < g.tlen + g.lead; ++x)
+                if (div_bin(x, d.lt, d.magic) != x / d.lt) return "FAIL div_bin";
+            const uint64_t cw_end = d.count_off + uint64_t(g.first_bin + g.nb) * d.wb;
+            if (cw_end > d.count_off + uint64_t(d.nbins) * d.wb) return "FAIL count words";
+            next = g.t0 + g.tlen;
+            next_bin = g.first_bin + g.nb;
+            ++seen;
+        }
+        if (next != d.off + d.numel || next_bin != d.nbins) return "FAIL coverage";
+        for (uint32_t c = ts.chunk_begin; c < ts.chunk_begin + ts.nchunks; ++c) {
+            if (T.chunk_seg[c] != s) return "FAIL chunk_seg";
+            const uint32_t a = T.chunk_tile_begin[c], b = T.chunk_tile_begin[c + 1];
+            if (b <= a || b - a > kChunkTiles) return "FAIL chunk size";
+            if (a < ts.tile_begin || b > ts.tile_begin + ts.ntiles) return "FAIL chunk crosses segment";
+            if ((a - ts.tile_begin) / kChunkTiles != c - ts.chunk_begin) return "FAIL chunk index";
+        }
+    }
+    if (seen != T.ntiles || T.chunk_tile_begin.back() != T.ntiles) return "FAIL tile count";
+    uint64_t in_variants = 0;
+    for (int v = 0; v < 3; ++v) in_variants += T.by_variant[v].size();
+    if (in_variants != T.ntiles) return "FAIL variants";
+    return "";
+}
+
 static std::string check(const std::vector<adacomp_segment>& segs, int expect_status) {
     Layout L;
     const int st = build_layout(segs.data(), static_cast<uint32_t>(segs.size()), L);
     if (st != expect_status) return "FAIL status " + std::to_string(st);
     if (st != ADACOMP_OK) return "OK rejected";
-    uint64_t tiles_seen = 0;
-    for (uint32_t s = 0; s < L.nseg; ++s) {
-        const SegDev& d = L.segs[s];
-        if (d.bpt == 0 || d.bpt > L.max_bpt[d.variant]) return "FAIL bpt";
-        uint64_t next = d.off;       // tiles must cover the segment in order
-        uint32_t next_bin = 0;
-        for (uint32_t t = d.tile_begin; t < d.tile_begin + d.ntiles; ++t) {
-            if (L.tile_seg[t] != s) return "FAIL tile_seg";
-            const TileGeom g = tile_geom(d, t);
-            if (g.t0 != next || g.first_bin != next_bin) return "FAIL partition";
-            if (g.nb == 0 || g.nb > d.bpt || g.tlen == 0) return "FAIL empty tile";
-            if (g.t0 + g.tlen > d.off + d.numel) return "FAIL tile past segment end";
-            if (g.t0 + g.tlen > L.span) return "FAIL tile past span";
-            // whole-float4 loads (lanes past the tile reload its last float4)
-            if (g.v0 + 4 * uint64_t(g.nvec) > L.span) return "FAIL float4 past padded span";
-            if (L.span % 4 != 0) return "FAIL span not padded";
-            if (g.nvec > kVarThreads[d.variant] * kVarVecs[d.variant]) return "FAIL vectors exceed threads";
-            if (uint64_t(g.nvec) * 4 > var_cap(int(d.variant))) return "FAIL vectors exceed cap";
-            // the first shape that holds the bin is used
-            for (uint32_t v = 0; v < d.variant; ++v)
-                if (d.lt + 3 <= var_cap(int(v))) return "FAIL shape not the smallest";
-            if (g.nvec > L.max_span_vecs[d.variant]) return "FAIL decode LDS too small";
-            if (g.lead + g.tlen >= 65536u) return "FAIL offsets exceed 16 bits";
-            if ((g.t0 & 3) != g.lead || g.v0 % 4 != 0) return "FAIL lead";
-            // every bin except the last of the segment is whole
-            if (g.first_bin + g.nb < d.nbins && g.tlen != uint64_t(g.nb) * d.lt) return "FAIL partial bin";
-            // exact division for every in-tile offset
-            for (uint32_t x = 0; x < g.tlen; ++x)
-                if (div_bin(x, d.lt, d.magic) != x / d.lt) return "FAIL div_bin";
-            // count words of the tile stay in the segment's count region
-            const uint64_t cw_end = d.count_off + uint64_t(g.first_bin + g.nb) * d.wb;
-            if (cw_end > d.count_off + uint64_t(d.nbins) * d.wb) return "FAIL count words";
-            next = g.t0 + g.tlen;
-            next_bin = g.first_bin + g.nb;
-            ++tiles_seen;
-        }
-        if (next != d.off + d.numel || next_bin != d.nbins) return "FAIL coverage";
-        if (round_up(d.count_off + uint64_t(d.nbins) * d.wb, 16) > L.entries_begin) return "FAIL count region";
-        // chunks of this segment
-        for (uint32_t c = d.chunk_begin; c < d.chunk_begin + d.nchunks; ++c) {
-            if (L.chunk_seg[c] != s) return "FAIL chunk_seg";
-            const uint32_t a = L.chunk_tile_begin[c], b = L.chunk_tile_begin[c + 1];
-            if (b <= a || b - a > kChunkTiles) return "FAIL chunk size";
-            if (a < d.tile_begin || b > d.tile_begin + d.ntiles) return "FAIL chunk crosses segment";
-            if ((a - d.tile_begin) / kChunkTiles != c - d.chunk_begin) return "FAIL chunk index";
-        }
+    if (L.span % 4 != 0) return "FAIL span not padded";
+    Shapes cs{}, ds{};
+    cs.n = kVariants;
+    for (int v = 0; v < kVariants; ++v) {
+        cs.cap[v] = var_cap(v);
+        cs.lanes_vecs[v] = kVarThreads[v] * kVarVecs[v];
     }
-    if (tiles_seen != L.ntiles || L.chunk_tile_begin.back() != L.ntiles) return "FAIL tile count";
-    // worst-case message fits its capacity
+    ds.n = kDecVariants;
+    ds.cap[0] = kDecCap;
+    ds.lanes_vecs[0] = kDecCap / 4;   // decode walks float4 with a strided loop
+    ds.cap[1] = kMaxCap;
+    ds.lanes_vecs[1] = kMaxCap / 4;
+    std::string r = check_tiling(L, L.ct, false, cs);
+    if (!r.empty()) return r + " (compress tiles)";
+    r = check_tiling(L, L.dt, true, ds);
+    if (!r.empty()) return r + " (decode tiles)";
+    for (const SegDev& d : L.segs)
+        if (round_up(d.count_off + uint64_t(d.nbins) * d.wb, 16) > L.entries_begin) return "FAIL count region";
     uint64_t at = L.entries_begin;
     for (const SegDev& d : L.segs) at = round_up(at + d.numel * d.wb, 16);
     if (at != L.capacity) return "FAIL capacity";
-    // staging: survivor slots t0 + rank < t0 + tlen <= span, inside the stage buffer
     if (L.ws_tile_cnt - L.ws_stage < 8 * L.span) return "FAIL stage size";
-    // LDS per workgroup (bytes) stays within 64 KiB: decode keeps narrow and
-    // medium tiles in LDS; the tile pass holds 2*bpt+1 words.
-    uint64_t tiles_in_variants = 0;
-    for (int v = 0; v < kVariants; ++v) {
-        tiles_in_variants += L.tiles_by_variant[v].size();
-        if (L.tiles_by_variant[v].empty()) continue;
-        const uint32_t ps = L.max_bpt[v] + 1;
+    // LDS per workgroup stays within 64 KiB.
+    for (int v = 0; v < kVariants; ++v)
+        if (!L.ct.by_variant[v].empty() && (2 * L.ct.max_bpt[v] + 1) * 4 > 65536) return "FAIL tile LDS";
+    for (int v = 0; v < kDecVariants; ++v) {
+        if (L.dt.by_variant[v].empty()) continue;
+        const uint32_t ps = L.dt.max_bpt[v] + 1;
         const uint32_t kg = std::max<uint32_t>(1, std::min<uint32_t>(ADACOMP_MAX_MESSAGES, kPrefWords / ps));
-        if (v < 2 && (L.max_span_vecs[v] * 4 + kg * ps) * 4 > 65536) return "FAIL decode LDS";
-        if (v == 2 && kg * ps * 4 > 65536) return "FAIL decode LDS";
-        if ((2 * L.max_bpt[v] + 1) * 4 > 65536) return "FAIL tile LDS";
+        const uint32_t acc = v == 0 ? L.dt.max_span_vecs[0] * 4 : 0;
+        if ((acc + kg * ps) * 4 > 65536) return "FAIL decode LDS";
     }
-    if (tiles_in_variants != L.ntiles) return "FAIL variants";
-    return "OK tiles=" + std::to_string(L.ntiles) + " chunks=" + std::to_string(L.nchunks);
+    return "OK tiles=" + std::to_string(L.ct.ntiles) + " dtiles=" + std::to_string(L.dt.ntiles);
 }
 
 int main(int argc, char** argv) {

@@ -70,7 +70,7 @@ def test_decode_parity(name, K):
     plan.close()
 
 
-@pytest.mark.parametrize("lt", [1, 3, 7, 50, 64, 500, 4094, 32768])
+@pytest.mark.parametrize("lt", [1, 3, 7, 50, 64, 500, 1021, 4093, 4094, 32768])
 def test_decode_edge_tables(lt):
     segs, off = [], 0
     for n in (1, 5, 63, 4097, 40003):
