@@ -418,17 +418,17 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
             const uint32_t n = static_cast<uint32_t>(L.dt.by_variant[v].size());
             if (n == 0) continue;
             const uint32_t ps = L.dt.max_bpt[v] + 1;
-            const uint32_t KG = std::max<uint32_t>(1, std::min<uint32_t>(K, adacomp::kPrefWords / ps));
+            const uint32_t KG = adacomp::decode_group(K, ps);
             if (v == 0) {   // the tile fits in LDS
                 const uint32_t acc_words = L.dt.max_span_vecs[0] * 4;
-                const uint32_t lds = (acc_words + KG * ps) * 4;
-                hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, 4>), dim3(n), dim3(256), lds,
+                const uint32_t lds = adacomp::decode_lds_bytes(acc_words, K, KG, ps, 4);
+                hipLaunchKernelGGL((adacomp::k_decode_apply<256, true>), dim3(n), dim3(256), lds,
                                    stream, mp, K, KG, plan->d_segs, plan->ddt.tile_seg,
                                    plan->ddt.vtiles[0], DT, DC, L.nseg, dw, out, accumulate,
                                    acc_words);
-            } else {        // one long bin per tile, accumulated in place in out
-                const uint32_t lds = KG * ps * 4;
-                hipLaunchKernelGGL((adacomp::k_decode_apply<1024, false, 2>), dim3(n), dim3(1024), lds,
+            } else {        // long bins, accumulated in place in out
+                const uint32_t lds = adacomp::decode_lds_bytes(0, K, KG, ps, 16);
+                hipLaunchKernelGGL((adacomp::k_decode_apply<1024, false>), dim3(n), dim3(1024), lds,
                                    stream, mp, K, KG, plan->d_segs, plan->ddt.tile_seg,
                                    plan->ddt.vtiles[1], DT, DC, L.nseg, dw, out, accumulate, 0u);
             }

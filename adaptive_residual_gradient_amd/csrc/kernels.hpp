@@ -668,31 +668,44 @@ k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, uint32_
 // Index word at byte address a (w = 8 or 16 bits), read as the aligned
 // 16-bit word that contains it; messages are 16-byte aligned and padded to a
 // multiple of 16 bytes, so the read stays inside the message.
+// The address is formed from integers kept in LDS, so it is cast to a
+// global-address-space pointer (a global load, not a flat one).
+typedef const __attribute__((address_space(1))) uint16_t* global_u16_ptr;
+
 __device__ __forceinline__ uint32_t word_at(uint64_t a, uint32_t wb) {
-    const uint32_t w16 = *reinterpret_cast<const uint16_t*>(a & ~uint64_t(1));
+    const uint32_t w16 = *(global_u16_ptr)(a & ~uint64_t(1));
     return wb == 1u ? (w16 >> (8u * uint32_t(a & 1u))) & 0xFFu : w16;
 }
 
 // Per decode tile: out[j] = (accumulate ? out[j] : +0) + q_0[j] + q_1[j] + ...
 // in message order, only at transmitted j.  LDS_ACC keeps the tile in LDS;
 // otherwise (bins longer than 4093) the tile is accumulated in place in out.
-// Messages are taken in groups of KG (their bin prefixes fill the LDS words
-// given at launch); each group's entries are gathered in windows of
-// THREADS*EPT: addresses first, then all loads, then the additions, message
-// by message, with a barrier between messages.
-template <int THREADS, bool LDS_ACC, int EPT>
+// Messages are taken in groups of KG (KG <= 64; their bin prefixes fill the
+// LDS words given at launch).  The tile's bins are split between the
+// wavefronts; each wavefront gathers the entries of its bins for the whole
+// group (message-major) 64 at a time and adds them message by message.  One
+// wavefront's LDS operations execute in program order, so the additions to
+// an element happen in message order without block barriers.
+// Dynamic LDS: [acc_words floats if LDS_ACC][K u64 message bases][KG u64
+// entry addresses][K floats s][K u32 validity][NW*(KG+1) u32 per-wavefront
+// flat prefixes][KG*(bpt+1) u32 bin prefixes].
+
+template <int THREADS, bool LDS_ACC>
 __global__ void __launch_bounds__(THREADS)
 k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__ segs,
                const uint32_t* __restrict__ tile_seg, const uint32_t* __restrict__ vtiles,
                uint32_t DT, uint32_t DC, uint32_t nseg, DecodeWs ws, float* __restrict__ out,
                int accumulate, uint32_t acc_words) {
     constexpr int NW = THREADS / 64;
-    extern __shared__ uint32_t dyn[];
-    __shared__ uint64_t mbase[ADACOMP_MAX_MESSAGES];      // message base addresses
-    __shared__ uint64_t eaddr[ADACOMP_MAX_MESSAGES];      // address of the tile's first entry
-    __shared__ uint32_t fk[ADACOMP_MAX_MESSAGES + 1];     // flat entry prefix over messages
-    __shared__ float ks[ADACOMP_MAX_MESSAGES];
-    __shared__ uint32_t kvalid[ADACOMP_MAX_MESSAGES];
+    extern __shared__ uint64_t dyn64[];
+    uint32_t* dyn = reinterpret_cast<uint32_t*>(dyn64);
+    const uint32_t accw = LDS_ACC ? (acc_words + 1u) & ~1u : 0u;   // keep 8-byte alignment
+    uint64_t* mbase = reinterpret_cast<uint64_t*>(dyn + accw);
+    uint64_t* eaddr = mbase + K;
+    float* ks = reinterpret_cast<float*>(eaddr + KG);
+    uint32_t* kvalid = reinterpret_cast<uint32_t*>(ks + K);
+    uint32_t* wfk_all = kvalid + K;                       // [NW][KG + 1]
+    uint32_t* pref = wfk_all + NW * (KG + 1);             // [KG][bpt + 1]
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint32_t tile = vtiles[blockIdx.x];
@@ -701,14 +714,16 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__
     const TileGeom tg = tile_geom(sg, sg.dt, tile);
     const uint32_t chunk = sg.dt.chunk_begin + (tile - sg.dt.tile_begin) / kChunkTiles;
     float* acc = LDS_ACC ? reinterpret_cast<float*>(dyn) : out + tg.v0;
-    uint32_t* pref = dyn + (LDS_ACC ? acc_words : 0u);    // [KG][bpt + 1]
     const uint32_t pstride = sg.dt.bpt + 1;
     const uint32_t wb = sg.wb, lt = sg.lt;
     const uint32_t topbit = wb == 1u ? 7u : 15u;
+    const uint32_t wb0 = tg.nb * uint32_t(wv) / NW, wb1 = tg.nb * uint32_t(wv + 1) / NW;
+    uint32_t* wfk = wfk_all + wv * (KG + 1);
 
     for (uint32_t k = tid; k < K; k += THREADS) {
         mbase[k] = reinterpret_cast<uint64_t>(msgs.p[k]);
         kvalid[k] = ws.dvalid[k];
+        ks[k] = ws.dseg_s[uint64_t(k) * nseg + si];
     }
     // Initial values: +0, or out.
     for (uint32_t vi = tid; vi < tg.nvec; vi += THREADS) {
@@ -735,120 +750,99 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__
 
     for (uint32_t k0 = 0; k0 < K; k0 += KG) {
         const uint32_t kn = min(KG, K - k0);
-        __syncthreads();
+        __syncthreads();   // bases staged; the previous group is done with pref
         // Count words of the tile's bins for this group of messages.
         for (uint32_t i = tid; i < kn * tg.nb; i += THREADS) {
             const uint32_t kk = i / tg.nb, b = i - kk * tg.nb;
             const uint32_t k = k0 + kk;
             uint32_t cw = 0;
-            if (kvalid[k]) {
-                const uint64_t a = mbase[k] + sg.count_off + uint64_t(tg.first_bin + b) * wb;
-                cw = word_at(a, wb);
-            }
+            if (kvalid[k])
+                cw = word_at(mbase[k] + sg.count_off + uint64_t(tg.first_bin + b) * wb, wb);
             pref[kk * pstride + b + 1] = cw;
         }
         if (tid < int(kn)) {
             const uint32_t k = k0 + tid;
-            const uint64_t kt = uint64_t(k) * DT + tile;
-            const uint64_t base = uint64_t(ws.dchunk_base[uint64_t(k) * DC + chunk]) + ws.doff[kt];
+            const uint64_t base = uint64_t(ws.dchunk_base[uint64_t(k) * DC + chunk]) +
+                                  ws.doff[uint64_t(k) * DT + tile];
             eaddr[tid] = mbase[k] + ws.dseg_eoff[uint64_t(k) * nseg + si] + base * wb;
-            ks[tid] = ws.dseg_s[uint64_t(k) * nseg + si];
         }
         __syncthreads();
-        // Per-message exclusive prefix over the tile's bins: one wavefront
-        // per message, 64 bins at a time.
-        for (uint32_t kk = wv; kk < kn; kk += NW) {
-            uint32_t* pr = pref + kk * pstride;
-            uint32_t carry = 0;
-            for (uint32_t b0 = 0; b0 < tg.nb; b0 += 64) {
-                const uint32_t b = b0 + lane;
-                const uint32_t v = b < tg.nb ? pr[b + 1] : 0u;
-                uint32_t inc = v;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const uint32_t t = __shfl_up(inc, d);
-                    if (lane >= d) inc += t;
+        // Per-message exclusive prefix over the tile's bins.
+        if (tg.nb <= 32) {
+            if (tid < int(kn)) {   // one thread per message
+                uint32_t* pr = pref + tid * pstride;
+                uint32_t run = 0;
+                pr[0] = 0;
+                for (uint32_t b = 0; b < tg.nb; ++b) {
+                    run += pr[b + 1];
+                    pr[b + 1] = run;
                 }
-                if (b < tg.nb) pr[b + 1] = carry + inc;
-                carry += __shfl(inc, 63);
             }
-            if (lane == 0) pr[0] = 0;
-        }
-        __syncthreads();
-        if (wv == 0) {
-            uint32_t carry = 0;
-            for (uint32_t k1 = 0; k1 < kn; k1 += 64) {
-                const uint32_t kk = k1 + lane;
-                const uint32_t v = kk < kn ? pref[kk * pstride + tg.nb] : 0u;
-                uint32_t inc = v;
+        } else {
+            for (uint32_t kk = wv; kk < kn; kk += NW) {   // one wavefront per message
+                uint32_t* pr = pref + kk * pstride;
+                uint32_t carry = 0;
+                for (uint32_t b0 = 0; b0 < tg.nb; b0 += 64) {
+                    const uint32_t b = b0 + lane;
+                    const uint32_t v = b < tg.nb ? pr[b + 1] : 0u;
+                    uint32_t inc = v;
 #pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const uint32_t t = __shfl_up(inc, d);
-                    if (lane >= d) inc += t;
-                }
-                if (kk < kn) fk[kk] = carry + inc - v;
-                carry += __shfl(inc, 63);
-            }
-            if (lane == 0) fk[kn] = carry;
-        }
-        __syncthreads();
-        const uint32_t E = fk[kn];
-        for (uint32_t w0 = 0; w0 < E; w0 += THREADS * EPT) {
-            uint64_t ad[EPT];
-            uint32_t kq[EPT], xb[EPT];
-            // (a) addresses: message and bin of each flat entry
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) {
-                const uint32_t i = w0 + j * THREADS + tid;
-                kq[j] = kSentinel;
-                xb[j] = 0;
-                ad[j] = mbase[k0];   // any readable address for idle slots
-                if (i < E) {
-                    uint32_t lo = 0, hi = kn;   // fk[lo] <= i < fk[hi]
-                    while (hi - lo > 1) {
-                        const uint32_t mid = (lo + hi) >> 1;
-                        if (fk[mid] <= i) lo = mid; else hi = mid;
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const uint32_t t = __shfl_up(inc, d);
+                        if (lane >= d) inc += t;
                     }
-                    const uint32_t e = i - fk[lo];
-                    const uint32_t* pr = pref + lo * pstride;
-                    uint32_t bl = 0, bh = tg.nb;   // pr[bl] <= e < pr[bh]
-                    while (bh - bl > 1) {
-                        const uint32_t mid = (bl + bh) >> 1;
-                        if (pr[mid] <= e) bl = mid; else bh = mid;
-                    }
-                    kq[j] = lo;
-                    xb[j] = bl * lt;
-                    ad[j] = eaddr[lo] + uint64_t(e) * wb;
+                    if (b < tg.nb) pr[b + 1] = carry + inc;
+                    carry += __shfl(inc, 63);
                 }
+                if (lane == 0) pr[0] = 0;
             }
-            // (b) all loads, then (c) positions and values
-            uint32_t wd[EPT];
+        }
+        __syncthreads();
+        if (wb0 >= wb1) continue;   // no bins for this wavefront
+        // This wavefront's entries, message-major: lane kk holds message kk's
+        // count over the wavefront's bins; wfk is their exclusive prefix.
+        {
+            const uint32_t c = uint32_t(lane) < kn
+                                   ? pref[lane * pstride + wb1] - pref[lane * pstride + wb0]
+                                   : 0u;
+            uint32_t inc = c;
 #pragma unroll
-            for (int j = 0; j < EPT; ++j) wd[j] = word_at(ad[j], wb);
-            uint32_t xk[EPT];
-            float qv[EPT];
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) {
-                const uint32_t idx = wd[j] & ((1u << topbit) - 1u);
-                const uint32_t x = xb[j] + idx;
-                xk[j] = x + tg.lead;
-                const float s = kq[j] != kSentinel ? ks[kq[j]] : 0.0f;
-                qv[j] = (wd[j] >> topbit) ? -s : s;
-                if (kq[j] != kSentinel && !(idx < lt && x < tg.tlen)) kq[j] = kSentinel;
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t t = __shfl_up(inc, d);
+                if (lane >= d) inc += t;
             }
-            // Apply in message order; within one message every index is distinct.
-            auto msg_of = [&](uint32_t i) {
-                uint32_t lo = 0, hi = kn;
-                while (hi - lo > 1) { const uint32_t mid = (lo + hi) >> 1; if (fk[mid] <= i) lo = mid; else hi = mid; }
-                return lo;
-            };
-            const uint32_t klo = msg_of(w0);
-            const uint32_t khi = msg_of(min(E, w0 + THREADS * EPT) - 1);
+            if (uint32_t(lane) < kn) wfk[lane + 1] = inc;
+            if (lane == 0) wfk[0] = 0;
+        }
+        const uint32_t Ew = wfk[kn];
+        for (uint32_t i0 = 0; i0 < Ew; i0 += 64) {
+            const uint32_t i = i0 + lane;
+            const bool valid = i < Ew;
+            const uint32_t ii = valid ? i : Ew - 1u;
+            uint32_t lo = 0, hi = kn;   // wfk[lo] <= ii < wfk[hi]
+            while (hi - lo > 1) {
+                const uint32_t mid = (lo + hi) >> 1;
+                if (wfk[mid] <= ii) lo = mid; else hi = mid;
+            }
+            const uint32_t* pr = pref + lo * pstride;
+            const uint32_t e = ii - wfk[lo] + pr[wb0];
+            uint32_t bl = wb0, bh = wb1;   // pr[bl] <= e < pr[bh]
+            while (bh - bl > 1) {
+                const uint32_t mid = (bl + bh) >> 1;
+                if (pr[mid] <= e) bl = mid; else bh = mid;
+            }
+            const uint32_t word = word_at(eaddr[lo] + uint64_t(e) * wb, wb);
+            const uint32_t idx = word & ((1u << topbit) - 1u);
+            const uint32_t x = bl * lt + idx;
+            const float sk = ks[k0 + lo];
+            const float q = (word >> topbit) ? -sk : sk;
+            const bool apply = valid && idx < lt && x < tg.tlen;
+            // Messages present in this batch, applied in order.
+            const uint32_t klo = __builtin_amdgcn_readfirstlane(lo);
+            const uint32_t khi = __shfl(lo, int(min(Ew - i0, 64u) - 1u));
             for (uint32_t kk = klo; kk <= khi; ++kk) {
-#pragma unroll
-                for (int j = 0; j < EPT; ++j)
-                    if (kq[j] == kk) acc[xk[j]] = acc[xk[j]] + qv[j];
-                __syncthreads();
+                if (apply && lo == kk) acc[x + tg.lead] = acc[x + tg.lead] + q;
+                if (!LDS_ACC) __threadfence_block();
             }
         }
     }

@@ -106,9 +106,11 @@ static std::string check(const std::vector<adacomp_segment>& segs, int expect_st
     for (int v = 0; v < kDecVariants; ++v) {
         if (L.dt.by_variant[v].empty()) continue;
         const uint32_t ps = L.dt.max_bpt[v] + 1;
-        const uint32_t kg = std::max<uint32_t>(1, std::min<uint32_t>(ADACOMP_MAX_MESSAGES, kPrefWords / ps));
+        const uint32_t kg = decode_group(ADACOMP_MAX_MESSAGES, ps);
+        if (kg > 64 || kg * ps > kPrefWords) return "FAIL decode group";
         const uint32_t acc = v == 0 ? L.dt.max_span_vecs[0] * 4 : 0;
-        if ((acc + kg * ps) * 4 > 65536) return "FAIL decode LDS";
+        if (decode_lds_bytes(acc, ADACOMP_MAX_MESSAGES, kg, ps, kDecThreads[v] / 64) > 65536)
+            return "FAIL decode LDS";
     }
     return "OK tiles=" + std::to_string(L.ct.ntiles) + " dtiles=" + std::to_string(L.dt.ntiles);
 }
