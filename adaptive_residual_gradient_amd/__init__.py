@@ -20,9 +20,9 @@ _HERE = pathlib.Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libadacomp.so"
 
 OK = 0
-NUM_STAGES = 7
+NUM_STAGES = 9
 STAGES = ("tile_pass", "chunk_scan", "finalize", "encode",
-          "decode_count", "decode_base", "decode_apply")
+          "decode_count", "decode_base", "decode_apply", "compress_call", "decode_call")
 MAX_MESSAGES = 256
 MAX_BIN_LEN = 32768
 

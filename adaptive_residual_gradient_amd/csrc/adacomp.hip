@@ -303,6 +303,7 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     uint64_t* seg_eoff = reinterpret_cast<uint64_t*>(w8 + L.ws_seg_eoff);
     uint8_t* m8 = static_cast<uint8_t*>(msg);
 
+    StageTimer whole(timer, stream, ADACOMP_STAGE_COMPRESS_CALL);
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_TILE_PASS);
         for (int v = 0; v < adacomp::kVariants; ++v) {
@@ -348,6 +349,7 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.stop();
     }
+    whole.stop();
     return ADACOMP_OK;
 }
 
@@ -397,6 +399,7 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
     dw.dvalid = reinterpret_cast<uint32_t*>(w8 + D.dvalid);
     const uint32_t DT = static_cast<uint32_t>(L.dt.ntiles), DC = static_cast<uint32_t>(L.dt.nchunks);
 
+    StageTimer whole(timer, stream, ADACOMP_STAGE_DECODE_CALL);
     {
         StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_COUNT);
         hipLaunchKernelGGL(adacomp::k_decode_count, dim3(DC, K), dim3(256), 0, stream, mp,
@@ -436,6 +439,7 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
         }
         tm.stop();
     }
+    whole.stop();
     return ADACOMP_OK;
 }
 

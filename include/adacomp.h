@@ -162,7 +162,9 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
 #define ADACOMP_STAGE_DECODE_COUNT 4
 #define ADACOMP_STAGE_DECODE_BASE 5
 #define ADACOMP_STAGE_DECODE_APPLY 6
-#define ADACOMP_NUM_STAGES 7
+#define ADACOMP_STAGE_COMPRESS_CALL 7  /* a whole adacomp_compress call, gaps between kernels included */
+#define ADACOMP_STAGE_DECODE_CALL 8    /* a whole adacomp_decode_accumulate call */
+#define ADACOMP_NUM_STAGES 9
 
 int adacomp_timer_create(adacomp_timer** timer);
 int adacomp_timer_destroy(adacomp_timer* timer);

@@ -200,8 +200,10 @@ def test_timer_reports_every_stage():
     for _ in range(3):
         A.compress(plan, r, d, msg, ws, timer=t)
     rd = t.read()
-    for st in ("tile_pass", "chunk_scan", "finalize", "encode"):
+    for st in ("tile_pass", "chunk_scan", "finalize", "encode", "compress_call"):
         assert rd[st][1] == 3 and rd[st][0] > 0
+    parts = sum(rd[st][0] for st in ("tile_pass", "chunk_scan", "finalize", "encode"))
+    assert rd["compress_call"][0] >= 0.9 * parts
     t.close()
     plan.close()
 

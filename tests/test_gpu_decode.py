@@ -154,3 +154,46 @@ def test_decode_large_workload_sampled():
     plan.close()
     del msgs, out, ws
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("K,lt", [(70, 50), (256, 500), (20, 1)])
+def test_decode_many_messages(K, lt):
+    """Message groups: more messages than one group holds (64 at most, fewer
+    when the bin prefixes of a tile are long), up to the 256-message limit."""
+    segs = [(0, 3001, lt), (3004, 517, lt)]
+    span = 3524
+    plan = A.Plan(segs)
+    rng = np.random.default_rng(K + lt)
+    cws = plan.compress_workspace(DEV)
+    msgs, host_msgs = [], []
+    for k in range(K):
+        r = torch.from_numpy((rng.standard_normal(span) * 1e-3).astype(np.float32)).to(DEV)
+        d = torch.from_numpy((rng.standard_normal(span) * 1e-3 * (1 + k % 3)).astype(np.float32)).to(DEV)
+        m = plan.message_buffer(DEV)
+        A.compress(plan, r, d, m, cws)
+        total, _, _ = A.message_header(plan, m)
+        msgs.append(m[:total].clone())
+        host_msgs.append(host(msgs[-1]))
+    ws = plan.decode_workspace(K, DEV)
+    start = rng.standard_normal(span).astype(np.float32)
+    out = torch.from_numpy(start.copy()).to(DEV)
+    say(f"  decode K={K} L_T={lt}")
+    A.decode_accumulate(plan, msgs, out, True, ws)
+    want = start.copy()
+    oracle.decode_accumulate(segs, host_msgs, want, True)
+    np.testing.assert_array_equal(bits(host(out)), bits(want))
+    plan.close()
+
+
+def test_decode_rejects_too_many_messages():
+    segs = [(0, 100, 50)]
+    plan = A.Plan(segs)
+    m = plan.message_buffer(DEV)
+    out = torch.zeros(100, dtype=torch.float32, device=DEV)
+    with pytest.raises(A.AdaCompError) as e:
+        A.decode_accumulate(plan, [m] * 257, out, False, plan.decode_workspace(257, DEV))
+    assert e.value.status == -1
+    with pytest.raises(A.AdaCompError) as e:
+        A.decode_accumulate(plan, [m], out, False, plan.decode_workspace(1, DEV)[:16])
+    assert e.value.status == -5
+    plan.close()
