@@ -50,12 +50,15 @@ hipError_t launch_tile_pass(const adacomp_plan* plan, hipStream_t stream, float*
 }
 }  // namespace adacomp
 
+// Per-call device timing: one event at the start of a call and one after each
+// stage, so consecutive stages share their boundary event.
 struct adacomp_timer {
-    struct Rec {
-        int stage;
-        hipEvent_t a, b;
+    struct Call {
+        std::vector<hipEvent_t> ev;   // ev[0] call start, ev[i + 1] end of stage[i]
+        std::vector<int> stage;
+        int whole;                    // the whole-call stage, ev.front() .. ev.back()
     };
-    std::vector<Rec> recs;
+    std::vector<Call> calls;
     double ms[ADACOMP_NUM_STAGES] = {};
     uint64_t n[ADACOMP_NUM_STAGES] = {};
 };
@@ -79,31 +82,43 @@ int check_device(const adacomp_plan* plan) {
     return dev == plan->device ? ADACOMP_OK : ADACOMP_ERR_INVALID_ARGUMENT;
 }
 
-// Records one stage's events around a group of launches.
-struct StageTimer {
+// Records the boundary events of one call's stages on its stream.  Any
+// event failure switches timing off for the call; launches are unaffected.
+struct CallTimer {
     adacomp_timer* t;
     hipStream_t s;
-    hipEvent_t a = nullptr, b = nullptr;
-    int stage;
-    StageTimer(adacomp_timer* timer, hipStream_t stream, int st) : t(timer), s(stream), stage(st) {
-        if (!t) return;
-        if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
-            t = nullptr;
+    adacomp_timer::Call c;
+    CallTimer(adacomp_timer* timer, hipStream_t stream, int whole) : t(timer), s(stream) {
+        c.whole = whole;
+        if (t) record();
+    }
+    void record() {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) {
+            drop();
             return;
         }
-        (void)hipEventRecord(a, s);
+        c.ev.push_back(e);
+        if (hipEventRecord(e, s) != hipSuccess) drop();
     }
-    void stop() {
+    void mark(int stage) {   // end of `stage`, start of the next one
         if (!t) return;
-        (void)hipEventRecord(b, s);
-        t->recs.push_back({stage, a, b});
+        c.stage.push_back(stage);
+        record();
+    }
+    void finish() {
+        if (!t) return;
+        t->calls.push_back(std::move(c));
+        c = adacomp_timer::Call{};
         t = nullptr;
     }
-    ~StageTimer() {
-        if (!t) return;   // a launch failed before stop(): drop the events
-        (void)hipEventDestroy(a);
-        (void)hipEventDestroy(b);
+    void drop() {
+        for (hipEvent_t e : c.ev) (void)hipEventDestroy(e);
+        c.ev.clear();
+        c.stage.clear();
+        t = nullptr;
     }
+    ~CallTimer() { drop(); }   // a launch failed before finish()
 };
 
 int launch_status() {
@@ -303,9 +318,8 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     uint64_t* seg_eoff = reinterpret_cast<uint64_t*>(w8 + L.ws_seg_eoff);
     uint8_t* m8 = static_cast<uint8_t*>(msg);
 
-    StageTimer whole(timer, stream, ADACOMP_STAGE_COMPRESS_CALL);
+    CallTimer tm(timer, stream, ADACOMP_STAGE_COMPRESS_CALL);
     {
-        StageTimer tm(timer, stream, ADACOMP_STAGE_TILE_PASS);
         for (int v = 0; v < adacomp::kVariants; ++v) {
             if (L.ct.by_variant[v].empty()) continue;
             hipError_t e;
@@ -320,26 +334,23 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
                                                  tile_gsum, bin_max_out);
             if (e != hipSuccess) return ADACOMP_ERR_HIP;
         }
-        tm.stop();
+        tm.mark(ADACOMP_STAGE_TILE_PASS);
     }
     {
-        StageTimer tm(timer, stream, ADACOMP_STAGE_CHUNK_SCAN);
         hipLaunchKernelGGL(adacomp::k_chunk_scan, dim3(static_cast<uint32_t>(L.ct.nchunks)), dim3(256),
                            0, stream, plan->dct.chunk_tile_begin, tile_cnt, tile_gsum, tile_off,
                            chunk_cnt, chunk_gsum);
         if ((st = launch_status()) != ADACOMP_OK) return st;
-        tm.stop();
+        tm.mark(ADACOMP_STAGE_CHUNK_SCAN);
     }
     {
-        StageTimer tm(timer, stream, ADACOMP_STAGE_FINALIZE);
         hipLaunchKernelGGL(adacomp::k_finalize, dim3(1), dim3(256), 0, stream, plan->d_segs, L.nseg,
                            L.plan_hash, L.entries_begin, chunk_cnt, chunk_gsum, chunk_base, seg_s,
                            seg_nsurv, seg_eoff, m8);
         if ((st = launch_status()) != ADACOMP_OK) return st;
-        tm.stop();
+        tm.mark(ADACOMP_STAGE_FINALIZE);
     }
     {
-        StageTimer tm(timer, stream, ADACOMP_STAGE_ENCODE);
         hipLaunchKernelGGL(adacomp::k_encode,
                            dim3(static_cast<uint32_t>((L.ct.ntiles + 4 * adacomp::kEncTiles - 1) /
                                                       (4 * adacomp::kEncTiles))),
@@ -347,9 +358,9 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
                            0, stream, plan->d_segs, plan->dct.tile_seg, stage, tile_cnt, tile_off,
                            chunk_base, seg_s, seg_eoff, m8, residue, static_cast<uint32_t>(L.ct.ntiles));
         if ((st = launch_status()) != ADACOMP_OK) return st;
-        tm.stop();
+        tm.mark(ADACOMP_STAGE_ENCODE);
     }
-    whole.stop();
+    tm.finish();
     return ADACOMP_OK;
 }
 
@@ -399,24 +410,21 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
     dw.dvalid = reinterpret_cast<uint32_t*>(w8 + D.dvalid);
     const uint32_t DT = static_cast<uint32_t>(L.dt.ntiles), DC = static_cast<uint32_t>(L.dt.nchunks);
 
-    StageTimer whole(timer, stream, ADACOMP_STAGE_DECODE_CALL);
+    CallTimer tm(timer, stream, ADACOMP_STAGE_DECODE_CALL);
     {
-        StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_COUNT);
         hipLaunchKernelGGL(adacomp::k_decode_count, dim3(DC, K), dim3(256), 0, stream, mp,
                            plan->d_segs, plan->ddt.chunk_tile_begin, plan->ddt.chunk_seg, DT, DC,
                            L.nseg, L.plan_hash, dw);
         if ((st = launch_status()) != ADACOMP_OK) return st;
-        tm.stop();
+        tm.mark(ADACOMP_STAGE_DECODE_COUNT);
     }
     {
-        StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_BASE);
         hipLaunchKernelGGL(adacomp::k_decode_base, dim3(1), dim3(256), 0, stream, mp, K,
                            plan->d_segs, L.nseg, L.plan_hash, DC, dw);
         if ((st = launch_status()) != ADACOMP_OK) return st;
-        tm.stop();
+        tm.mark(ADACOMP_STAGE_DECODE_BASE);
     }
     {
-        StageTimer tm(timer, stream, ADACOMP_STAGE_DECODE_APPLY);
         for (int v = 0; v < adacomp::kDecVariants; ++v) {
             const uint32_t n = static_cast<uint32_t>(L.dt.by_variant[v].size());
             if (n == 0) continue;
@@ -437,9 +445,9 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
             }
             if ((st = launch_status()) != ADACOMP_OK) return st;
         }
-        tm.stop();
+        tm.mark(ADACOMP_STAGE_DECODE_APPLY);
     }
-    whole.stop();
+    tm.finish();
     return ADACOMP_OK;
 }
 
@@ -459,12 +467,11 @@ int adacomp_timer_create(adacomp_timer** timer) {
 int adacomp_timer_reset(adacomp_timer* timer) {
     if (timer == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
     int st = ADACOMP_OK;
-    for (auto& r : timer->recs) {
-        if (hipEventSynchronize(r.b) != hipSuccess) st = ADACOMP_ERR_HIP;
-        (void)hipEventDestroy(r.a);
-        (void)hipEventDestroy(r.b);
+    for (auto& c : timer->calls) {
+        if (hipEventSynchronize(c.ev.back()) != hipSuccess) st = ADACOMP_ERR_HIP;
+        for (hipEvent_t e : c.ev) (void)hipEventDestroy(e);
     }
-    timer->recs.clear();
+    timer->calls.clear();
     for (int i = 0; i < ADACOMP_NUM_STAGES; ++i) {
         timer->ms[i] = 0.0;
         timer->n[i] = 0;
@@ -481,16 +488,20 @@ int adacomp_timer_destroy(adacomp_timer* timer) {
 
 int adacomp_timer_read(adacomp_timer* timer, double* ms, uint64_t* launches, uint32_t nstages) {
     if (timer == nullptr || ms == nullptr || launches == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
-    for (auto& r : timer->recs) {
-        if (hipEventSynchronize(r.b) != hipSuccess) return ADACOMP_ERR_HIP;
+    for (auto& c : timer->calls) {
+        if (hipEventSynchronize(c.ev.back()) != hipSuccess) return ADACOMP_ERR_HIP;
         float t = 0.f;
-        if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return ADACOMP_ERR_HIP;
-        timer->ms[r.stage] += t;
-        timer->n[r.stage] += 1;
-        (void)hipEventDestroy(r.a);
-        (void)hipEventDestroy(r.b);
+        for (size_t i = 0; i < c.stage.size(); ++i) {
+            if (hipEventElapsedTime(&t, c.ev[i], c.ev[i + 1]) != hipSuccess) return ADACOMP_ERR_HIP;
+            timer->ms[c.stage[i]] += t;
+            timer->n[c.stage[i]] += 1;
+        }
+        if (hipEventElapsedTime(&t, c.ev.front(), c.ev.back()) != hipSuccess) return ADACOMP_ERR_HIP;
+        timer->ms[c.whole] += t;
+        timer->n[c.whole] += 1;
+        for (hipEvent_t e : c.ev) (void)hipEventDestroy(e);
     }
-    timer->recs.clear();
+    timer->calls.clear();
     for (uint32_t i = 0; i < nstages && i < ADACOMP_NUM_STAGES; ++i) {
         ms[i] = timer->ms[i];
         launches[i] = timer->n[i];

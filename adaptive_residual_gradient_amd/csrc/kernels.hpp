@@ -495,8 +495,17 @@ k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
 // Encode + residue fix-up.  Each wavefront covers 64 consecutive tiles: lane
 // i reads tile i's metadata, a wavefront scan of the survivor counts flattens
 // the 64 tiles' survivors, and the lanes then walk them 64 at a time, so one
-// round of metadata latency serves ~64 tiles.
+// round of metadata latency serves ~64 tiles.  The staged pairs of
+// kEncBatch rounds are loaded before any of them is used, so a wavefront
+// waits for memory about once per kEncBatch * 64 survivors.
 constexpr uint32_t kEncTiles = 64;
+#ifndef ADACOMP_ENC_BATCH
+#define ADACOMP_ENC_BATCH 8
+#endif
+#ifndef ADACOMP_ENC_NT
+#define ADACOMP_ENC_NT 0
+#endif
+constexpr int kEncBatch = ADACOMP_ENC_BATCH;
 
 __global__ void __launch_bounds__(256)
 k_encode(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
@@ -538,25 +547,41 @@ k_encode(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
     if (lane == 0) pre[wv][0] = 0;
     __syncthreads();
     const uint32_t E = pre[wv][kEncTiles];
-    for (uint32_t e = lane; e < E; e += 64) {
-        uint32_t lo = 0, hi = kEncTiles;   // pre[lo] <= e < pre[hi]
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (pre[wv][mid] <= e) lo = mid; else hi = mid;
+    for (uint32_t e0 = lane; e0 < E; e0 += 64u * kEncBatch) {
+        uint32_t at[kEncBatch], rk[kEncBatch];
+        uint2 p[kEncBatch];
+        // Loads first: lanes past the end reload the last survivor.
+#pragma unroll
+        for (int u = 0; u < kEncBatch; ++u) {
+            const uint32_t e = min(e0 + 64u * u, E - 1u);
+            uint32_t lo = 0, hi = kEncTiles;   // pre[lo] <= e < pre[hi]
+#pragma unroll
+            for (int step = 0; step < 6; ++step) {
+                const uint32_t mid = (lo + hi) >> 1;
+                if (pre[wv][mid] <= e) lo = mid; else hi = mid;
+            }
+            at[u] = lo;
+            rk[u] = e - pre[wv][lo];
+            p[u] = stage[t0s[wv][lo] + rk[u]];
         }
-        const uint32_t r = e - pre[wv][lo];
-        const uint64_t t0 = t0s[wv][lo];
-        const uint32_t lt = lts[wv][lo], wb = wbs[wv][lo];
-        const uint2 p = stage[t0 + r];
-        const uint32_t x = p.x & 0x7FFFFFFFu;
-        const uint32_t neg = p.x >> 31;
-        const uint32_t b = div_bin(x, lt, mags[wv][lo]);
-        const uint32_t topbit = wb == 1u ? 7u : 15u;
-        put_word(msg + eat[wv][lo] + uint64_t(r) * wb, wb, (neg << topbit) | (x - b * lt));
-        const float gv = __uint_as_float(p.y);
-        const float s = ss[wv][lo];
-        // residue <- G - G_q with G_q = sign(G) * s
-        residue[t0 + x] = neg ? gv + s : gv - s;
+#pragma unroll
+        for (int u = 0; u < kEncBatch; ++u) {
+            if (e0 + 64u * u >= E) break;
+            const uint32_t lo = at[u], r = rk[u];
+            const uint64_t t0 = t0s[wv][lo];
+            const uint32_t lt = lts[wv][lo], wb = wbs[wv][lo];
+            const uint32_t x = p[u].x & 0x7FFFFFFFu;
+            const uint32_t neg = p[u].x >> 31;
+            const uint32_t b = div_bin(x, lt, mags[wv][lo]);
+            const uint32_t topbit = wb == 1u ? 7u : 15u;
+            put_word(msg + eat[wv][lo] + uint64_t(r) * wb, wb, (neg << topbit) | (x - b * lt));
+            const float gv = __uint_as_float(p[u].y);
+            const float s = ss[wv][lo];
+            // residue <- G - G_q with G_q = sign(G) * s
+            const float rv = neg ? gv + s : gv - s;
+            if (ADACOMP_ENC_NT) __builtin_nontemporal_store(rv, residue + t0 + x);
+            else residue[t0 + x] = rv;
+        }
     }
 }
 
