@@ -121,6 +121,14 @@ struct CallTimer {
     ~CallTimer() { drop(); }   // a launch failed before finish()
 };
 
+// Encode workgroups (4 wavefronts each): about one wavefront per 2048
+// elements, at most one per wavefront slot of the chip.  The survivors are
+// shared out evenly among them on the device.
+uint32_t encode_blocks(const Layout& L) {
+    const uint64_t b = (L.total_numel + 8191) / 8192;
+    return static_cast<uint32_t>(std::min<uint64_t>(std::max<uint64_t>(b, 1), adacomp::kEncMaxBlocks));
+}
+
 int launch_status() {
     return hipGetLastError() == hipSuccess ? ADACOMP_OK : ADACOMP_ERR_HIP;
 }
@@ -316,6 +324,7 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     float* seg_s = reinterpret_cast<float*>(w8 + L.ws_seg_s);
     uint32_t* seg_nsurv = reinterpret_cast<uint32_t*>(w8 + L.ws_seg_nsurv);
     uint64_t* seg_eoff = reinterpret_cast<uint64_t*>(w8 + L.ws_seg_eoff);
+    uint64_t* seg_sbase = reinterpret_cast<uint64_t*>(w8 + L.ws_seg_sbase);
     uint8_t* m8 = static_cast<uint8_t*>(msg);
 
     CallTimer tm(timer, stream, ADACOMP_STAGE_COMPRESS_CALL);
@@ -346,17 +355,15 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     {
         hipLaunchKernelGGL(adacomp::k_finalize, dim3(1), dim3(256), 0, stream, plan->d_segs, L.nseg,
                            L.plan_hash, L.entries_begin, chunk_cnt, chunk_gsum, chunk_base, seg_s,
-                           seg_nsurv, seg_eoff, m8);
+                           seg_nsurv, seg_eoff, seg_sbase, m8);
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.mark(ADACOMP_STAGE_FINALIZE);
     }
     {
-        hipLaunchKernelGGL(adacomp::k_encode,
-                           dim3(static_cast<uint32_t>((L.ct.ntiles + 4 * adacomp::kEncTiles - 1) /
-                                                      (4 * adacomp::kEncTiles))),
-                           dim3(256),
-                           0, stream, plan->d_segs, plan->dct.tile_seg, stage, tile_cnt, tile_off,
-                           chunk_base, seg_s, seg_eoff, m8, residue, static_cast<uint32_t>(L.ct.ntiles));
+        hipLaunchKernelGGL(adacomp::k_encode, dim3(encode_blocks(L)), dim3(256), 0, stream,
+                           plan->d_segs, L.nseg, plan->dct.tile_seg, stage, tile_cnt, tile_off,
+                           chunk_base, seg_s, seg_eoff, seg_sbase, m8, residue,
+                           static_cast<uint32_t>(L.ct.ntiles));
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.mark(ADACOMP_STAGE_ENCODE);
     }

@@ -158,7 +158,7 @@ struct Layout {
     // Compress workspace (byte offsets).
     uint64_t ws_stage = 0, ws_tile_cnt = 0, ws_tile_gsum = 0, ws_tile_off = 0;
     uint64_t ws_chunk_cnt = 0, ws_chunk_gsum = 0, ws_chunk_base = 0;
-    uint64_t ws_seg_s = 0, ws_seg_nsurv = 0, ws_seg_eoff = 0, ws_compress = 0;
+    uint64_t ws_seg_s = 0, ws_seg_nsurv = 0, ws_seg_eoff = 0, ws_seg_sbase = 0, ws_compress = 0;
 
     // Decode workspace: fixed part, then per-message arrays.
     uint64_t dws_fixed = 0, dws_per_msg = 0;
@@ -309,6 +309,7 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
     L.ws_seg_s = take(4 * uint64_t(nseg));
     L.ws_seg_nsurv = take(4 * uint64_t(nseg));
     L.ws_seg_eoff = take(8 * uint64_t(nseg));
+    L.ws_seg_sbase = take(8 * (uint64_t(nseg) + 1));   // survivors before each segment, then the total
     L.ws_compress = w;
 
     // Decode workspace for K messages: a status block, then arrays indexed by

@@ -134,6 +134,41 @@ def test_degenerate_inputs():
     plan.close()
 
 
+def test_survivor_distribution_extremes():
+    """The encode shares survivors out evenly among wavefronts, so its start
+    search and tile walk must hold for both extremes: a few survivors spread
+    over long runs of empty tiles (most bins all zero), and a first step from
+    a zero residue where a large share of the elements survive."""
+    segs = [(0, 3000000, 50), (3000000, 1000000, 500), (4000000, 2000003, 7),
+            (6000004, 4096, 4093)]
+    span = 6000004 + 4096
+    plan = A.Plan(segs)
+    msg, ws = plan.message_buffer(DEV), plan.compress_workspace(DEV)
+    gmax = torch.empty(int(plan.info.total_bins), dtype=torch.float32, device=DEV)
+    rng = np.random.default_rng(11)
+    # sparse: only every 997th bin of each layer is nonzero
+    r = np.zeros(span, np.float32)
+    d = np.zeros(span, np.float32)
+    for off, n, lt in segs:
+        for b0 in range(0, n, 997 * lt):
+            e = min(b0 + lt, n)
+            d[off + b0:off + e] = (rng.standard_normal(e - b0) * 1e-3).astype(np.float32)
+    say("  sparse survivors")
+    m, r_out, g = run_gpu_step(plan, torch.from_numpy(r.copy()).to(DEV), torch.from_numpy(d).to(DEV),
+                               msg, ws, gmax)
+    rep = compare_step(segs, r, d, r_out, m, g)
+    say(f"    survivors {rep.survivors}")
+    # dense: first step from zero residue
+    d = (rng.standard_normal(span) * 1e-3).astype(np.float32)
+    say("  dense first step")
+    m, r_out, g = run_gpu_step(plan, torch.from_numpy(r.copy()).to(DEV), torch.from_numpy(d).to(DEV),
+                               msg, ws, gmax)
+    rep = compare_step(segs, r, d, r_out, m, g)
+    say(f"    survivors {rep.survivors}")
+    assert rep.survivors > span // 20
+    plan.close()
+
+
 def test_determinism_and_resume():
     """Two runs give the same bits; 5 steps + residue checkpoint + 5 steps equal
     10 straight steps."""
