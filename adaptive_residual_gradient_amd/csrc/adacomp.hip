@@ -33,6 +33,7 @@ struct adacomp_plan {
     void* dmem = nullptr;
     SegDev* d_segs = nullptr;
     DevTiling dct, ddt;                                        // compress and decode tiles
+    adacomp::DecDesc* ddesc[adacomp::kDecVariants] = {nullptr, nullptr};   // decode tiles in launch order
     uint32_t tile_lds_words[adacomp::kVariants] = {0, 0, 0};  // one tile's LDS words
 };
 
@@ -241,6 +242,11 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
         };
         const uint64_t o_segs = put(L.segs.data(), sizeof(SegDev) * L.nseg);
         const TilingOffsets oc = put_tiling(L.ct), od = put_tiling(L.dt);
+        uint64_t o_desc[adacomp::kDecVariants];
+        for (int v = 0; v < adacomp::kDecVariants; ++v) {
+            const std::vector<adacomp::DecDesc> d = adacomp::decode_descs(L, v);
+            o_desc[v] = put(d.data(), sizeof(adacomp::DecDesc) * d.size());
+        }
         if (hipMalloc(&p->dmem, host.size()) != hipSuccess) {
             p->dmem = nullptr;
             delete p;
@@ -262,6 +268,8 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
         };
         bind(p->dct, oc);
         bind(p->ddt, od);
+        for (int v = 0; v < adacomp::kDecVariants; ++v)
+            p->ddesc[v] = reinterpret_cast<adacomp::DecDesc*>(base + o_desc[v]);
         for (int v = 0; v < adacomp::kVariants; ++v) p->tile_lds_words[v] = 2 * L.ct.max_bpt[v] + 1;
         *out = p;
         return ADACOMP_OK;
@@ -441,14 +449,13 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
                 const uint32_t acc_words = L.dt.max_span_vecs[0] * 4;
                 const uint32_t lds = adacomp::decode_lds_bytes(acc_words, K, KG, ps, 4);
                 hipLaunchKernelGGL((adacomp::k_decode_apply<256, true>), dim3(n), dim3(256), lds,
-                                   stream, mp, K, KG, plan->d_segs, plan->ddt.tile_seg,
-                                   plan->ddt.vtiles[0], DT, DC, L.nseg, dw, out, accumulate,
-                                   acc_words);
+                                   stream, mp, K, KG, ps, plan->ddesc[0], DT, DC, L.nseg, dw, out,
+                                   accumulate, acc_words);
             } else {        // long bins, accumulated in place in out
                 const uint32_t lds = adacomp::decode_lds_bytes(0, K, KG, ps, 16);
                 hipLaunchKernelGGL((adacomp::k_decode_apply<1024, false>), dim3(n), dim3(1024), lds,
-                                   stream, mp, K, KG, plan->d_segs, plan->ddt.tile_seg,
-                                   plan->ddt.vtiles[1], DT, DC, L.nseg, dw, out, accumulate, 0u);
+                                   stream, mp, K, KG, ps, plan->ddesc[1], DT, DC, L.nseg, dw, out,
+                                   accumulate, 0u);
             }
             if ((st = launch_status()) != ADACOMP_OK) return st;
         }

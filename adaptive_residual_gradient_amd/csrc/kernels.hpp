@@ -663,6 +663,24 @@ __device__ __forceinline__ bool header_matches(const uint8_t* m, uint32_t nseg, 
            *reinterpret_cast<const uint32_t*>(m + 12) == plan_hash;
 }
 
+// Sum of the count words in message bytes [a0, a1), read as the aligned
+// 32-bit words that cover them (count regions start 16-byte aligned and are
+// zero-padded to 16 bytes, so those words lie inside the message).
+__device__ __forceinline__ uint32_t sum_count_words(const uint8_t* m, uint64_t a0, uint64_t a1,
+                                                    uint32_t wb) {
+    typedef const __attribute__((address_space(1))) uint32_t* gu32;
+    uint32_t s = 0;
+#pragma unroll 4
+    for (uint64_t d = a0 & ~uint64_t(3); d < a1; d += 4) {
+        uint32_t v = *(gu32)(m + d);
+        if (d < a0) v &= ~0u << (8u * uint32_t(a0 - d));          // bytes before a0
+        if (d + 4 > a1) v &= ~0u >> (8u * uint32_t(d + 4 - a1));  // bytes from a1 on
+        s += wb == 1u ? (v & 0xFFu) + ((v >> 8) & 0xFFu) + ((v >> 16) & 0xFFu) + (v >> 24)
+                      : (v & 0xFFFFu) + (v >> 16);
+    }
+    return s;
+}
+
 // Per (chunk of decode tiles, message): survivors of each decode tile from
 // the count words, offsets within the chunk, chunk totals.
 __global__ void __launch_bounds__(256)
@@ -685,8 +703,8 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
         if (ok && t < n) {
             const uint32_t first_bin = (tb + t - sg.dt.tile_begin) * sg.dt.bpt;
             const uint32_t nb = min(sg.dt.bpt, sg.nbins - first_bin);
-            const uint8_t* cw = m + sg.count_off + uint64_t(first_bin) * sg.wb;
-            for (uint32_t b = 0; b < nb; ++b) s += get_word(cw + uint64_t(b) * sg.wb, sg.wb);
+            const uint64_t a0 = sg.count_off + uint64_t(first_bin) * sg.wb;
+            s = sum_count_words(m, a0, a0 + uint64_t(nb) * sg.wb, sg.wb);
         }
         cnt[i] = s;
         mine += s;
@@ -750,6 +768,11 @@ k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, uint32_
 // global-address-space pointer (a global load, not a flat one).
 typedef const __attribute__((address_space(1))) uint16_t* global_u16_ptr;
 
+#ifndef ADACOMP_DEC_BATCH
+#define ADACOMP_DEC_BATCH 2
+#endif
+constexpr int kDecBatch = ADACOMP_DEC_BATCH;   // entry rounds whose loads are issued together
+
 __device__ __forceinline__ uint32_t word_at(uint64_t a, uint32_t wb) {
     const uint32_t w16 = *(global_u16_ptr)(a & ~uint64_t(1));
     return wb == 1u ? (w16 >> (8u * uint32_t(a & 1u))) & 0xFFu : w16;
@@ -764,50 +787,42 @@ __device__ __forceinline__ uint32_t word_at(uint64_t a, uint32_t wb) {
 // group (message-major) 64 at a time and adds them message by message.  One
 // wavefront's LDS operations execute in program order, so the additions to
 // an element happen in message order without block barriers.
-// Dynamic LDS: [acc_words floats if LDS_ACC][K u64 message bases][KG u64
-// entry addresses][K floats s][K u32 validity][NW*(KG+1) u32 per-wavefront
-// flat prefixes][KG*(bpt+1) u32 bin prefixes].
+// Dynamic LDS: [acc_words floats if LDS_ACC][KG u64 entry addresses][K
+// floats s][NW*(KG+1) u32 per-wavefront flat prefixes][KG*pstride u32 bin
+// prefixes].  Everything else about the tile comes from its descriptor.
 
 template <int THREADS, bool LDS_ACC>
 __global__ void __launch_bounds__(THREADS)
-k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__ segs,
-               const uint32_t* __restrict__ tile_seg, const uint32_t* __restrict__ vtiles,
-               uint32_t DT, uint32_t DC, uint32_t nseg, DecodeWs ws, float* __restrict__ out,
-               int accumulate, uint32_t acc_words) {
+k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
+               const DecDesc* __restrict__ descs, uint32_t DT, uint32_t DC, uint32_t nseg,
+               DecodeWs ws, float* __restrict__ out, int accumulate, uint32_t acc_words) {
     constexpr int NW = THREADS / 64;
     extern __shared__ uint64_t dyn64[];
     uint32_t* dyn = reinterpret_cast<uint32_t*>(dyn64);
     const uint32_t accw = LDS_ACC ? (acc_words + 1u) & ~1u : 0u;   // keep 8-byte alignment
-    uint64_t* mbase = reinterpret_cast<uint64_t*>(dyn + accw);
-    uint64_t* eaddr = mbase + K;
+    uint64_t* eaddr = reinterpret_cast<uint64_t*>(dyn + accw);
     float* ks = reinterpret_cast<float*>(eaddr + KG);
-    uint32_t* kvalid = reinterpret_cast<uint32_t*>(ks + K);
-    uint32_t* wfk_all = kvalid + K;                       // [NW][KG + 1]
-    uint32_t* pref = wfk_all + NW * (KG + 1);             // [KG][bpt + 1]
+    uint32_t* wfk_all = reinterpret_cast<uint32_t*>(ks + K);   // [NW][KG + 1]
+    uint32_t* pref = wfk_all + NW * (KG + 1);             // [KG][pstride]
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const uint32_t tile = vtiles[blockIdx.x];
-    const uint32_t si = tile_seg[tile];
-    const SegDev sg = segs[si];
-    const TileGeom tg = tile_geom(sg, sg.dt, tile);
-    const uint32_t chunk = sg.dt.chunk_begin + (tile - sg.dt.tile_begin) / kChunkTiles;
-    float* acc = LDS_ACC ? reinterpret_cast<float*>(dyn) : out + tg.v0;
-    const uint32_t pstride = sg.dt.bpt + 1;
-    const uint32_t wb = sg.wb, lt = sg.lt;
+    const DecDesc dd = descs[blockIdx.x];
+    const uint64_t v0 = dd.t0 & ~uint64_t(3);
+    const uint32_t lead = uint32_t(dd.t0 - v0);
+    const uint32_t nvec = (lead + dd.tlen + 3u) >> 2;
+    const uint32_t nb = dd.nb, tlen = dd.tlen;
+    float* acc = LDS_ACC ? reinterpret_cast<float*>(dyn) : out + v0;
+    const uint32_t wb = dd.wb, lt = dd.lt;
     const uint32_t topbit = wb == 1u ? 7u : 15u;
-    const uint32_t wb0 = tg.nb * uint32_t(wv) / NW, wb1 = tg.nb * uint32_t(wv + 1) / NW;
+    const uint32_t wb0 = nb * uint32_t(wv) / NW, wb1 = nb * uint32_t(wv + 1) / NW;
     uint32_t* wfk = wfk_all + wv * (KG + 1);
 
-    for (uint32_t k = tid; k < K; k += THREADS) {
-        mbase[k] = reinterpret_cast<uint64_t>(msgs.p[k]);
-        kvalid[k] = ws.dvalid[k];
-        ks[k] = ws.dseg_s[uint64_t(k) * nseg + si];
-    }
+    for (uint32_t k = tid; k < K; k += THREADS) ks[k] = ws.dseg_s[uint64_t(k) * nseg + dd.si];
     // Initial values: +0, or out.
-    for (uint32_t vi = tid; vi < tg.nvec; vi += THREADS) {
-        const int x0 = int(vi * 4) - int(tg.lead);
-        const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
-        if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
+    for (uint32_t vi = tid; vi < nvec; vi += THREADS) {
+        const int x0 = int(vi * 4) - int(lead);
+        const uint64_t e0 = v0 + uint64_t(vi) * 4u;
+        if (x0 >= 0 && x0 + 4 <= int(tlen)) {
             if (LDS_ACC) {
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
                 if (accumulate) a = load4<true>(out + e0);
@@ -818,7 +833,7 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__
         } else {
             for (int c = 0; c < 4; ++c) {
                 const int x = x0 + c;
-                if (x >= 0 && x < int(tg.tlen)) {
+                if (x >= 0 && x < int(tlen)) {
                     if (LDS_ACC) acc[vi * 4 + c] = accumulate ? out[e0 + c] : 0.0f;
                     else if (!accumulate) out[e0 + c] = 0.0f;
                 }
@@ -829,29 +844,32 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__
     for (uint32_t k0 = 0; k0 < K; k0 += KG) {
         const uint32_t kn = min(KG, K - k0);
         __syncthreads();   // bases staged; the previous group is done with pref
-        // Count words of the tile's bins for this group of messages.
-        for (uint32_t i = tid; i < kn * tg.nb; i += THREADS) {
-            const uint32_t kk = i / tg.nb, b = i - kk * tg.nb;
+        // Count words of the tile's bins for this group of messages (the
+        // message pointer and validity are read directly, not from LDS, so
+        // these loads wait only for the descriptor).
+        for (uint32_t i = tid; i < kn * nb; i += THREADS) {
+            const uint32_t kk = i / nb, b = i - kk * nb;
             const uint32_t k = k0 + kk;
             uint32_t cw = 0;
-            if (kvalid[k])
-                cw = word_at(mbase[k] + sg.count_off + uint64_t(tg.first_bin + b) * wb, wb);
+            if (ws.dvalid[k])
+                cw = word_at(reinterpret_cast<uint64_t>(msgs.p[k]) + dd.count_at + uint64_t(b) * wb, wb);
             pref[kk * pstride + b + 1] = cw;
         }
         if (tid < int(kn)) {
             const uint32_t k = k0 + tid;
-            const uint64_t base = uint64_t(ws.dchunk_base[uint64_t(k) * DC + chunk]) +
-                                  ws.doff[uint64_t(k) * DT + tile];
-            eaddr[tid] = mbase[k] + ws.dseg_eoff[uint64_t(k) * nseg + si] + base * wb;
+            const uint64_t base = uint64_t(ws.dchunk_base[uint64_t(k) * DC + dd.chunk]) +
+                                  ws.doff[uint64_t(k) * DT + dd.tile];
+            eaddr[tid] = reinterpret_cast<uint64_t>(msgs.p[k]) +
+                         ws.dseg_eoff[uint64_t(k) * nseg + dd.si] + base * wb;
         }
         __syncthreads();
         // Per-message exclusive prefix over the tile's bins.
-        if (tg.nb <= 32) {
+        if (nb <= 32) {
             if (tid < int(kn)) {   // one thread per message
                 uint32_t* pr = pref + tid * pstride;
                 uint32_t run = 0;
                 pr[0] = 0;
-                for (uint32_t b = 0; b < tg.nb; ++b) {
+                for (uint32_t b = 0; b < nb; ++b) {
                     run += pr[b + 1];
                     pr[b + 1] = run;
                 }
@@ -860,16 +878,16 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__
             for (uint32_t kk = wv; kk < kn; kk += NW) {   // one wavefront per message
                 uint32_t* pr = pref + kk * pstride;
                 uint32_t carry = 0;
-                for (uint32_t b0 = 0; b0 < tg.nb; b0 += 64) {
+                for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
                     const uint32_t b = b0 + lane;
-                    const uint32_t v = b < tg.nb ? pr[b + 1] : 0u;
+                    const uint32_t v = b < nb ? pr[b + 1] : 0u;
                     uint32_t inc = v;
 #pragma unroll
                     for (int d = 1; d < 64; d <<= 1) {
                         const uint32_t t = __shfl_up(inc, d);
                         if (lane >= d) inc += t;
                     }
-                    if (b < tg.nb) pr[b + 1] = carry + inc;
+                    if (b < nb) pr[b + 1] = carry + inc;
                     carry += __shfl(inc, 63);
                 }
                 if (lane == 0) pr[0] = 0;
@@ -893,48 +911,61 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, const SegDev* __restrict__
             if (lane == 0) wfk[0] = 0;
         }
         const uint32_t Ew = wfk[kn];
-        for (uint32_t i0 = 0; i0 < Ew; i0 += 64) {
-            const uint32_t i = i0 + lane;
-            const bool valid = i < Ew;
-            const uint32_t ii = valid ? i : Ew - 1u;
-            uint32_t lo = 0, hi = kn;   // wfk[lo] <= ii < wfk[hi]
-            while (hi - lo > 1) {
-                const uint32_t mid = (lo + hi) >> 1;
-                if (wfk[mid] <= ii) lo = mid; else hi = mid;
+        // kDecBatch rounds of 64 entries: every entry word of the batch is
+        // requested before any is used, then the rounds are applied in order.
+        for (uint32_t i0 = 0; i0 < Ew; i0 += 64u * kDecBatch) {
+            uint32_t kof[kDecBatch], xs[kDecBatch], words[kDecBatch];
+#pragma unroll
+            for (int u = 0; u < kDecBatch; ++u) {
+                const uint32_t ii = min(i0 + 64u * u + uint32_t(lane), Ew - 1u);
+                uint32_t lo = 0, hi = kn;   // wfk[lo] <= ii < wfk[hi]
+                while (hi - lo > 1) {
+                    const uint32_t mid = (lo + hi) >> 1;
+                    if (wfk[mid] <= ii) lo = mid; else hi = mid;
+                }
+                const uint32_t* pr = pref + lo * pstride;
+                const uint32_t e = ii - wfk[lo] + pr[wb0];
+                uint32_t bl = wb0, bh = wb1;   // pr[bl] <= e < pr[bh]
+                while (bh - bl > 1) {
+                    const uint32_t mid = (bl + bh) >> 1;
+                    if (pr[mid] <= e) bl = mid; else bh = mid;
+                }
+                kof[u] = lo;
+                xs[u] = bl * lt;
+                words[u] = word_at(eaddr[lo] + uint64_t(e) * wb, wb);
             }
-            const uint32_t* pr = pref + lo * pstride;
-            const uint32_t e = ii - wfk[lo] + pr[wb0];
-            uint32_t bl = wb0, bh = wb1;   // pr[bl] <= e < pr[bh]
-            while (bh - bl > 1) {
-                const uint32_t mid = (bl + bh) >> 1;
-                if (pr[mid] <= e) bl = mid; else bh = mid;
-            }
-            const uint32_t word = word_at(eaddr[lo] + uint64_t(e) * wb, wb);
-            const uint32_t idx = word & ((1u << topbit) - 1u);
-            const uint32_t x = bl * lt + idx;
-            const float sk = ks[k0 + lo];
-            const float q = (word >> topbit) ? -sk : sk;
-            const bool apply = valid && idx < lt && x < tg.tlen;
-            // Messages present in this batch, applied in order.
-            const uint32_t klo = __builtin_amdgcn_readfirstlane(lo);
-            const uint32_t khi = __shfl(lo, int(min(Ew - i0, 64u) - 1u));
-            for (uint32_t kk = klo; kk <= khi; ++kk) {
-                if (apply && lo == kk) acc[x + tg.lead] = acc[x + tg.lead] + q;
-                if (!LDS_ACC) __threadfence_block();
+#pragma unroll
+            for (int u = 0; u < kDecBatch; ++u) {
+                const uint32_t r0 = i0 + 64u * u;
+                if (r0 >= Ew) break;   // wavefront-uniform
+                const uint32_t lo = kof[u];
+                const uint32_t word = words[u];
+                const uint32_t idx = word & ((1u << topbit) - 1u);
+                const uint32_t x = xs[u] + idx;
+                const float sk = ks[k0 + lo];
+                const float q = (word >> topbit) ? -sk : sk;
+                const bool apply = r0 + uint32_t(lane) < Ew && idx < lt && x < tlen;
+                // Messages present in this round, applied in order.
+                const uint32_t klo = __builtin_amdgcn_readfirstlane(lo);
+                const uint32_t khi = __shfl(lo, int(min(Ew - r0, 64u) - 1u));
+                for (uint32_t kk = klo; kk <= khi; ++kk) {
+                    if (apply && lo == kk) acc[x + lead] = acc[x + lead] + q;
+                    if (!LDS_ACC) __threadfence_block();
+                }
             }
         }
     }
     if (LDS_ACC) {
         __syncthreads();
-        for (uint32_t vi = tid; vi < tg.nvec; vi += THREADS) {
-            const int x0 = int(vi * 4) - int(tg.lead);
-            const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
-            if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
+        for (uint32_t vi = tid; vi < nvec; vi += THREADS) {
+            const int x0 = int(vi * 4) - int(lead);
+            const uint64_t e0 = v0 + uint64_t(vi) * 4u;
+            if (x0 >= 0 && x0 + 4 <= int(tlen)) {
                 store4<true>(out + e0, *reinterpret_cast<const f32x4*>(acc + vi * 4));
             } else {
                 for (int c = 0; c < 4; ++c) {
                     const int x = x0 + c;
-                    if (x >= 0 && x < int(tg.tlen)) out[e0 + c] = acc[vi * 4 + c];
+                    if (x >= 0 && x < int(tlen)) out[e0 + c] = acc[vi * 4 + c];
                 }
             }
         }

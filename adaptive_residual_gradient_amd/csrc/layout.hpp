@@ -120,6 +120,22 @@ struct Tiling {
     uint64_t ntiles = 0, nchunks = 0;
 };
 
+// Everything the decode apply kernel needs about one decode tile, built at
+// plan time in launch order so that a workgroup starts with a single load.
+struct DecDesc {
+    uint64_t t0;        // flat index of the tile's first element
+    uint64_t count_at;  // message byte offset of the tile's first count word
+    uint32_t tile;      // global decode tile index
+    uint32_t si;        // segment
+    uint32_t nb;        // bins in the tile
+    uint32_t tlen;      // elements in the tile
+    uint32_t lt;
+    uint32_t wb;
+    uint32_t chunk;     // global decode scan chunk
+    uint32_t pad;
+};
+static_assert(sizeof(DecDesc) == 48, "DecDesc layout");
+
 // Decode tiles: accumulated in LDS up to kDecCap elements (L_T <= 4093),
 // otherwise one bin per tile accumulated in place in out.
 constexpr uint32_t kDecCap = 4096;
@@ -127,13 +143,13 @@ constexpr int kDecVariants = 2;
 constexpr uint32_t kDecThreads[kDecVariants] = {256, 1024};
 
 // Dynamic LDS bytes of the decode apply kernel: the tile accumulator
-// (acc_words floats, rounded to even), per message a u64 base, s and
-// validity, per group message a u64 entry address, the per-wavefront flat
-// prefixes and the bin prefixes of KG messages.
+// (acc_words floats, rounded to even), per group message a u64 entry
+// address, per message s, the per-wavefront flat prefixes and the bin
+// prefixes of KG messages.
 inline uint32_t decode_lds_bytes(uint32_t acc_words, uint32_t K, uint32_t KG, uint32_t pstride,
                                  uint32_t nw) {
     const uint32_t accw = (acc_words + 1u) & ~1u;
-    return 4u * (accw + 2u * K + 2u * KG + K + K + nw * (KG + 1u) + KG * pstride);
+    return 4u * (accw + 2u * KG + K + nw * (KG + 1u) + KG * pstride);
 }
 
 // Messages per decode group: at most 64 (one wavefront lane each) and as many
@@ -319,6 +335,29 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
     L.dws_fixed = 9 * kAlign;
     L.dws_per_msg = round_up(8 * L.dt.ntiles + 8 * L.dt.nchunks + 12 * uint64_t(nseg) + 4, 16);
     return ADACOMP_OK;
+}
+
+// Descriptors of the decode tiles of shape v, in launch order.
+inline std::vector<DecDesc> decode_descs(const Layout& L, int v) {
+    std::vector<DecDesc> out;
+    out.reserve(L.dt.by_variant[v].size());
+    for (uint32_t tile : L.dt.by_variant[v]) {
+        const uint32_t si = L.dt.tile_seg[tile];
+        const SegDev& sg = L.segs[si];
+        const TileGeom g = tile_geom(sg, sg.dt, tile);
+        DecDesc d{};
+        d.t0 = g.t0;
+        d.count_at = sg.count_off + uint64_t(g.first_bin) * sg.wb;
+        d.tile = tile;
+        d.si = si;
+        d.nb = g.nb;
+        d.tlen = g.tlen;
+        d.lt = sg.lt;
+        d.wb = sg.wb;
+        d.chunk = sg.dt.chunk_begin + (tile - sg.dt.tile_begin) / kChunkTiles;
+        out.push_back(d);
+    }
+    return out;
 }
 
 inline void fill_info(const Layout& L, adacomp_plan_info* info) {
