@@ -17,6 +17,10 @@
  *   [Lim]  Claims, Limitation "minibatch size, activity and variable message
  *          length" and "Curated Limitations & Negative Results": the number
  *          of transmitted elements varies, so the message has variable length.
+ *   [LS]   Claims, Mechanism "self-adjusting sparsity prevents residual
+ *          explosion" (Figures 4-6): the hard Local Selection (LS) baseline
+ *          that AdaComp is contrasted with, which has no soft threshold and
+ *          transmits only a fixed number of bin maxima.
  *
  * Per layer (segment) the pages define, in this order:
  *   G = residue + dW;  H = G + dW;  bins of length L_T over G;
@@ -37,6 +41,11 @@
  *     once to float.
  *   - the message layout below is this project's own definition; the pages
  *     give only the index word widths.
+ *   - LS (segment flag 1): per bin exactly one element is transmitted, the
+ *     first (lowest index) whose |G| equals the bin maximum, and none when
+ *     the maximum is 0; it is quantized with the same layer-wide s and the
+ *     residue is updated as above.  The page says only "a fixed number of
+ *     bin maxima"; one per bin is the plainest reading.
  *
  * Message layout (all fields little-endian, every region 16-byte aligned,
  * padding bytes zero):
@@ -60,8 +69,10 @@ typedef struct {
     uint64_t offset;  /* first element of the layer in the flat buffers */
     uint64_t numel;   /* number of elements of the layer */
     uint32_t bin_len; /* L_T */
-    uint32_t flags;   /* must be 0 */
+    uint32_t flags;   /* 0: AdaComp; ORACLE_FLAG_LS: hard local selection */
 } oracle_segment;
+
+#define ORACLE_FLAG_LS 1u
 
 enum {
     ORACLE_OK = 0,
@@ -134,7 +145,7 @@ static int check_segments(const oracle_segment *segs, uint32_t nseg) {
     for (uint32_t i = 0; i < nseg; ++i) {
         if (segs[i].numel == 0u || segs[i].numel >= ((uint64_t)1 << 32)) return ORACLE_BAD_ARG;
         if (segs[i].bin_len == 0u || segs[i].bin_len > 32768u) return ORACLE_BAD_ARG;
-        if (segs[i].flags != 0u) return ORACLE_BAD_ARG;
+        if (segs[i].flags != 0u && segs[i].flags != ORACLE_FLAG_LS) return ORACLE_BAD_ARG;
     }
     return ORACLE_OK;
 }
@@ -220,13 +231,19 @@ int oracle_compress(const oracle_segment *segs, uint32_t nseg, float *residue,
         const float s = (float)(acc / (double)B);
 
         /* [Def], [M1]: soft-threshold selection, ternary quantization and the
-         * residue update; [App]: the sparse-indexed ternarized words. */
+         * residue update; [App]: the sparse-indexed ternarized words.
+         * [LS]: instead of the soft threshold, only the bin's first maximum. */
+        const int ls = (sg->flags & ORACLE_FLAG_LS) != 0u;
         uint64_t nsurv = 0;
         for (uint64_t b = 0; b < B; ++b) {
             uint64_t lo = b * LT, hi = lo + LT < N ? lo + LT : N;
+            uint64_t first_max = hi;
+            if (ls && gmax[b] > 0.0f)
+                for (uint64_t j = lo; j < hi && first_max == hi; ++j)
+                    if (fabsf(G[j]) == gmax[b]) first_max = j;
             uint32_t cnt = 0;
             for (uint64_t j = lo; j < hi; ++j) {
-                int sent = fabsf(H[j]) >= gmax[b] && G[j] != 0.0f;
+                int sent = ls ? j == first_max : fabsf(H[j]) >= gmax[b] && G[j] != 0.0f;
                 if (sent) {
                     float gq = G[j] > 0.0f ? s : -s;
                     r[j] = G[j] - gq;

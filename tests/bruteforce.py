@@ -10,6 +10,12 @@ maxima rounded once to float32 (computed here with exact rationals), residue
 
 It shares nothing with the C oracle: scalar numpy.float32 arithmetic,
 fractions.Fraction for the mean, and the message bytes packed with struct.
+
+Segments with flag 1 use hard Local Selection (the baseline the same page's
+Mechanism claim "self-adjusting sparsity prevents residual explosion"
+contrasts AdaComp with): per bin only the first element whose |G| equals the
+bin maximum is sent, none when the maximum is 0; s and the residue update are
+unchanged.
 """
 from __future__ import annotations
 
@@ -52,7 +58,7 @@ def ulp_distance(a: np.float32, b: np.float32) -> int:
     return abs(ia - ib)
 
 
-def compress_segment(r, dw, bin_len):
+def compress_segment(r, dw, bin_len, ls=False):
     """Returns (new_residue list, gmax list, s, sent list of (idx, negative))."""
     n = len(r)
     G = [F32(F32(r[j]) + F32(dw[j])) for j in range(n)]
@@ -63,11 +69,19 @@ def compress_segment(r, dw, bin_len):
         members = [j for j in range(n) if j // bin_len == b]
         gmax.append(max(abs(G[j]) for j in members))
     s = rn_f32(sum((Fraction(float(g)) for g in gmax), Fraction(0)) / nb)
+    # LS: the first index of each bin holding the bin maximum (bins with a
+    # zero maximum send nothing)
+    first = {}
+    for j in range(n):
+        b = j // bin_len
+        if gmax[b] > 0 and abs(G[j]) == gmax[b] and b not in first:
+            first[b] = j
     new_r = []
     sent = []
     for j in range(n):
         g = gmax[j // bin_len]
-        if abs(H[j]) >= g and G[j] != 0:
+        chosen = first.get(j // bin_len) == j if ls else (abs(H[j]) >= g and G[j] != 0)
+        if chosen:
             q = s if G[j] > 0 else -s
             new_r.append(F32(G[j] - q))
             sent.append((j, bool(G[j] < 0)))
@@ -93,8 +107,9 @@ def compress(segments, residue: np.ndarray, dW: np.ndarray):
     total = 0
     for i, (off, n, lt, *rest) in enumerate(segments):
         wb = word_bytes(lt)
+        flags = rest[0] if rest else 0
         r_new, gmax, s, sent = compress_segment(list(residue[off:off + n]),
-                                                list(dW[off:off + n]), lt)
+                                                list(dW[off:off + n]), lt, ls=bool(flags & 1))
         out_r[off:off + n] = np.array(r_new, dtype=np.float32)
         gm_all += gmax
         s_all.append(s)

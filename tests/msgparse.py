@@ -172,7 +172,7 @@ def single_segment_message(buf, segments, i: int) -> bytes:
     _, n, lt, *rest = segments[i]
     wb = word_bytes(lt)
     nb = (n + lt - 1) // lt
-    sub = [(0, n, lt)]
+    sub = [(0, n, lt, *rest)]
     count_at = align16(32 + 16)
     entry_at = align16(count_at + nb * wb)
     dt = np.uint8 if wb == 1 else np.dtype("<u2")

@@ -459,7 +459,7 @@ def test_sent_count_adapts_to_activity():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("segs", [[(0, 0, 50)], [(0, 10, 0)], [(0, 10, 32769)],
-                                  [(0, 10, 50, 1)]])
+                                  [(0, 10, 50, 2)]])
 def test_oracle_rejects_bad_tables(segs):
     with pytest.raises(oracle.OracleError):
         oracle.message_capacity(segs)
@@ -485,3 +485,110 @@ def test_single_segment_repack_matches_full_decode():
                                  sub, False)
         np.testing.assert_array_equal(bits(sub), bits(full[o:o + n]))
         mp.parse(mp.single_segment_message(msgs[0], segs, i), [(0, n, lt)])
+
+
+# --------------------------------------------------------------------------
+# Hard Local Selection (segment flag 1): the baseline of the Mechanism claim
+# "self-adjusting sparsity prevents residual explosion" (Figures 4-6)
+# --------------------------------------------------------------------------
+
+LS = 1
+
+
+def _with_flags(segs, rng):
+    return [(o, n, lt, int(rng.integers(0, 2))) for (o, n, lt) in segs]
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_ls_bruteforce_tiny(mode):
+    """Catches: a wrong LS rule (not the first maximum, a tie sent twice, a
+    zero bin sent) in tables that mix LS and AdaComp layers."""
+    rng = np.random.default_rng(300 + mode)
+    for _ in range(120):
+        segs, span = random_table(rng)
+        segs = _with_flags(segs, rng)
+        r = tiny_values(rng, span, mode)
+        d = tiny_values(rng, span, mode)
+        r_or, gm_or, msg_or = run_oracle(segs, r, d)
+        r_bf, gm_bf, msg_bf, s_bf = bf.compress(segs, r, d)
+        np.testing.assert_array_equal(bits(gm_or), bits(gm_bf))
+        m_or, m_bf = mp.parse(msg_or, segs), mp.parse(msg_bf, segs)
+        for a, b in zip(m_or.segs, m_bf.segs):
+            assert a.counts.tolist() == b.counts.tolist()
+            assert a.words.tolist() == b.words.tolist()
+            assert bf.ulp_distance(np.float32(a.s), np.float32(b.s)) <= 1
+        if all(np.float32(a.s) == np.float32(b.s) for a, b in zip(m_or.segs, m_bf.segs)):
+            assert bytes(msg_or) == msg_bf
+            np.testing.assert_array_equal(bits(r_or), bits(r_bf))
+
+
+def test_ls_sends_first_maximum_of_each_bin():
+    """Catches: more or fewer than one element per nonzero bin, a later tie
+    chosen over an earlier one, a scale that differs from AdaComp's."""
+    rng = np.random.default_rng(31)
+    segs, span = _medium(rng)
+    r = tiny_values(rng, span, 2) * np.float32(1e-3)
+    d = tiny_values(rng, span, 0) * np.float32(1e-3)
+    segs_ls = [(o, n, lt, LS) for (o, n, lt) in segs]
+    r_ls, gm, msg = run_oracle(segs_ls, r, d)
+    _, gm_ada, msg_ada = run_oracle(segs, r, d)
+    np.testing.assert_array_equal(bits(gm), bits(gm_ada))
+    m, m_ada = mp.parse(msg, segs_ls), mp.parse(msg_ada, segs)
+    G = (r + d).astype(np.float32)
+    for (off, n, lt), sm, sa in zip(segs, m.segs, m_ada.segs):
+        assert sm.s_bits == sa.s_bits
+        g = np.abs(G[off:off + n])
+        nb = (n + lt - 1) // lt
+        want = []
+        for b in range(nb):
+            blk = g[b * lt:(b + 1) * lt]
+            if blk.max() > 0:
+                want.append(b * lt + int(np.argmax(blk == blk.max())))
+        assert sm.counts.tolist() == [1 if g[b * lt:(b + 1) * lt].max() > 0 else 0 for b in range(nb)]
+        assert sm.index.tolist() == want
+        sent = np.zeros(n, bool)
+        sent[want] = True
+        q = np.where(G[off:off + n] > 0, np.float32(sm.s), -np.float32(sm.s)).astype(np.float32)
+        np.testing.assert_array_equal(bits(r_ls[off:off + n][sent]), bits((G[off:off + n] - q)[sent]))
+        np.testing.assert_array_equal(bits(r_ls[off:off + n][~sent]), bits(G[off:off + n][~sent]))
+
+
+def test_ls_equals_adacomp_without_gradient_and_ties():
+    """With dW = 0 AdaComp sends exactly the bin maxima and their ties (H = G);
+    with distinct magnitudes that is one element per bin, LS's choice.
+    Catches: LS and AdaComp diverging where the definitions coincide."""
+    rng = np.random.default_rng(32)
+    segs, span = _medium(rng)
+    r = (rng.permutation(span).astype(np.float32) + 1) * rng.choice([-1, 1], span).astype(np.float32)
+    d = np.zeros(span, np.float32)
+    r_ls, _, msg_ls = run_oracle([(o, n, lt, LS) for (o, n, lt) in segs], r, d)
+    r_ada, _, msg_ada = run_oracle(segs, r, d)
+    np.testing.assert_array_equal(bits(r_ls), bits(r_ada))
+    m_ls = mp.parse(msg_ls, [(o, n, lt, LS) for (o, n, lt) in segs])
+    m_ada = mp.parse(msg_ada, segs)
+    for a, b in zip(m_ls.segs, m_ada.segs):
+        assert a.counts.tolist() == b.counts.tolist() and a.words.tolist() == b.words.tolist()
+
+
+def test_ls_residue_keeps_growing_where_adacomp_saturates():
+    """The page contrasts the two: without the soft threshold, residues grow
+    (in training, through feedback, without bound); AdaComp's soft threshold
+    drains them.  Synthetic, open-loop demonstration at L_T = 500 on a
+    stationary N(0, 1e-3) gradient stream: AdaComp's residue RMS levels off
+    while LS's keeps rising and ends more than twice as large.  Catches: an
+    LS that sends more than the bin maxima, or an AdaComp that does not adapt."""
+    n, lt = 20000, 500
+    rms = {}
+    for flags in (0, LS):
+        segs = [(0, n, lt, flags)]
+        r = np.zeros(n, np.float32)
+        hist = []
+        for t in range(1, 201):
+            d = (np.random.default_rng(1000 + t).standard_normal(n) * 1e-3).astype(np.float32)
+            oracle.compress(segs, r, d)
+            hist.append(float(np.sqrt(np.mean(r.astype(np.float64) ** 2))))
+        rms[flags] = hist
+    ada, ls = rms[0], rms[LS]
+    assert ada[199] < 1.05 * ada[99]
+    assert ls[199] > 1.1 * ls[99]
+    assert ls[199] > 2.0 * ada[199]
