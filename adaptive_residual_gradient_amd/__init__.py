@@ -25,6 +25,7 @@ STAGES = ("tile_pass", "chunk_scan", "finalize", "encode",
           "decode_count", "decode_base", "decode_apply", "compress_call", "decode_call")
 MAX_MESSAGES = 256
 MAX_BIN_LEN = 32768
+SEG_LS = 1   # segment flag: hard local selection (see include/adacomp.h)
 
 
 class HipLibraryMissing(RuntimeError):
@@ -178,8 +179,9 @@ class Timer:
 class Plan:
     """A segment table made into device tile tables on the current device.
 
-    ``segments``: (offset, numel, bin_len) per layer, offsets in elements of
-    the flat float32 buffers (multiples of 4)."""
+    ``segments``: (offset, numel, bin_len) or (offset, numel, bin_len, flags)
+    per layer, offsets in elements of the flat float32 buffers (multiples of
+    4); flags 0 (AdaComp) or SEG_LS."""
 
     def __init__(self, segments):
         self.segments = [tuple(int(x) for x in s) for s in segments]

@@ -270,7 +270,10 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
         bind(p->ddt, od);
         for (int v = 0; v < adacomp::kDecVariants; ++v)
             p->ddesc[v] = reinterpret_cast<adacomp::DecDesc*>(base + o_desc[v]);
-        for (int v = 0; v < adacomp::kVariants; ++v) p->tile_lds_words[v] = 2 * L.ct.max_bpt[v] + 1;
+        // Per tile: bin maxima, bin boundaries, and for hard local selection
+        // the first index of each bin's maximum.
+        for (int v = 0; v < adacomp::kVariants; ++v)
+            p->tile_lds_words[v] = (L.has_ls ? 3 : 2) * L.ct.max_bpt[v] + 1;
         *out = p;
         return ADACOMP_OK;
     } catch (...) {

@@ -173,8 +173,13 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
     const uint32_t lt = sg.lt, magic = sg.magic;
     uint32_t* smax = lds;                 // [bpt] bin maxima as float bits
     uint32_t* sbound = lds + sg.ct.bpt;      // [bpt + 1] survivors before each bin
+    uint32_t* sfirst = sbound + sg.ct.bpt + 1;   // [bpt] LS only: first index of the maximum
+    const bool ls = (sg.flags & ADACOMP_SEG_LS) != 0u;
 
-    for (uint32_t b = tid; b < tg.nb; b += THREADS) smax[b] = 0u;
+    for (uint32_t b = tid; b < tg.nb; b += THREADS) {
+        smax[b] = 0u;
+        if (ls) sfirst[b] = kSentinel;
+    }
 
     float g[VPT][4];
 #pragma unroll
@@ -231,7 +236,27 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
     }
     __syncthreads();
 
-    // ---- selection: |H| >= g_max of the bin and G != 0 ----
+    if (ls) {
+        // Hard local selection: the lowest index whose |G| is the (nonzero)
+        // bin maximum.
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const int vi = v * THREADS + tid;
+            const int x0 = vi * 4 - int(tg.lead);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int x = x0 + c;
+                if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen)) {
+                    const uint32_t b = div_bin(uint32_t(x), lt, magic);
+                    const uint32_t m = __float_as_uint(fabsf(g[v][c]));
+                    if (m != 0u && m == smax[b]) atomicMin(&sfirst[b], uint32_t(x));
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- selection: |H| >= g_max of the bin and G != 0 (LS: the first maximum) ----
     uint32_t sel[VPT];
     uint32_t wrank[VPT];
 #pragma unroll
@@ -243,9 +268,11 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
         for (int c = 0; c < 4; ++c) {
             const int x = x0 + c;
             if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen)) {
-                const float gm = __uint_as_float(smax[div_bin(uint32_t(x), lt, magic)]);
+                const uint32_t b = div_bin(uint32_t(x), lt, magic);
+                const float gm = __uint_as_float(smax[b]);
                 const float h = g[v][c] + in.dw[v][c];      // H = G + dW
-                if (fabsf(h) >= gm && g[v][c] != 0.0f) m |= 1u << c;
+                const bool take = ls ? sfirst[b] == uint32_t(x) : fabsf(h) >= gm && g[v][c] != 0.0f;
+                if (take) m |= 1u << c;
             }
         }
         sel[v] = m;

@@ -59,7 +59,7 @@ struct TileSpec {
     uint32_t variant;     // tile shape index
 };
 
-// Per-segment parameters read by every kernel (96 bytes).
+// Per-segment parameters read by every kernel (112 bytes).
 struct SegDev {
     uint64_t off;        // element offset in the flat buffers
     uint64_t numel;
@@ -71,8 +71,10 @@ struct SegDev {
     uint32_t wb;         // index word bytes: 1 if lt < 64 else 2
     TileSpec ct;         // compress tiles
     TileSpec dt;         // decode tiles
+    uint32_t flags;      // 0 or ADACOMP_SEG_LS
+    uint32_t pad[3];
 };
-static_assert(sizeof(SegDev) == 96, "SegDev layout");
+static_assert(sizeof(SegDev) == 112, "SegDev layout");
 
 // Exact x / lt for 0 <= x < 2^16 and 2 <= lt <= 2^16 with magic =
 // floor(2^32 / lt) + 1: the product overshoots x / lt by x * e / 2^32 with
@@ -168,6 +170,7 @@ struct Layout {
     Tiling ct;                               // compress tiles
     Tiling dt;                               // decode tiles
     uint64_t total_numel = 0, total_bins = 0;
+    bool has_ls = false;   // some segment uses hard local selection
     uint64_t span = 0;   // max(offset + numel) rounded up to 4: the flat buffers' minimum length
     uint64_t counts_begin = 0, entries_begin = 0, capacity = 0;
 
@@ -219,7 +222,7 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
     if (segs == nullptr || nseg == 0) return ADACOMP_ERR_INVALID_ARGUMENT;
     for (uint32_t i = 0; i < nseg; ++i) {
         const adacomp_segment& s = segs[i];
-        if (s.numel == 0 || s.flags != 0) return ADACOMP_ERR_INVALID_ARGUMENT;
+        if (s.numel == 0 || (s.flags != 0 && s.flags != ADACOMP_SEG_LS)) return ADACOMP_ERR_INVALID_ARGUMENT;
         if (s.bin_len == 0 || s.bin_len > ADACOMP_MAX_BIN_LEN) return ADACOMP_ERR_UNSUPPORTED_BIN;
         if (s.offset % 4 != 0) return ADACOMP_ERR_MISALIGNED;
         if (s.numel >= (uint64_t(1) << 32)) return ADACOMP_ERR_TOO_LARGE;
@@ -284,6 +287,8 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
         const uint64_t nb = (s.numel + s.bin_len - 1) / s.bin_len;
         d.nbins = static_cast<uint32_t>(nb);
         d.wb = s.bin_len < 64 ? 1u : 2u;
+        d.flags = s.flags;
+        L.has_ls |= s.flags == ADACOMP_SEG_LS;
         d.bin_base = bins;
         d.count_off = count_at;
         uint32_t cv = kVariants - 1;

@@ -60,7 +60,7 @@ extern "C" {
 
 /* Status codes. */
 #define ADACOMP_OK 0
-#define ADACOMP_ERR_INVALID_ARGUMENT (-1) /* null pointer, empty table, numel 0, flags != 0, wrong device, aliasing */
+#define ADACOMP_ERR_INVALID_ARGUMENT (-1) /* null pointer, empty table, numel 0, unknown flags, wrong device, aliasing */
 #define ADACOMP_ERR_UNSUPPORTED_BIN (-2)  /* L_T = 0 or L_T > 32768 (a 16-bit word holds a 15-bit index) */
 #define ADACOMP_ERR_MISALIGNED (-3)       /* segment offset not a multiple of 4, or a buffer not 16-byte aligned */
 #define ADACOMP_ERR_OVERLAP (-4)          /* two segments share an element */
@@ -69,11 +69,20 @@ extern "C" {
 #define ADACOMP_ERR_TOO_LARGE (-7)        /* numel >= 2^32 in one segment, or the table exceeds launch limits */
 
 #define ADACOMP_MAX_BIN_LEN 32768u
+
+/* Segment flag: hard Local Selection (LS) instead of AdaComp's soft threshold.
+ * The baseline the same page's Mechanism claim "self-adjusting sparsity
+ * prevents residual explosion" (Figures 4-6) contrasts AdaComp with: per bin
+ * only the first element (lowest index) whose |G| equals the bin maximum is
+ * transmitted, none when the maximum is 0; s, the residue update and the
+ * message format are those of AdaComp. */
+#define ADACOMP_SEG_LS 1u
 #define ADACOMP_MAX_MESSAGES 256u         /* most messages one decode_accumulate call sums */
 
 /* One layer: numel consecutive elements of the flat buffers starting at
  * element `offset` (a multiple of 4), compressed with bins of bin_len = L_T
- * elements over its flattened storage order.  flags must be 0. */
+ * elements over its flattened storage order.  flags: 0 (AdaComp) or
+ * ADACOMP_SEG_LS. */
 typedef struct adacomp_segment {
     uint64_t offset;
     uint64_t numel;

@@ -59,7 +59,8 @@ def test_status_strings():
     ([(0, 100, 50), (96, 10, 50)], -4),
     ([(100, 10, 50), (0, 101, 50)], -4),
     ([(0, 1 << 32, 500)], -7),
-    ([(0, 100, 50, 1)], -1),
+    ([(0, 100, 50, 2)], -1),
+    ([(0, 100, 50, 3)], -1),
 ])
 def test_plan_query_rejects(segs, status):
     with pytest.raises(A.AdaCompError) as e:
@@ -77,6 +78,16 @@ def test_plan_info_matches_format(name):
     assert info.header_bytes == 32 + 16 * len(wl.segments)
     assert info.plan_hash == mp.table_hash(wl.segments) == oracle.plan_hash(wl.segments)
     assert info.message_capacity == oracle.message_capacity(wl.segments)
+
+
+def test_ls_flag_enters_plan_hash():
+    """The hard-local-selection flag is part of the segment table, so it enters
+    the header hash; capacity is unchanged."""
+    segs = [(0, 1000, 50, A.SEG_LS), (1000, 500, 500)]
+    info = A.plan_query(segs)
+    assert info.plan_hash == mp.table_hash(segs) == oracle.plan_hash(segs)
+    assert info.plan_hash != A.plan_query([(0, 1000, 50), (1000, 500, 500)]).plan_hash
+    assert info.message_capacity == oracle.message_capacity(segs)
 
 
 def test_null_plan_calls_fail_cleanly():

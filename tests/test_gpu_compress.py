@@ -169,6 +169,69 @@ def test_survivor_distribution_extremes():
     plan.close()
 
 
+@pytest.mark.parametrize("values", ["normal", "ties"])
+def test_local_selection_parity(values):
+    """Hard local selection (segment flag 1) next to AdaComp layers, over every
+    tile shape (bins of 1 to 32768 elements, the 1024-thread tiles included),
+    ragged last bins and ties of the bin maximum; three steps each, then the
+    LS messages summed by decode_accumulate."""
+    lts = [1, 3, 50, 500, 4093, 5000, 32768]
+    segs, off = [], 0
+    for i, lt in enumerate(lts):
+        n = lt * 5 + 3 if lt > 1000 else 40003
+        segs.append((off, n, lt, A.SEG_LS if i % 2 == 0 else 0))
+        segs.append((off + (n + 3) // 4 * 4, 4097, lt, A.SEG_LS if i % 2 == 1 else 0))
+        off += (n + 3) // 4 * 4 + 4100
+    span = off
+    plan = A.Plan(segs)
+    msg, ws = plan.message_buffer(DEV), plan.compress_workspace(DEV)
+    gmax = torch.empty(int(plan.info.total_bins), dtype=torch.float32, device=DEV)
+    rng = np.random.default_rng(17)
+    r = np.zeros(span, np.float32)
+    host_msgs, dev_msgs = [], []
+    for step in range(3):
+        d = _values(rng, span, values)
+        say(f"  LS table, {values}, step {step}")
+        m, r_out, g = run_gpu_step(plan, torch.from_numpy(r.copy()).to(DEV),
+                                   torch.from_numpy(d).to(DEV), msg, ws, gmax)
+        rep = compare_step(segs, r, d, r_out, m, g)
+        pm = mp.parse(m, segs)
+        for (o, n, lt, fl), sm in zip(segs, pm.segs):
+            if fl == A.SEG_LS:
+                assert int(sm.counts.max()) <= 1
+        host_msgs.append(m.copy())
+        dev_msgs.append(torch.from_numpy(m.copy()).to(DEV))
+        r = r_out
+    say(f"    survivors {rep.survivors}")
+    out = torch.zeros(span, dtype=torch.float32, device=DEV)
+    A.decode_accumulate(plan, dev_msgs, out, False, plan.decode_workspace(3, DEV))
+    want = np.zeros(span, np.float32)
+    oracle.decode_accumulate(segs, host_msgs, want, False)
+    np.testing.assert_array_equal(bits(out.cpu().numpy()), bits(want))
+    plan.close()
+
+
+def test_local_selection_conv_workload():
+    """The conv workload (L_T = 50) with every layer under hard local
+    selection, 20 steps with the residue carried over."""
+    wl = W.workload("conv")
+    segs = [(o, n, lt, A.SEG_LS) for (o, n, lt) in wl.segments]
+    plan = A.Plan(segs)
+    n = W.alloc_len(wl)
+    r_dev = torch.zeros(n, dtype=torch.float32, device=DEV)
+    d_dev = torch.empty(n, dtype=torch.float32, device=DEV)
+    msg, ws = plan.message_buffer(DEV), plan.compress_workspace(DEV)
+    gmax = torch.empty(int(plan.info.total_bins), dtype=torch.float32, device=DEV)
+    for step in range(1, 21):
+        W.fill_dw(d_dev, wl, 0, step)
+        r_in, d = r_dev.cpu().numpy(), d_dev.cpu().numpy()
+        m, r_out, g = run_gpu_step(plan, r_dev, d_dev, msg, ws, gmax)
+        rep = compare_step(segs, r_in, d, r_out, m, g)
+    say(f"  conv under LS: survivors at step 20 {rep.survivors} (bins {wl.bins})")
+    assert rep.survivors <= wl.bins
+    plan.close()
+
+
 def test_determinism_and_resume():
     """Two runs give the same bits; 5 steps + residue checkpoint + 5 steps equal
     10 straight steps."""
