@@ -43,10 +43,16 @@ hipError_t launch_tile_pass(const adacomp_plan* plan, hipStream_t stream, float*
                             const float* dW, uint8_t* msg, uint2* stage, uint32_t* tile_cnt,
                             double* tile_gsum, float* bin_max_out) {
     const uint32_t n = static_cast<uint32_t>(plan->L.ct.by_variant[V].size());
-    hipLaunchKernelGGL((k_tile_pass<kVarThreads[V], kVarVecs[V]>), dim3(n), dim3(kVarThreads[V]),
-                       plan->tile_lds_words[V] * 4, stream, plan->d_segs, plan->dct.tile_seg,
-                       plan->dct.vtiles[V], residue, dW, msg, stage, tile_cnt, tile_gsum,
-                       bin_max_out);
+    if (V == 2)   // long bins: one bin per workgroup, streamed in chunks
+        hipLaunchKernelGGL((k_tile_pass_long<kVarThreads[V], kVarVecs[V]>), dim3(n),
+                           dim3(kVarThreads[V]), 0, stream, plan->d_segs, plan->dct.tile_seg,
+                           plan->dct.vtiles[V], residue, dW, msg, stage, tile_cnt, tile_gsum,
+                           bin_max_out);
+    else
+        hipLaunchKernelGGL((k_tile_pass<kVarThreads[V], kVarVecs[V]>), dim3(n), dim3(kVarThreads[V]),
+                           plan->tile_lds_words[V] * 4, stream, plan->d_segs, plan->dct.tile_seg,
+                           plan->dct.vtiles[V], residue, dW, msg, stage, tile_cnt, tile_gsum,
+                           bin_max_out);
     return hipGetLastError();
 }
 }  // namespace adacomp

@@ -373,6 +373,158 @@ k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_s
                                bin_max_out, ch_tot);
 }
 
+// Long bins (L_T > 4093): one workgroup per bin.  The bin is streamed twice
+// in chunks of THREADS x VPT float4: the first pass finds g_max (and, for
+// hard local selection, the first index holding it), the second forms G and
+// H again, selects, compacts and writes the residue.  The second pass reads
+// what the first one just brought on chip (non-temporal: it is the last use),
+// so HBM traffic stays near 12 B/element while bins fit the caches (L_T =
+// 5000: 40 KiB of residue and dW per workgroup) and only 2 float4 per array
+// live in registers.
+template <int THREADS, int VPT>
+__global__ void __launch_bounds__(THREADS)
+k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
+                 const uint32_t* __restrict__ vtiles, float* __restrict__ residue,
+                 const float* __restrict__ dW, uint8_t* __restrict__ msg, uint2* __restrict__ stage,
+                 uint32_t* __restrict__ tile_cnt, double* __restrict__ tile_gsum,
+                 float* __restrict__ bin_max_out) {
+    constexpr int NW = THREADS / 64;
+    constexpr int NCH = NW * VPT;
+    constexpr uint32_t CV = THREADS * VPT;   // float4 per chunk
+    __shared__ uint32_t red_m[NW], red_i[NW];
+    __shared__ uint32_t ch_tot[NCH];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint32_t tile = vtiles[blockIdx.x];
+    const SegDev sg = segs[tile_seg[tile]];
+    const TileGeom tg = tile_geom(sg, sg.ct, tile);   // exactly one bin
+    const bool ls = (sg.flags & ADACOMP_SEG_LS) != 0u;
+    const int lead = int(tg.lead), tlen = int(tg.tlen);
+
+    // ---- pass 1: g_max = max |G| over the bin, and its first index ----
+    uint32_t m = 0u, mi = kSentinel;
+    for (uint32_t c0 = 0; c0 < tg.nvec; c0 += CV) {
+        f32x4 a[VPT], b[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const uint32_t vi = min(c0 + uint32_t(v * THREADS + tid), tg.nvec - 1u);
+            a[v] = load4<false>(residue + tg.v0 + uint64_t(vi) * 4u);
+            b[v] = load4<false>(dW + tg.v0 + uint64_t(vi) * 4u);
+        }
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const uint32_t vi = c0 + uint32_t(v * THREADS + tid);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int x = int(vi * 4) + c - lead;
+                if (vi < tg.nvec && x >= 0 && x < tlen) {
+                    const uint32_t mm = __float_as_uint(fabsf(a[v][c] + b[v][c]));
+                    if (mm > m) { m = mm; mi = uint32_t(x); }   // x grows, so the first index is kept
+                }
+            }
+        }
+    }
+    // largest |G|, ties to the lowest index
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const uint32_t om = __shfl_xor(m, d), oi = __shfl_xor(mi, d);
+        if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
+    }
+    if (lane == 0) { red_m[wv] = m; red_i[wv] = mi; }
+    __syncthreads();
+    m = red_m[0];
+    mi = red_i[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w)
+        if (red_m[w] > m || (red_m[w] == m && red_i[w] < mi)) { m = red_m[w]; mi = red_i[w]; }
+    const float gm = __uint_as_float(m);
+    const uint32_t first = m != 0u ? mi : kSentinel;   // LS: nothing in an all-zero bin
+
+    // ---- pass 2: selection, compaction to staging, residue <- G ----
+#ifndef ADACOMP_LONG_NT2
+#define ADACOMP_LONG_NT2 1
+#endif
+    uint32_t carry = 0;
+    uint2* st = stage + tg.t0;
+    for (uint32_t c0 = 0; c0 < tg.nvec; c0 += CV) {
+        f32x4 a[VPT], b[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const uint32_t vi = min(c0 + uint32_t(v * THREADS + tid), tg.nvec - 1u);
+            a[v] = load4<ADACOMP_LONG_NT2>(residue + tg.v0 + uint64_t(vi) * 4u);
+            b[v] = load4<ADACOMP_LONG_NT2>(dW + tg.v0 + uint64_t(vi) * 4u);
+        }
+        uint32_t sel[VPT], wrank[VPT];
+        float g[VPT][4];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const uint32_t vi = c0 + uint32_t(v * THREADS + tid);
+            uint32_t msk = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                g[v][c] = a[v][c] + b[v][c];                 // G = residue + dW
+                const int x = int(vi * 4) + c - lead;
+                if (vi < tg.nvec && x >= 0 && x < tlen) {
+                    const float h = g[v][c] + b[v][c];      // H = G + dW
+                    const bool take = ls ? uint32_t(x) == first : fabsf(h) >= gm && g[v][c] != 0.0f;
+                    if (take) msk |= 1u << c;
+                }
+            }
+            sel[v] = msk;
+            const uint64_t b0 = __ballot(msk & 1u), b1 = __ballot(msk & 2u);
+            const uint64_t b2 = __ballot(msk & 4u), b3 = __ballot(msk & 8u);
+            wrank[v] = mbcnt64(b0) + mbcnt64(b1) + mbcnt64(b2) + mbcnt64(b3);
+            if (lane == 0) ch_tot[v * NW + wv] = __popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3);
+        }
+        __syncthreads();
+        uint32_t total = 0, cbase[VPT];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) cbase[v] = 0;
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            const uint32_t t = ch_tot[q];
+#pragma unroll
+            for (int v = 0; v < VPT; ++v)
+                if (q < v * NW + wv) cbase[v] += t;
+            total += t;
+        }
+        __syncthreads();   // ch_tot is rewritten by the next chunk
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const uint32_t vi = c0 + uint32_t(v * THREADS + tid);
+            if (vi >= tg.nvec) continue;
+            const int x0 = int(vi * 4) - lead;
+            uint32_t r = carry + cbase[v] + wrank[v];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (sel[v] & (1u << c)) {
+                    const uint32_t neg = g[v][c] < 0.0f ? 0x80000000u : 0u;
+                    st[r] = make_uint2(neg | uint32_t(x0 + c), __float_as_uint(g[v][c]));
+                    ++r;
+                }
+            }
+            const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
+            if (x0 >= 0 && x0 + 4 <= tlen) {
+                f32x4 o;
+                o.x = g[v][0]; o.y = g[v][1]; o.z = g[v][2]; o.w = g[v][3];
+                store4<ADACOMP_NT_ST>(residue + e0, o);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int x = x0 + c;
+                    if (x >= 0 && x < tlen) residue[e0 + c] = g[v][c];
+                }
+            }
+        }
+        carry += total;
+    }
+    if (tid == 0) {
+        put_word(msg + sg.count_off + uint64_t(tg.first_bin) * sg.wb, sg.wb, carry);
+        if (bin_max_out) bin_max_out[sg.bin_base + tg.first_bin] = gm;
+        tile_gsum[tile] = double(gm);
+        tile_cnt[tile] = carry;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Block-wide exclusive scan of one value per thread (256 threads).
 // ---------------------------------------------------------------------------

@@ -4,12 +4,11 @@
 // Work decomposition.  Each segment (one layer) is cut into tiles of whole
 // bins, so that every bin maximum, survivor count and compaction is local to
 // one workgroup and no cross-workgroup combination is needed for a bin.
-//   - narrow tiles: 256 threads x 1 float4 per thread per array, at most 1024
-//     elements (two bins of 500, twenty bins of 50), for L_T <= 1021;
+//   - narrow tiles: 256 threads x 2 float4 per thread per array, at most 2048
+//     elements (four bins of 500, forty bins of 50), for L_T <= 2045;
 //   - medium tiles: 256 threads x 4 float4, at most 4096 elements, for
 //     L_T <= 4093;
-//   - large tiles: 1024 threads x 9 float4, at most 36864 elements, for
-//     L_T <= 32768.
+//   - long bins (L_T > 4093): one bin per tile, streamed in chunks.
 // Bins per tile are chosen so that tile starts fall on 16-byte boundaries
 // whenever that fits, which keeps every load and store a whole float4 except
 // at the ends of segments.
@@ -30,9 +29,11 @@
 
 namespace adacomp {
 
-// Tile shapes (threads per workgroup x float4 per thread per array).  A
-// layer uses the first shape whose capacity holds one bin plus the up-to-3
-// leading elements of an unaligned tile start.
+// Tile shapes.  Shapes 0 and 1 hold a tile of whole bins in registers
+// (threads per workgroup x float4 per thread per array); a layer uses the
+// first of them whose capacity holds one bin plus the up-to-3 leading
+// elements of an unaligned tile start.  Longer bins take shape 2: one bin
+// per tile, streamed twice by 256 threads in chunks of 256 x 2 float4.
 #ifndef ADACOMP_NARROW_VECS
 #define ADACOMP_NARROW_VECS 2
 #endif
@@ -40,11 +41,14 @@ namespace adacomp {
 #define ADACOMP_NARROW_THREADS 256
 #endif
 constexpr int kVariants = 3;
-constexpr uint32_t kVarThreads[kVariants] = {ADACOMP_NARROW_THREADS, 256, 1024};
-constexpr uint32_t kVarVecs[kVariants] = {ADACOMP_NARROW_VECS, 4, 9};
-constexpr uint32_t var_cap(int v) { return kVarThreads[v] * kVarVecs[v] * 4; }
-constexpr uint32_t kMaxCap = 1024 * 9 * 4;   // 36864 elements
-static_assert(var_cap(2) == kMaxCap, "largest tile shape");
+constexpr uint32_t kVarThreads[kVariants] = {ADACOMP_NARROW_THREADS, 256, 256};
+#ifndef ADACOMP_LONG_VECS
+#define ADACOMP_LONG_VECS 2
+#endif
+constexpr uint32_t kVarVecs[kVariants] = {ADACOMP_NARROW_VECS, 4, ADACOMP_LONG_VECS};   // shape 2: per chunk
+constexpr uint32_t kLongCap = ADACOMP_MAX_BIN_LEN + 4;   // one bin and an unaligned start
+constexpr uint32_t var_cap(int v) { return v == 2 ? kLongCap : kVarThreads[v] * kVarVecs[v] * 4; }
+constexpr uint32_t kMaxCap = 1024 * 9 * 4;   // 36864 elements: long-bin decode tiles
 constexpr uint32_t kChunkTiles = 1024;  // tiles per scan chunk (4 per thread of a 256-thread block)
 constexpr uint32_t kPrefWords = 8192;   // LDS words for per-message bin prefixes in decode
 constexpr uint64_t kAlign = 256;        // workspace sub-buffer alignment
@@ -247,10 +251,11 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
     uint64_t count_at = L.counts_begin;
     uint64_t bins = 0;
     // Cut layer i into tiles of spec ts (shape v, capacity cap elements).
-    auto cut = [&](Tiling& T, TileSpec& ts, uint32_t i, uint32_t v, uint32_t cap) -> int {
+    auto cut = [&](Tiling& T, TileSpec& ts, uint32_t i, uint32_t v, uint32_t cap,
+                   uint32_t max_bins) -> int {
         const SegDev& d = L.segs[i];
         ts.variant = v;
-        ts.bpt = bins_per_tile(d.lt, cap, d.nbins);
+        ts.bpt = std::min(bins_per_tile(d.lt, cap, d.nbins), max_bins);
         ts.ntiles = (d.nbins + ts.bpt - 1) / ts.bpt;
         if (T.ntiles + ts.ntiles >= (uint64_t(1) << 31)) return ADACOMP_ERR_TOO_LARGE;
         ts.tile_begin = static_cast<uint32_t>(T.ntiles);
@@ -294,10 +299,10 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
         uint32_t cv = kVariants - 1;
         for (int v = kVariants - 1; v >= 0; --v)
             if (s.bin_len + 3 <= var_cap(v)) cv = uint32_t(v);
-        int st = cut(L.ct, d.ct, i, cv, var_cap(int(cv)));
+        int st = cut(L.ct, d.ct, i, cv, var_cap(int(cv)), cv == 2 ? 1u : ~0u);
         if (st != ADACOMP_OK) return st;
         const uint32_t dv = s.bin_len + 3 <= kDecCap ? 0u : 1u;
-        st = cut(L.dt, d.dt, i, dv, dv == 0 ? kDecCap : kMaxCap);
+        st = cut(L.dt, d.dt, i, dv, dv == 0 ? kDecCap : kMaxCap, ~0u);
         if (st != ADACOMP_OK) return st;
         bins += nb;
         count_at = round_up(count_at + nb * d.wb, 16);

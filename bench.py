@@ -86,6 +86,62 @@ def cpu_baseline(wl, dws_host_fn, max_steps: int, seconds: float = 15.0):
     }
 
 
+def lt_sweep(args):
+    """Bin-length sweep (not the default run): the same 64 x 4096 x 4096
+    layers and the same gradient stream compressed with L_T = 50, 500 and 5000
+    (8-bit words at 50, 16-bit otherwise), 10 steps each from a zero residue.
+    One JSON line per L_T: compress time and HBM fraction over steps 6..10,
+    payload and wire compression ratio and the largest |residue| at step 10."""
+    import torch
+    import adaptive_residual_gradient_amd as A
+    import workloads as W
+    from adaptive_residual_gradient_amd import stats
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.workload(args.workload)
+    n_alloc, N = W.alloc_len(wl), wl.numel
+    steps = 10
+    dws = []
+    for s in range(1, steps + 1):
+        t = torch.empty(n_alloc, dtype=torch.float32, device=dev)
+        W.fill_dw(t, wl, 0, s)
+        dws.append(t)
+    for lt in (50, 500, 5000):
+        segs = [(o, n, lt) for (o, n, _) in wl.segments]
+        plan = A.Plan(segs)
+        msg, ws = plan.message_buffer(dev), plan.compress_workspace(dev)
+        residue = torch.zeros(n_alloc, dtype=torch.float32, device=dev)
+        timer = A.Timer()
+        for i in range(steps):
+            if i == 5:
+                torch.cuda.synchronize()
+                timer.reset()
+            A.compress(plan, residue, dws[i], msg, ws, timer=timer if i >= 5 else None)
+        torch.cuda.synchronize()
+        st = timer.read()
+        call = st["compress_call"][0] / st["compress_call"][1]
+        tile = st["tile_pass"][0] / st["tile_pass"][1]
+        total, surv, _ = A.message_header(plan, msg)
+        pr, wr, _, _ = stats.message_ratios(segs, bytes(msg[: int(plan.info.header_bytes)].cpu().numpy()))
+        rmax = float(residue.abs().max().item())
+        print(json.dumps({
+            "sweep": "bin_len", "workload": wl.name, "bin_len": lt,
+            "index_bits": 8 if lt < 64 else 16, "steps": steps,
+            "compress_ms": round(call, 4), "Gelem_per_s": round(N / (call * 1e-3) / 1e9, 2),
+            "compress_frac_of_peak": round(12.0 * N / (call * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "tile_pass_ms": round(tile, 4),
+            "tile_pass_frac_of_peak": round(12.0 * N / (tile * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "survivors_step10": int(surv), "message_bytes_step10": int(total),
+            "payload_ratio": round(pr, 1), "wire_ratio": round(wr, 1),
+            "max_abs_residue_step10": rmax,
+        }), flush=True)
+        timer.close()
+        plan.close()
+        del msg, ws, residue
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +151,9 @@ def main():
     ap.add_argument("--learners", type=int, default=16)
     ap.add_argument("--learner-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lt-sweep", action="store_true",
+                    help="instead of the benchmark, compress the workload with L_T = 50, 500 "
+                         "and 5000 and print one JSON line per bin length")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device copy of 1 GiB (a known-size reference "
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -104,6 +163,9 @@ def main():
         print(json.dumps({"error": "this build measures one GPU: the compressor runs per learner "
                                    "on its own GPU; multi-GPU exchange is not built (run with --gpus 1)"}))
         sys.exit(2)
+    if args.lt_sweep:
+        lt_sweep(args)
+        return
 
     import numpy as np
     import torch

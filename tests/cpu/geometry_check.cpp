@@ -31,6 +31,7 @@ static std::string check_tiling(const Layout& L, const Tiling& T, bool decode, c
         const SegDev& d = L.segs[s];
         const TileSpec& ts = decode ? d.dt : d.ct;
         if (int(ts.variant) >= sh.n) return "FAIL variant";
+        if (!decode && ts.variant == 2 && ts.bpt != 1) return "FAIL long bins share a tile";
         if (ts.bpt == 0 || ts.bpt > T.max_bpt[ts.variant]) return "FAIL bpt";
         for (uint32_t v = 0; v < ts.variant; ++v)
             if (d.lt + 3 <= sh.cap[v]) return "FAIL shape not the smallest";
@@ -83,7 +84,8 @@ static std::string check(const std::vector<adacomp_segment>& segs, int expect_st
     cs.n = kVariants;
     for (int v = 0; v < kVariants; ++v) {
         cs.cap[v] = var_cap(v);
-        cs.lanes_vecs[v] = kVarThreads[v] * kVarVecs[v];
+        // shape 2 streams its one bin in chunks
+        cs.lanes_vecs[v] = v == 2 ? kLongCap / 4 : kVarThreads[v] * kVarVecs[v];
     }
     ds.n = kDecVariants;
     ds.cap[0] = kDecCap;
