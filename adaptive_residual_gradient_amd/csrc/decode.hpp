@@ -1,0 +1,347 @@
+// Decode-accumulate kernels for gfx950.
+//
+// Method: "AdaComp (Adaptive Residual Gradient Compression)", AIMech curated
+// page, definition paragraph and Mechanism claim on local-bin soft threshold
+// and mean-g_max quantization (Algorithm 2); word widths from its Application
+// claim (Table 2).
+#pragma once
+
+#include "common.hpp"
+
+namespace adacomp {
+
+// ---------------------------------------------------------------------------
+// Decode-accumulate, over decode tiles (TileSpec dt of each layer).
+// ---------------------------------------------------------------------------
+struct MsgPtrs {
+    const uint8_t* p[ADACOMP_MAX_MESSAGES];
+};
+
+struct DecodeWs {
+    uint32_t* status;     // [1]
+    uint32_t* dcnt;       // [K*DT]
+    uint32_t* doff;       // [K*DT]
+    uint32_t* dchunk_cnt; // [K*DC]
+    uint32_t* dchunk_base;// [K*DC]
+    float* dseg_s;        // [K*nseg]
+    uint64_t* dseg_eoff;  // [K*nseg]
+    uint32_t* dvalid;     // [K]
+};
+
+__device__ __forceinline__ bool header_matches(const uint8_t* m, uint32_t nseg, uint32_t plan_hash) {
+    return *reinterpret_cast<const uint32_t*>(m) == 0x43414441u &&
+           *reinterpret_cast<const uint16_t*>(m + 4) == 1 &&
+           *reinterpret_cast<const uint32_t*>(m + 8) == nseg &&
+           *reinterpret_cast<const uint32_t*>(m + 12) == plan_hash;
+}
+
+// Sum of the count words in message bytes [a0, a1), read as the aligned
+// 32-bit words that cover them (count regions start 16-byte aligned and are
+// zero-padded to 16 bytes, so those words lie inside the message).
+__device__ __forceinline__ uint32_t sum_count_words(const uint8_t* m, uint64_t a0, uint64_t a1,
+                                                    uint32_t wb) {
+    typedef const __attribute__((address_space(1))) uint32_t* gu32;
+    uint32_t s = 0;
+#pragma unroll 4
+    for (uint64_t d = a0 & ~uint64_t(3); d < a1; d += 4) {
+        uint32_t v = *(gu32)(m + d);
+        if (d < a0) v &= ~0u << (8u * uint32_t(a0 - d));          // bytes before a0
+        if (d + 4 > a1) v &= ~0u >> (8u * uint32_t(d + 4 - a1));  // bytes from a1 on
+        s += wb == 1u ? (v & 0xFFu) + ((v >> 8) & 0xFFu) + ((v >> 16) & 0xFFu) + (v >> 24)
+                      : (v & 0xFFFFu) + (v >> 16);
+    }
+    return s;
+}
+
+// Per (chunk of decode tiles, message): survivors of each decode tile from
+// the count words, offsets within the chunk, chunk totals.
+__global__ void __launch_bounds__(256)
+k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
+               const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ chunk_seg,
+               uint32_t DT, uint32_t DC, uint32_t nseg, uint32_t plan_hash, DecodeWs ws) {
+    __shared__ uint32_t lw[4];
+    const uint32_t c = blockIdx.x, k = blockIdx.y;
+    const uint8_t* m = msgs.p[k];
+    // A message made for another table is never read past its header.
+    const bool ok = header_matches(m, nseg, plan_hash);
+    const SegDev sg = segs[chunk_seg[c]];
+    const uint32_t tb = chunk_tile_begin[c], n = chunk_tile_begin[c + 1] - tb;
+    uint32_t cnt[4];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = threadIdx.x * 4u + i;
+        uint32_t s = 0;
+        if (ok && t < n) {
+            const uint32_t first_bin = (tb + t - sg.dt.tile_begin) * sg.dt.bpt;
+            const uint32_t nb = min(sg.dt.bpt, sg.nbins - first_bin);
+            const uint64_t a0 = sg.count_off + uint64_t(first_bin) * sg.wb;
+            s = sum_count_words(m, a0, a0 + uint64_t(nb) * sg.wb, sg.wb);
+        }
+        cnt[i] = s;
+        mine += s;
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan<256>(mine, lw, &total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = threadIdx.x * 4u + i;
+        if (t < n) {
+            ws.dcnt[uint64_t(k) * DT + tb + t] = cnt[i];
+            ws.doff[uint64_t(k) * DT + tb + t] = run;
+        }
+        run += cnt[i];
+    }
+    if (threadIdx.x == 0) ws.dchunk_cnt[uint64_t(k) * DC + c] = total;
+}
+
+// One block: message validity, per-segment s and entry offsets, chunk bases.
+__global__ void __launch_bounds__(256)
+k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, uint32_t nseg,
+              uint32_t plan_hash, uint32_t DC, DecodeWs ws) {
+    __shared__ uint32_t valid[ADACOMP_MAX_MESSAGES];
+    __shared__ uint32_t bad;
+    if (threadIdx.x == 0) bad = 0;
+    __syncthreads();
+    for (uint32_t k = threadIdx.x; k < K; k += 256) {
+        const bool ok = header_matches(msgs.p[k], nseg, plan_hash);
+        valid[k] = ok ? 1u : 0u;
+        ws.dvalid[k] = ok ? 1u : 0u;
+        if (!ok) atomicAdd(&bad, 1u);
+    }
+    __syncthreads();
+    for (uint64_t i = threadIdx.x; i < uint64_t(K) * nseg; i += 256) {
+        const uint32_t k = uint32_t(i / nseg), l = uint32_t(i % nseg);
+        float s = 0.0f;
+        uint64_t eoff = 0;
+        if (valid[k]) {
+            const uint8_t* d = msgs.p[k] + 32 + 16 * uint64_t(l);
+            s = *reinterpret_cast<const float*>(d);
+            eoff = *reinterpret_cast<const uint64_t*>(d + 8);
+        }
+        ws.dseg_s[i] = s;
+        ws.dseg_eoff[i] = eoff;
+        const SegDev sg = segs[l];
+        uint32_t run = 0;
+        for (uint32_t c = 0; c < sg.dt.nchunks; ++c) {
+            const uint64_t ci = uint64_t(k) * DC + sg.dt.chunk_begin + c;
+            ws.dchunk_base[ci] = run;
+            run += ws.dchunk_cnt[ci];
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) *ws.status = bad;
+}
+
+// Index word at byte address a (w = 8 or 16 bits), read as the aligned
+// 16-bit word that contains it; messages are 16-byte aligned and padded to a
+// multiple of 16 bytes, so the read stays inside the message.
+// The address is formed from integers kept in LDS, so it is cast to a
+// global-address-space pointer (a global load, not a flat one).
+typedef const __attribute__((address_space(1))) uint16_t* global_u16_ptr;
+
+#ifndef ADACOMP_DEC_BATCH
+#define ADACOMP_DEC_BATCH 2
+#endif
+constexpr int kDecBatch = ADACOMP_DEC_BATCH;   // entry rounds whose loads are issued together
+
+__device__ __forceinline__ uint32_t word_at(uint64_t a, uint32_t wb) {
+    const uint32_t w16 = *(global_u16_ptr)(a & ~uint64_t(1));
+    return wb == 1u ? (w16 >> (8u * uint32_t(a & 1u))) & 0xFFu : w16;
+}
+
+// Per decode tile: out[j] = (accumulate ? out[j] : +0) + q_0[j] + q_1[j] + ...
+// in message order, only at transmitted j.  LDS_ACC keeps the tile in LDS;
+// otherwise (bins longer than 4093) the tile is accumulated in place in out.
+// Messages are taken in groups of KG (KG <= 64; their bin prefixes fill the
+// LDS words given at launch).  The tile's bins are split between the
+// wavefronts; each wavefront gathers the entries of its bins for the whole
+// group (message-major) 64 at a time and adds them message by message.  One
+// wavefront's LDS operations execute in program order, so the additions to
+// an element happen in message order without block barriers.
+// Dynamic LDS: [acc_words floats if LDS_ACC][KG u64 entry addresses][K
+// floats s][NW*(KG+1) u32 per-wavefront flat prefixes][KG*pstride u32 bin
+// prefixes].  Everything else about the tile comes from its descriptor.
+
+template <int THREADS, bool LDS_ACC>
+__global__ void __launch_bounds__(THREADS)
+k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
+               const DecDesc* __restrict__ descs, uint32_t DT, uint32_t DC, uint32_t nseg,
+               DecodeWs ws, float* __restrict__ out, int accumulate, uint32_t acc_words) {
+    constexpr int NW = THREADS / 64;
+    extern __shared__ uint64_t dyn64[];
+    uint32_t* dyn = reinterpret_cast<uint32_t*>(dyn64);
+    const uint32_t accw = LDS_ACC ? (acc_words + 1u) & ~1u : 0u;   // keep 8-byte alignment
+    uint64_t* eaddr = reinterpret_cast<uint64_t*>(dyn + accw);
+    float* ks = reinterpret_cast<float*>(eaddr + KG);
+    uint32_t* wfk_all = reinterpret_cast<uint32_t*>(ks + K);   // [NW][KG + 1]
+    uint32_t* pref = wfk_all + NW * (KG + 1);             // [KG][pstride]
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const DecDesc dd = descs[blockIdx.x];
+    const uint64_t v0 = dd.t0 & ~uint64_t(3);
+    const uint32_t lead = uint32_t(dd.t0 - v0);
+    const uint32_t nvec = (lead + dd.tlen + 3u) >> 2;
+    const uint32_t nb = dd.nb, tlen = dd.tlen;
+    float* acc = LDS_ACC ? reinterpret_cast<float*>(dyn) : out + v0;
+    const uint32_t wb = dd.wb, lt = dd.lt;
+    const uint32_t topbit = wb == 1u ? 7u : 15u;
+    const uint32_t wb0 = nb * uint32_t(wv) / NW, wb1 = nb * uint32_t(wv + 1) / NW;
+    uint32_t* wfk = wfk_all + wv * (KG + 1);
+
+    for (uint32_t k = tid; k < K; k += THREADS) ks[k] = ws.dseg_s[uint64_t(k) * nseg + dd.si];
+    // Initial values: +0, or out.
+    for (uint32_t vi = tid; vi < nvec; vi += THREADS) {
+        const int x0 = int(vi * 4) - int(lead);
+        const uint64_t e0 = v0 + uint64_t(vi) * 4u;
+        if (x0 >= 0 && x0 + 4 <= int(tlen)) {
+            if (LDS_ACC) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                if (accumulate) a = load4<true>(out + e0);
+                *reinterpret_cast<f32x4*>(acc + vi * 4) = a;
+            } else if (!accumulate) {
+                store4<false>(out + e0, f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+        } else {
+            for (int c = 0; c < 4; ++c) {
+                const int x = x0 + c;
+                if (x >= 0 && x < int(tlen)) {
+                    if (LDS_ACC) acc[vi * 4 + c] = accumulate ? out[e0 + c] : 0.0f;
+                    else if (!accumulate) out[e0 + c] = 0.0f;
+                }
+            }
+        }
+    }
+
+    for (uint32_t k0 = 0; k0 < K; k0 += KG) {
+        const uint32_t kn = min(KG, K - k0);
+        __syncthreads();   // bases staged; the previous group is done with pref
+        // Count words of the tile's bins for this group of messages (the
+        // message pointer and validity are read directly, not from LDS, so
+        // these loads wait only for the descriptor).
+        for (uint32_t i = tid; i < kn * nb; i += THREADS) {
+            const uint32_t kk = i / nb, b = i - kk * nb;
+            const uint32_t k = k0 + kk;
+            uint32_t cw = 0;
+            if (ws.dvalid[k])
+                cw = word_at(reinterpret_cast<uint64_t>(msgs.p[k]) + dd.count_at + uint64_t(b) * wb, wb);
+            pref[kk * pstride + b + 1] = cw;
+        }
+        if (tid < int(kn)) {
+            const uint32_t k = k0 + tid;
+            const uint64_t base = uint64_t(ws.dchunk_base[uint64_t(k) * DC + dd.chunk]) +
+                                  ws.doff[uint64_t(k) * DT + dd.tile];
+            eaddr[tid] = reinterpret_cast<uint64_t>(msgs.p[k]) +
+                         ws.dseg_eoff[uint64_t(k) * nseg + dd.si] + base * wb;
+        }
+        __syncthreads();
+        // Per-message exclusive prefix over the tile's bins.
+        if (nb <= 32) {
+            if (tid < int(kn)) {   // one thread per message
+                uint32_t* pr = pref + tid * pstride;
+                uint32_t run = 0;
+                pr[0] = 0;
+                for (uint32_t b = 0; b < nb; ++b) {
+                    run += pr[b + 1];
+                    pr[b + 1] = run;
+                }
+            }
+        } else {
+            for (uint32_t kk = wv; kk < kn; kk += NW) {   // one wavefront per message
+                uint32_t* pr = pref + kk * pstride;
+                uint32_t carry = 0;
+                for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
+                    const uint32_t b = b0 + lane;
+                    const uint32_t v = b < nb ? pr[b + 1] : 0u;
+                    uint32_t inc = v;
+#pragma unroll
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const uint32_t t = __shfl_up(inc, d);
+                        if (lane >= d) inc += t;
+                    }
+                    if (b < nb) pr[b + 1] = carry + inc;
+                    carry += __shfl(inc, 63);
+                }
+                if (lane == 0) pr[0] = 0;
+            }
+        }
+        __syncthreads();
+        if (wb0 >= wb1) continue;   // no bins for this wavefront
+        // This wavefront's entries, message-major: lane kk holds message kk's
+        // count over the wavefront's bins; wfk is their exclusive prefix.
+        {
+            const uint32_t c = uint32_t(lane) < kn
+                                   ? pref[lane * pstride + wb1] - pref[lane * pstride + wb0]
+                                   : 0u;
+            uint32_t inc = c;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t t = __shfl_up(inc, d);
+                if (lane >= d) inc += t;
+            }
+            if (uint32_t(lane) < kn) wfk[lane + 1] = inc;
+            if (lane == 0) wfk[0] = 0;
+        }
+        const uint32_t Ew = wfk[kn];
+        // kDecBatch rounds of 64 entries: every entry word of the batch is
+        // requested before any is used, then the rounds are applied in order.
+        for (uint32_t i0 = 0; i0 < Ew; i0 += 64u * kDecBatch) {
+            uint32_t kof[kDecBatch], xs[kDecBatch], words[kDecBatch];
+#pragma unroll
+            for (int u = 0; u < kDecBatch; ++u) {
+                const uint32_t ii = min(i0 + 64u * u + uint32_t(lane), Ew - 1u);
+                uint32_t lo = 0, hi = kn;   // wfk[lo] <= ii < wfk[hi]
+                while (hi - lo > 1) {
+                    const uint32_t mid = (lo + hi) >> 1;
+                    if (wfk[mid] <= ii) lo = mid; else hi = mid;
+                }
+                const uint32_t* pr = pref + lo * pstride;
+                const uint32_t e = ii - wfk[lo] + pr[wb0];
+                uint32_t bl = wb0, bh = wb1;   // pr[bl] <= e < pr[bh]
+                while (bh - bl > 1) {
+                    const uint32_t mid = (bl + bh) >> 1;
+                    if (pr[mid] <= e) bl = mid; else bh = mid;
+                }
+                kof[u] = lo;
+                xs[u] = bl * lt;
+                words[u] = word_at(eaddr[lo] + uint64_t(e) * wb, wb);
+            }
+#pragma unroll
+            for (int u = 0; u < kDecBatch; ++u) {
+                const uint32_t r0 = i0 + 64u * u;
+                if (r0 >= Ew) break;   // wavefront-uniform
+                const uint32_t lo = kof[u];
+                const uint32_t word = words[u];
+                const uint32_t idx = word & ((1u << topbit) - 1u);
+                const uint32_t x = xs[u] + idx;
+                const float sk = ks[k0 + lo];
+                const float q = (word >> topbit) ? -sk : sk;
+                const bool apply = r0 + uint32_t(lane) < Ew && idx < lt && x < tlen;
+                // Messages present in this round, applied in order.
+                const uint32_t klo = __builtin_amdgcn_readfirstlane(lo);
+                const uint32_t khi = __shfl(lo, int(min(Ew - r0, 64u) - 1u));
+                for (uint32_t kk = klo; kk <= khi; ++kk) {
+                    if (apply && lo == kk) acc[x + lead] = acc[x + lead] + q;
+                    if (!LDS_ACC) __threadfence_block();
+                }
+            }
+        }
+    }
+    if (LDS_ACC) {
+        __syncthreads();
+        for (uint32_t vi = tid; vi < nvec; vi += THREADS) {
+            const int x0 = int(vi * 4) - int(lead);
+            const uint64_t e0 = v0 + uint64_t(vi) * 4u;
+            if (x0 >= 0 && x0 + 4 <= int(tlen)) {
+                store4<true>(out + e0, *reinterpret_cast<const f32x4*>(acc + vi * 4));
+            } else {
+                for (int c = 0; c < 4; ++c) {
+                    const int x = x0 + c;
+                    if (x >= 0 && x < int(tlen)) out[e0 + c] = acc[vi * 4 + c];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace adacomp

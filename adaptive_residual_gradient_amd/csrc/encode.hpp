@@ -1,0 +1,305 @@
+// Compress, survivor offsets, scale, message header and encode for gfx950.
+//
+// Method: "AdaComp (Adaptive Residual Gradient Compression)", AIMech curated
+// page, definition paragraph and Mechanism claim on local-bin soft threshold
+// and mean-g_max quantization (Algorithm 2); word widths from its Application
+// claim (Table 2).
+#pragma once
+
+#include "common.hpp"
+
+namespace adacomp {
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive scan of one value per thread (256 threads).
+// ---------------------------------------------------------------------------
+template <int THREADS>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds_w,
+                                                         uint32_t* total) {
+    constexpr int NW = THREADS / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    uint32_t inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t t = __shfl_up(inc, d);
+        if (lane >= d) inc += t;
+    }
+    if (lane == 63) lds_w[wv] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t x = lds_w[w];
+        if (w < wv) before += x;
+        all += x;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - v;
+}
+
+// Chunk scan: tiles [chunk_tile_begin[c], chunk_tile_begin[c+1]) <= 1024.
+__global__ void __launch_bounds__(256)
+k_chunk_scan(const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ tile_cnt,
+             const double* __restrict__ tile_gsum, uint32_t* __restrict__ tile_off,
+             uint32_t* __restrict__ chunk_cnt, double* __restrict__ chunk_gsum) {
+    __shared__ uint32_t lw[4];
+    __shared__ double lg[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint32_t c = blockIdx.x;
+    const uint32_t tb = chunk_tile_begin[c], n = chunk_tile_begin[c + 1] - tb;
+    uint32_t cnt[4];
+    uint32_t mine = 0;
+    double gs = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = uint32_t(tid) * 4u + i;
+        cnt[i] = t < n ? tile_cnt[tb + t] : 0u;
+        if (t < n) gs += tile_gsum[tb + t];
+        mine += cnt[i];
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan<256>(mine, lw, &total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = uint32_t(tid) * 4u + i;
+        if (t < n) tile_off[tb + t] = run;
+        run += cnt[i];
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) gs += __shfl_xor(gs, d);
+    if (lane == 0) lg[wv] = gs;
+    __syncthreads();
+    if (tid == 0) {
+        chunk_cnt[c] = total;
+        chunk_gsum[c] = ((lg[0] + lg[1]) + lg[2]) + lg[3];
+    }
+}
+
+// Finalize: one block of 256 threads.
+__global__ void __launch_bounds__(256)
+k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
+           uint64_t entries_begin, const uint32_t* __restrict__ chunk_cnt,
+           const double* __restrict__ chunk_gsum, uint32_t* __restrict__ chunk_base,
+           float* __restrict__ seg_s, uint32_t* __restrict__ seg_nsurv,
+           uint64_t* __restrict__ seg_eoff, uint64_t* __restrict__ seg_sbase,
+           uint8_t* __restrict__ msg) {
+    __shared__ uint64_t lsz[4], lns[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // s and survivor totals per segment; chunk bases within the segment.
+    for (uint32_t l = tid; l < nseg; l += 256) {
+        const SegDev sg = segs[l];
+        double acc = 0.0;
+        uint32_t run = 0;
+        for (uint32_t c = 0; c < sg.ct.nchunks; ++c) {
+            const uint32_t ci = sg.ct.chunk_begin + c;
+            acc += chunk_gsum[ci];
+            chunk_base[ci] = run;
+            run += chunk_cnt[ci];
+        }
+        // s = mean of the bin maxima, rounded once to float32.
+        seg_s[l] = float(acc / double(sg.nbins));
+        seg_nsurv[l] = run;
+        // Zero the padding after the count region.
+        const uint64_t cend = sg.count_off + uint64_t(sg.nbins) * sg.wb;
+        for (uint64_t p = cend; p < rup16(cend); ++p) msg[p] = 0;
+    }
+    __syncthreads();
+    // Entry regions in table order, each 16-byte aligned, and the number of
+    // survivors before each segment.
+    uint64_t carry = 0, surv = 0;
+    for (uint32_t base = 0; base < nseg; base += 256) {
+        const uint32_t l = base + tid;
+        uint64_t sz = 0, ns = 0;
+        if (l < nseg) {
+            ns = seg_nsurv[l];
+            sz = rup16(ns * segs[l].wb);
+        }
+        uint64_t isz = sz, ins = ns;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint64_t t = __shfl_up(isz, d);
+            const uint64_t t2 = __shfl_up(ins, d);
+            if (lane >= d) { isz += t; ins += t2; }
+        }
+        if (lane == 63) { lsz[wv] = isz; lns[wv] = ins; }
+        __syncthreads();
+        uint64_t bsz = 0, bns = 0, asz = 0, ans = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if (w < wv) { bsz += lsz[w]; bns += lns[w]; }
+            asz += lsz[w];
+            ans += lns[w];
+        }
+        __syncthreads();
+        if (l < nseg) {
+            const uint64_t eoff = entries_begin + carry + bsz + isz - sz;
+            seg_eoff[l] = eoff;
+            seg_sbase[l] = surv + bns + ins - ns;
+            uint8_t* d = msg + 32 + 16 * uint64_t(l);
+            *reinterpret_cast<float*>(d) = seg_s[l];
+            *reinterpret_cast<uint32_t*>(d + 4) = uint32_t(ns);
+            *reinterpret_cast<uint64_t*>(d + 8) = eoff;
+            const uint64_t wend = eoff + ns * segs[l].wb;
+            for (uint64_t p = wend; p < eoff + sz; ++p) msg[p] = 0;
+        }
+        carry += asz;
+        surv += ans;
+    }
+    if (tid == 0) {
+        *reinterpret_cast<uint32_t*>(msg) = 0x43414441u;
+        *reinterpret_cast<uint16_t*>(msg + 4) = 1;
+        *reinterpret_cast<uint16_t*>(msg + 6) = 0;
+        *reinterpret_cast<uint32_t*>(msg + 8) = nseg;
+        *reinterpret_cast<uint32_t*>(msg + 12) = plan_hash;
+        *reinterpret_cast<uint64_t*>(msg + 16) = entries_begin + carry;
+        *reinterpret_cast<uint64_t*>(msg + 24) = surv;
+        seg_sbase[nseg] = surv;
+    }
+}
+
+// Encode + residue fix-up, balanced over survivors.  The survivors of the
+// table are numbered in message order (segment, bin, in-bin index);
+// wavefront w of W takes survivors [S*w/W, S*(w+1)/W).  It finds the tile
+// holding its first survivor with three 64-way searches (segment, scan chunk,
+// tile), then walks the tiles from there 64 at a time: lane i holds tile i's
+// metadata, a wavefront scan of the survivor counts flattens their
+// survivors, and the lanes take them 64 at a time, with the staged pairs of
+// kEncBatch rounds loaded before any of them is used.  Only wavefront-level
+// operations are used, so every wavefront ends on its own.
+#ifndef ADACOMP_ENC_BATCH
+#define ADACOMP_ENC_BATCH 8
+#endif
+constexpr int kEncBatch = ADACOMP_ENC_BATCH;
+constexpr uint32_t kEncMaxBlocks = 2048;   // 8192 wavefronts: one per wavefront slot of the chip
+
+// Largest i in [0, n) with key(i) <= x, for key nondecreasing with
+// key(0) = 0 <= x; wavefront-uniform, and *kv = key(i).  Each round probes
+// 64 evenly spaced keys; the last round probes the answer itself.
+template <class Key>
+__device__ __forceinline__ uint32_t wave_last_le(uint32_t n, uint64_t x, Key key, uint64_t* kv) {
+    const uint32_t lane = threadIdx.x & 63u;
+    uint32_t lo = 0, len = n;
+    uint64_t v = 0;
+    while (len > 1) {
+        const uint32_t step = (len + 63u) / 64u;
+        const uint32_t off = lane * step;
+        const uint64_t k = off < len ? key(lo + off) : ~uint64_t(0);
+        const uint64_t m = __ballot(k <= x);     // a prefix of the lanes, lane 0 included
+        const uint32_t j = 63u - uint32_t(__clzll(m));
+        v = (uint64_t(__shfl(uint32_t(k >> 32), int(j))) << 32) | __shfl(uint32_t(k), int(j));
+        lo += j * step;
+        len = min(step, len - j * step);
+    }
+    *kv = v;
+    return lo;
+}
+
+__global__ void __launch_bounds__(256)
+k_encode(const SegDev* __restrict__ segs, uint32_t nseg, const uint32_t* __restrict__ tile_seg,
+         const uint2* __restrict__ stage, const uint32_t* __restrict__ tile_cnt,
+         const uint32_t* __restrict__ tile_off, const uint32_t* __restrict__ chunk_base,
+         const float* __restrict__ seg_s, const uint64_t* __restrict__ seg_eoff,
+         const uint64_t* __restrict__ seg_sbase, uint8_t* __restrict__ msg,
+         float* __restrict__ residue, uint32_t ntiles) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t W = gridDim.x * 4u, w = blockIdx.x * 4u + (threadIdx.x >> 6);
+    const uint64_t S = seg_sbase[nseg];
+    const uint64_t a = S * w / W, b = S * (w + 1) / W;
+    if (a >= b) return;   // wavefront-uniform
+
+    // The tile holding survivor a, and a's rank in it.
+    uint64_t kv;
+    const uint32_t l = wave_last_le(nseg, a, [&](uint32_t i) { return seg_sbase[i]; }, &kv);
+    const SegDev sg = segs[l];
+    const uint64_t ra = a - kv;
+    const uint32_t c = wave_last_le(sg.ct.nchunks, ra, [&](uint32_t i) {
+        return uint64_t(chunk_base[sg.ct.chunk_begin + i]);
+    }, &kv);
+    const uint64_t rc = ra - kv;
+    const uint32_t tb = sg.ct.tile_begin + c * kChunkTiles;
+    const uint32_t nt = min(kChunkTiles, sg.ct.ntiles - c * kChunkTiles);
+    const uint32_t t = wave_last_le(nt, rc, [&](uint32_t i) { return uint64_t(tile_off[tb + i]); }, &kv);
+    uint32_t r0 = uint32_t(rc - kv);
+    uint32_t tile0 = tb + t;
+    uint64_t remaining = b - a;
+
+    while (remaining > 0 && tile0 < ntiles) {   // the tile bound only guards against bad counts
+        const uint32_t tl = tile0 + lane;
+        uint32_t cnt = 0, si = 0;
+        if (tl < ntiles) {
+            cnt = tile_cnt[tl];
+            si = tile_seg[tl];
+        }
+        const uint32_t skip = lane == 0 ? r0 : 0u;   // survivors of the first tile already taken
+        cnt -= skip;
+        uint32_t incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t v = __shfl_up(incl, d);
+            if (lane >= uint32_t(d)) incl += v;
+        }
+        const uint32_t total = __shfl(incl, 63);
+        const uint32_t take = uint32_t(min<uint64_t>(total, remaining));
+        const uint32_t excl = incl - cnt;
+        // This lane's tile: flat index of its first element, message byte of
+        // its first word taken here, s, L_T | word bytes, magic.
+        uint64_t t0 = 0, eat = 0;
+        float s = 0.0f;
+        uint32_t ltwb = 0, mag = 0;
+        if (cnt != 0 && excl < take) {
+            const SegDev q = segs[si];
+            const TileGeom tg = tile_geom(q, q.ct, tl);
+            const uint32_t chunk = q.ct.chunk_begin + (tl - q.ct.tile_begin) / kChunkTiles;
+            const uint64_t rank = uint64_t(chunk_base[chunk]) + tile_off[tl] + skip;
+            t0 = tg.t0;
+            eat = seg_eoff[si] + rank * q.wb;
+            s = seg_s[si];
+            ltwb = (q.lt << 2) | q.wb;
+            mag = q.magic;
+        }
+        for (uint32_t base = 0; base < take; base += 64u * kEncBatch) {   // wavefront-uniform
+            uint32_t own[kEncBatch], k[kEncBatch];
+            uint64_t tt[kEncBatch];
+            uint2 p[kEncBatch];
+            // Owners and staged pairs first; lanes past the end reload the last survivor.
+#pragma unroll
+            for (int u = 0; u < kEncBatch; ++u) {
+                const uint32_t e = min(base + 64u * u + lane, take - 1u);
+                uint32_t L = 0;   // lanes whose survivors all precede e
+#pragma unroll
+                for (uint32_t bit = 32; bit >= 1; bit >>= 1)
+                    if (__shfl(incl, int(L + bit - 1u)) <= e) L += bit;
+                own[u] = L;
+                k[u] = e - __shfl(excl, int(L));
+                tt[u] = (uint64_t(__shfl(uint32_t(t0 >> 32), int(L))) << 32) |
+                        __shfl(uint32_t(t0), int(L));
+                p[u] = stage[tt[u] + (L == 0 ? r0 : 0u) + k[u]];
+            }
+#pragma unroll
+            for (int u = 0; u < kEncBatch; ++u) {
+                const uint32_t L = own[u];
+                const uint64_t ea = (uint64_t(__shfl(uint32_t(eat >> 32), int(L))) << 32) |
+                                    __shfl(uint32_t(eat), int(L));
+                const uint32_t lw = __shfl(ltwb, int(L)), mg = __shfl(mag, int(L));
+                const float sv = __shfl(s, int(L));
+                if (base + 64u * u + lane < take) {
+                    const uint32_t lt = lw >> 2, wb = lw & 3u;
+                    const uint32_t x = p[u].x & 0x7FFFFFFFu;
+                    const uint32_t neg = p[u].x >> 31;
+                    const uint32_t bin = div_bin(x, lt, mg);
+                    const uint32_t topbit = wb == 1u ? 7u : 15u;
+                    put_word(msg + ea + uint64_t(k[u]) * wb, wb, (neg << topbit) | (x - bin * lt));
+                    const float gv = __uint_as_float(p[u].y);
+                    // residue <- G - G_q with G_q = sign(G) * s
+                    residue[tt[u] + x] = neg ? gv + sv : gv - sv;
+                }
+            }
+        }
+        remaining -= take;
+        tile0 += 64u;
+        r0 = 0;
+    }
+}
+
+}  // namespace adacomp

@@ -34,10 +34,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The sources the dense tile pass is built from (its HBM counters stay valid
+# while these are unchanged).
+TILE_PASS_SOURCES = ("layout.hpp", "common.hpp", "tile_pass.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for p in sorted((ROOT / "adaptive_residual_gradient_amd" / "csrc").glob("*")):
-        h.update(p.read_bytes())
+    for name in TILE_PASS_SOURCES:
+        h.update((ROOT / "adaptive_residual_gradient_amd" / "csrc" / name).read_bytes())
     return h.hexdigest()[:16]
 
 
@@ -125,6 +130,28 @@ def lt_sweep(args):
         total, surv, _ = A.message_header(plan, msg)
         pr, wr, _, _ = stats.message_ratios(segs, bytes(msg[: int(plan.info.header_bytes)].cpu().numpy()))
         rmax = float(residue.abs().max().item())
+        # decode of K learners' step-10 messages (learners 1..K, own seeds)
+        K = args.learners
+        msgs = []
+        lr = torch.empty(n_alloc, dtype=torch.float32, device=dev)
+        for k in range(1, K + 1):
+            lr.zero_()
+            for s in range(1, steps + 1):
+                W.fill_dw(dws[0], wl, k, s)
+                A.compress(plan, lr, dws[0], msg, ws)
+            t_k, _, _ = A.message_header(plan, msg)
+            msgs.append(msg[:t_k].clone())
+        W.fill_dw(dws[0], wl, 0, 1)
+        out = torch.empty(n_alloc, dtype=torch.float32, device=dev)
+        dws_dec = plan.decode_workspace(K, dev)
+        timer.reset()
+        for i in range(6):
+            A.decode_accumulate(plan, msgs, out, False, dws_dec, timer=timer if i >= 2 else None)
+        torch.cuda.synchronize()
+        dst = timer.read()
+        dec = dst["decode_call"][0] / dst["decode_call"][1]
+        dec_bytes = float(sum(m.numel() for m in msgs)) + 4.0 * N
+        del msgs, lr, out, dws_dec
         print(json.dumps({
             "sweep": "bin_len", "workload": wl.name, "bin_len": lt,
             "index_bits": 8 if lt < 64 else 16, "steps": steps,
@@ -135,6 +162,8 @@ def lt_sweep(args):
             "survivors_step10": int(surv), "message_bytes_step10": int(total),
             "payload_ratio": round(pr, 1), "wire_ratio": round(wr, 1),
             "max_abs_residue_step10": rmax,
+            "decode_messages": K, "decode_ms": round(dec, 4),
+            "decode_GBps": round(dec_bytes / (dec * 1e-3) / 1e9, 1),
         }), flush=True)
         timer.close()
         plan.close()
