@@ -68,6 +68,11 @@ def _load():
                                                  P(ctypes.c_void_p), ctypes.c_uint32,
                                                  ctypes.c_void_p, ctypes.c_int]
         lib.oracle_decode_accumulate.restype = ctypes.c_int
+        lib.oracle_decode_sgd.argtypes = [P(_Seg), ctypes.c_uint32, P(ctypes.c_void_p),
+                                          ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                          ctypes.c_float]
+        lib.oracle_decode_sgd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -144,3 +149,24 @@ def decode_accumulate(segments, messages, out: np.ndarray, accumulate: bool) -> 
                                           1 if accumulate else 0)
     if st != 0:
         raise OracleError(f"oracle_decode_accumulate failed: {st}")
+
+
+def decode_sgd(segments, messages, w: np.ndarray, m: np.ndarray, lr: float, momentum: float,
+               weight_decay: float = 0.0, scale: float = 1.0) -> None:
+    """Sum the messages and take one SGD-with-momentum step on ``w`` and ``m``
+    (float32, in place): g = scale*sum (+ weight_decay*w), m = momentum*m + g,
+    w = w - lr*m, every operation rounded to float32."""
+    for a in (w, m):
+        if a.dtype != np.float32 or not a.flags.c_contiguous:
+            raise TypeError("w and m must be contiguous float32")
+    arr, n = _segs(segments)
+    span = max(int(s[0]) + int(s[1]) for s in segments)
+    if w.size < span or m.size < span:
+        raise ValueError("w or m shorter than the segment table's span")
+    keep = [np.frombuffer(bytes(x), dtype=np.uint8) if isinstance(x, (bytes, bytearray, memoryview))
+            else np.ascontiguousarray(x, dtype=np.uint8) for x in messages]
+    ptrs = (ctypes.c_void_p * max(1, len(keep)))(*[x.ctypes.data for x in keep])
+    st = _load().oracle_decode_sgd(arr, n, ptrs, len(keep), w.ctypes.data, m.ctypes.data,
+                                   float(lr), float(momentum), float(weight_decay), float(scale))
+    if st != 0:
+        raise OracleError(f"oracle_decode_sgd failed: {st}")

@@ -17,6 +17,8 @@
  *   [Lim]  Claims, Limitation "minibatch size, activity and variable message
  *          length" and "Curated Limitations & Negative Results": the number
  *          of transmitted elements varies, so the message has variable length.
+ *   [Opt]  the arXiv abstract of the same paper: AdaComp is shown with SGD
+ *          with momentum and Adam as the optimizers of the training runs.
  *   [LS]   Claims, Mechanism "self-adjusting sparsity prevents residual
  *          explosion" (Figures 4-6): the hard Local Selection (LS) baseline
  *          that AdaComp is contrasted with, which has no soft threshold and
@@ -41,6 +43,10 @@
  *     once to float.
  *   - the message layout below is this project's own definition; the pages
  *     give only the index word widths.
+ *   - decode + SGD step: the summed messages are the gradient of one step
+ *     of SGD with momentum in its usual form (no dampening, no Nesterov):
+ *     g = scale * sum (+ weight_decay * w when weight_decay != 0),
+ *     m = momentum * m + g, w = w - lr * m, each operation rounded to float.
  *   - LS (segment flag 1): per bin exactly one element is transmitted, the
  *     first (lowest index) whose |G| equals the bin maximum, and none when
  *     the maximum is 0; it is quantized with the same layer-wide s and the
@@ -338,4 +344,37 @@ int oracle_decode_accumulate(const oracle_segment *segs, uint32_t nseg,
         }
     }
     return ORACLE_OK;
+}
+
+/*
+ * Sum K messages (as oracle_decode_accumulate with accumulate = 0) and apply
+ * one step of SGD with momentum to every element of every segment, [Opt]:
+ *   g = scale * sum;  if weight_decay != 0: g = g + weight_decay * w;
+ *   m = momentum * m + g;  w = w - lr * m.
+ * Every operation is one float operation rounded to nearest (no contraction).
+ * Elements outside every segment are left untouched.
+ */
+int oracle_decode_sgd(const oracle_segment *segs, uint32_t nseg, const uint8_t *const *msgs,
+                      uint32_t K, float *w, float *m, float lr, float momentum,
+                      float weight_decay, float scale) {
+    int st = check_segments(segs, nseg);
+    if (st != ORACLE_OK) return st;
+    uint64_t span = 0;
+    for (uint32_t l = 0; l < nseg; ++l)
+        if (segs[l].offset + segs[l].numel > span) span = segs[l].offset + segs[l].numel;
+    float *sum = (float *)malloc((span ? span : 1) * sizeof(float));
+    if (!sum) return ORACLE_BAD_ARG;
+    st = oracle_decode_accumulate(segs, nseg, msgs, K, sum, 0);
+    if (st == ORACLE_OK) {
+        for (uint32_t l = 0; l < nseg; ++l) {
+            for (uint64_t j = segs[l].offset; j < segs[l].offset + segs[l].numel; ++j) {
+                float g = scale * sum[j];
+                if (weight_decay != 0.0f) g = g + weight_decay * w[j];
+                m[j] = momentum * m[j] + g;
+                w[j] = w[j] - lr * m[j];
+            }
+        }
+    }
+    free(sum);
+    return st;
 }

@@ -592,3 +592,100 @@ def test_ls_residue_keeps_growing_where_adacomp_saturates():
     assert ada[199] < 1.05 * ada[99]
     assert ls[199] > 1.1 * ls[99]
     assert ls[199] > 2.0 * ada[199]
+
+
+# --------------------------------------------------------------------------
+# Decode fused with one SGD-with-momentum step (the optimizer the paper's
+# abstract names): g = scale*sum (+ wd*w), m = mu*m + g, w = w - lr*m
+# --------------------------------------------------------------------------
+
+def _sgd_inputs(seed, K=3):
+    rng = np.random.default_rng(seed)
+    segs, span = _medium(rng)
+    msgs = []
+    for k in range(K):
+        r = (rng.standard_normal(span) * 1e-3).astype(np.float32)
+        d = (rng.standard_normal(span) * 1e-3).astype(np.float32)
+        msgs.append(run_oracle(segs, r, d)[2])
+    w = rng.standard_normal(span).astype(np.float32)
+    m = (rng.standard_normal(span) * 1e-2).astype(np.float32)
+    return segs, span, msgs, w, m
+
+
+def test_decode_sgd_matches_torch_sgd_in_float64():
+    """torch.optim.SGD (momentum, weight decay, no dampening) evaluated in
+    float64 on the decoded gradient: the float32 step agrees to a few ulp.
+    Catches: a wrong sign of the step, weight decay applied after momentum,
+    momentum applied to w instead of the buffer, a missing scale."""
+    import torch
+    segs, span, msgs, w, m = _sgd_inputs(41)
+    lr, mu, wd, scale = 0.05, 0.9, 1e-2, 1.0 / 3.0
+    s32 = np.zeros(span, np.float32)
+    oracle.decode_accumulate(segs, msgs, s32, False)
+    w1, m1 = w.copy(), m.copy()
+    oracle.decode_sgd(segs, msgs, w1, m1, lr, mu, wd, scale)
+    p = torch.tensor(w.astype(np.float64), requires_grad=True)
+    p.grad = torch.tensor(s32.astype(np.float64) * np.float64(np.float32(scale)))
+    opt = torch.optim.SGD([p], lr=float(np.float32(lr)), momentum=float(np.float32(mu)),
+                          weight_decay=float(np.float32(wd)))
+    opt.state[p]["momentum_buffer"] = torch.tensor(m.astype(np.float64))
+    opt.step()
+    inside = np.zeros(span, bool)
+    for o, n, _ in segs:
+        inside[o:o + n] = True
+    p_ref, b_ref = p.detach().numpy(), opt.state[p]["momentum_buffer"].numpy()
+    # float32 rounding error bounds from the magnitudes of the terms (a few
+    # roundings of eps32/2 each, cancellation included)
+    eps = np.float64(np.finfo(np.float32).eps)
+    g_mag = np.abs(s32.astype(np.float64) * scale) + np.abs(wd * w.astype(np.float64))
+    m_mag = np.abs(mu * m.astype(np.float64)) + g_mag
+    w_mag = np.abs(w.astype(np.float64)) + lr * m_mag
+    for got, ref, mag in ((m1, b_ref, m_mag), (w1, p_ref, w_mag)):
+        err = np.abs(got[inside].astype(np.float64) - ref[inside])
+        assert np.all(err <= 3 * eps * mag[inside] + 1e-38)
+    # and the formula differs from the neighbouring wrong ones by far more
+    assert np.max(np.abs(w1[inside] - p_ref[inside])) < 1e-3 * np.max(np.abs(p_ref[inside] - w[inside]))
+    np.testing.assert_array_equal(bits(w1[~inside]), bits(w[~inside]))
+    np.testing.assert_array_equal(bits(m1[~inside]), bits(m[~inside]))
+
+
+def test_decode_sgd_dyadic_closed_form():
+    """Every bin holds one element of magnitude 1 (the others smaller) and
+    dW = 0, so s = 1 and exactly those elements are sent with q = +-1.  Three
+    steps of momentum 1/2 and lr 1/4 from m = 0 give m = 1, 3/2, 7/4 and
+    w = w0 - 1/4, - 5/8, - 17/16 per unit of q, exactly."""
+    n, lt = 1000, 50
+    segs = [(0, n, lt)]
+    rng = np.random.default_rng(7)
+    r = (rng.integers(-7, 8, n) / 16.0).astype(np.float32)
+    ones = np.arange(0, n, lt) + rng.integers(0, lt, n // lt)
+    sign = rng.choice([-1.0, 1.0], ones.size).astype(np.float32)
+    r[ones] = sign
+    msg = run_oracle(segs, r, np.zeros(n, np.float32))[2]
+    sm = mp.parse(msg, segs).segs[0]
+    assert sm.s == 1.0 and sorted(sm.index.tolist()) == sorted(ones.tolist())
+    w0 = (rng.integers(-64, 64, n) / 8.0).astype(np.float32)
+    w, m = w0.copy(), np.zeros(n, np.float32)
+    for step in range(3):
+        oracle.decode_sgd(segs, [msg], w, m, 0.25, 0.5)
+    q = np.zeros(n, np.float32)
+    q[ones] = sign
+    np.testing.assert_array_equal(m, (q * np.float32(1.75)).astype(np.float32))
+    np.testing.assert_array_equal(w, (w0 - q * np.float32(17.0 / 16.0)).astype(np.float32))
+
+
+def test_decode_sgd_special_cases():
+    """lr = 0 leaves w bit for bit; momentum 0, no weight decay and scale 1
+    leave m equal to the decoded sum bit for bit (also -0 where nothing was
+    sent: 0*m is +-0 and +-0 + +0 = +0)."""
+    segs, span, msgs, w, m = _sgd_inputs(43)
+    s32 = np.zeros(span, np.float32)
+    oracle.decode_accumulate(segs, msgs, s32, False)
+    w1, m1 = w.copy(), m.copy()
+    oracle.decode_sgd(segs, msgs, w1, m1, 0.0, 0.9, 0.0, 1.0)
+    np.testing.assert_array_equal(bits(w1), bits(w))
+    w2, m2 = w.copy(), m.copy()
+    oracle.decode_sgd(segs, msgs, w2, m2, 0.125, 0.0, 0.0, 1.0)
+    for o, n, _ in segs:
+        np.testing.assert_array_equal(m2[o:o + n], s32[o:o + n])
+        np.testing.assert_array_equal(w2[o:o + n], (w[o:o + n] - np.float32(0.125) * s32[o:o + n]).astype(np.float32))
