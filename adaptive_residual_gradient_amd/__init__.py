@@ -20,9 +20,10 @@ _HERE = pathlib.Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libadacomp.so"
 
 OK = 0
-NUM_STAGES = 9
+NUM_STAGES = 10
 STAGES = ("tile_pass", "chunk_scan", "finalize", "encode",
-          "decode_count", "decode_base", "decode_apply", "compress_call", "decode_call")
+          "decode_count", "decode_base", "decode_apply", "compress_call", "decode_call",
+          "decode_sgd_call")
 MAX_MESSAGES = 256
 MAX_BIN_LEN = 32768
 SEG_LS = 1   # segment flag: hard local selection (see include/adacomp.h)
@@ -59,6 +60,13 @@ class PlanInfo(ctypes.Structure):
         return int(self.decode_workspace_bytes_fixed) + K * int(self.decode_workspace_bytes_per_message)
 
 
+class Sgd(ctypes.Structure):
+    """One step of SGD with momentum: g = scale*sum (+ weight_decay*w),
+    m = momentum*m + g, w = w - lr*m."""
+    _fields_ = [("lr", ctypes.c_float), ("momentum", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("scale", ctypes.c_float)]
+
+
 # Every exported symbol, with its C signature (argtypes, restype).
 _P = ctypes.c_void_p
 _U32, _U64, _INT = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int
@@ -72,6 +80,11 @@ SIGNATURES = {
     "adacomp_compress_timed": ([_P, _P, _P, _U64, _P, _U64, _P, _U64, _P, _P, _P], _INT),
     "adacomp_decode_accumulate_timed": ([_P, ctypes.POINTER(_P), _U32, _P, _U64, _INT, _P, _U64,
                                          _P, _P], _INT),
+    "adacomp_decode_sgd": ([_P, ctypes.POINTER(_P), _U32, _P, _P, _U64, ctypes.POINTER(Sgd), _P, _U64,
+                            _P], _INT),
+    "adacomp_decode_sgd_timed": ([_P, ctypes.POINTER(_P), _U32, _P, _P, _U64, ctypes.POINTER(Sgd), _P,
+                                  _U64, _P, _P], _INT),
+    "adacomp_decode_sgd_workspace_bytes": ([_P, _U32, ctypes.POINTER(_U64)], _INT),
     "adacomp_timer_create": ([ctypes.POINTER(_P)], _INT),
     "adacomp_timer_destroy": ([_P], _INT),
     "adacomp_timer_read": ([_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_U64), _U32], _INT),
@@ -217,6 +230,16 @@ class Plan:
         import torch
         return torch.empty(self.info.decode_workspace_bytes(K), dtype=torch.uint8, device=device)
 
+    def decode_sgd_workspace_bytes(self, K: int) -> int:
+        n = _U64(0)
+        _check("adacomp_decode_sgd_workspace_bytes",
+               lib().adacomp_decode_sgd_workspace_bytes(self.handle, int(K), ctypes.byref(n)))
+        return int(n.value)
+
+    def decode_sgd_workspace(self, K: int, device="cuda"):
+        import torch
+        return torch.empty(self.decode_sgd_workspace_bytes(K), dtype=torch.uint8, device=device)
+
 
 def compress(plan: Plan, residue, dW, msg, ws, bin_max_out=None, stream=None,
              timer: Optional[Timer] = None) -> None:
@@ -241,6 +264,21 @@ def decode_accumulate(plan: Plan, msgs: List, out, accumulate: bool, ws, stream=
         1 if accumulate else 0, _u8_ptr(ws, "ws"), ws.numel(), _stream_handle(stream),
         timer.handle if timer is not None else None)
     _check("adacomp_decode_accumulate", st)
+
+
+def decode_sgd(plan: Plan, msgs: List, weights, momentum, lr: float, momentum_coef: float,
+               ws, weight_decay: float = 0.0, scale: float = 1.0, stream=None,
+               timer: Optional[Timer] = None) -> None:
+    """Sum the messages (in list order) and take one SGD-with-momentum step on
+    weights and momentum (in place), without writing the sum."""
+    ptrs = (_P * max(1, len(msgs)))(*[_u8_ptr(m, "msgs[k]") for m in msgs])
+    n = min(weights.numel(), momentum.numel())
+    p = Sgd(lr, momentum_coef, weight_decay, scale)
+    st = lib().adacomp_decode_sgd_timed(
+        plan.handle, ptrs, len(msgs), _f32_ptr(weights, "weights"), _f32_ptr(momentum, "momentum"),
+        n, ctypes.byref(p), _u8_ptr(ws, "ws"), ws.numel(), _stream_handle(stream),
+        timer.handle if timer is not None else None)
+    _check("adacomp_decode_sgd", st)
 
 
 def message_header(plan: Plan, msg):

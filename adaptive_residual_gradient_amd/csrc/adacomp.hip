@@ -395,27 +395,63 @@ int adacomp_compress(const adacomp_plan* plan, float* residue, const float* dW, 
                                   bin_max_out, stream, nullptr);
 }
 
-int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
-                                    float* out, uint64_t n_elems, int accumulate, void* ws,
-                                    uint64_t ws_bytes, void* stream_, adacomp_timer* timer) {
-    if (plan == nullptr || msgs == nullptr || out == nullptr || ws == nullptr)
-        return ADACOMP_ERR_INVALID_ARGUMENT;
+}  // extern "C"
+
+namespace {
+
+// Workspace of decode + SGD: the decode workspace, then (plans with bins
+// longer than 4093) a dense float32 scratch for those tiles' sums.
+struct SgdLayout {
+    uint64_t decode_bytes, scratch, total;
+};
+SgdLayout sgd_layout(const Layout& L, uint32_t K) {
+    SgdLayout o{};
+    const uint64_t d = std::max<uint64_t>(decode_layout(L, K).total, L.dws_fixed + uint64_t(K) * L.dws_per_msg);
+    o.decode_bytes = d;
+    o.scratch = adacomp::round_up(d, adacomp::kAlign);
+    o.total = o.scratch + (L.dt.by_variant[1].empty() ? 0 : 4 * L.span);
+    return o;
+}
+
+// Shared by decode_accumulate (out != nullptr) and decode + SGD (sgd != nullptr).
+int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, float* out,
+                int accumulate, const adacomp_sgd* sgd, float* weights, float* momentum,
+                uint64_t n_elems, void* ws, uint64_t ws_bytes, void* stream_, adacomp_timer* timer,
+                int call_stage) {
+    if (plan == nullptr || msgs == nullptr || ws == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
     if (K == 0 || K > ADACOMP_MAX_MESSAGES) return ADACOMP_ERR_INVALID_ARGUMENT;
     if (accumulate != 0 && accumulate != 1) return ADACOMP_ERR_INVALID_ARGUMENT;
     const Layout& L = plan->L;
     const DecodeLayout D = decode_layout(L, K);
-    if (!aligned16(out) || !aligned16(ws)) return ADACOMP_ERR_MISALIGNED;
-    if (n_elems < L.span || ws_bytes < D.total ||
-        ws_bytes < L.dws_fixed + uint64_t(K) * L.dws_per_msg)
-        return ADACOMP_ERR_CAPACITY;
-    const Range ro = range_of(out, 4 * L.span), rw = range_of(ws, D.total);
-    if (overlaps(ro, rw)) return ADACOMP_ERR_INVALID_ARGUMENT;
+    const SgdLayout S = sgd_layout(L, K);
+    std::vector<Range> dense;   // the dense buffers written
+    if (sgd == nullptr) {
+        if (out == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+        if (!aligned16(out)) return ADACOMP_ERR_MISALIGNED;
+        dense.push_back(range_of(out, 4 * L.span));
+    } else {
+        if (weights == nullptr || momentum == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+        if (!aligned16(weights) || !aligned16(momentum)) return ADACOMP_ERR_MISALIGNED;
+        dense.push_back(range_of(weights, 4 * L.span));
+        dense.push_back(range_of(momentum, 4 * L.span));
+    }
+    if (!aligned16(ws)) return ADACOMP_ERR_MISALIGNED;
+    const uint64_t need = sgd ? S.total : std::max<uint64_t>(D.total, L.dws_fixed + uint64_t(K) * L.dws_per_msg);
+    if (n_elems < L.span || ws_bytes < need) return ADACOMP_ERR_CAPACITY;
+    const Range rw = range_of(ws, need);
+    for (size_t i = 0; i < dense.size(); ++i) {
+        if (overlaps(dense[i], rw)) return ADACOMP_ERR_INVALID_ARGUMENT;
+        for (size_t j = i + 1; j < dense.size(); ++j)
+            if (overlaps(dense[i], dense[j])) return ADACOMP_ERR_INVALID_ARGUMENT;
+    }
     adacomp::MsgPtrs mp{};
     for (uint32_t k = 0; k < K; ++k) {
         if (msgs[k] == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
         if (!aligned16(msgs[k])) return ADACOMP_ERR_MISALIGNED;
         const Range rm = range_of(msgs[k], 32 + 16 * uint64_t(L.nseg));
-        if (overlaps(rm, ro) || overlaps(rm, rw)) return ADACOMP_ERR_INVALID_ARGUMENT;
+        if (overlaps(rm, rw)) return ADACOMP_ERR_INVALID_ARGUMENT;
+        for (const Range& r : dense)
+            if (overlaps(rm, r)) return ADACOMP_ERR_INVALID_ARGUMENT;
         mp.p[k] = static_cast<const uint8_t*>(msgs[k]);
     }
     int st = check_device(plan);
@@ -433,8 +469,20 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
     dw.dseg_eoff = reinterpret_cast<uint64_t*>(w8 + D.dseg_eoff);
     dw.dvalid = reinterpret_cast<uint32_t*>(w8 + D.dvalid);
     const uint32_t DT = static_cast<uint32_t>(L.dt.ntiles), DC = static_cast<uint32_t>(L.dt.nchunks);
+    adacomp::SgdParams sp{};
+    float* sums = out;   // where long-bin tiles accumulate
+    if (sgd) {
+        sp.lr = sgd->lr;
+        sp.momentum = sgd->momentum;
+        sp.weight_decay = sgd->weight_decay;
+        sp.scale = sgd->scale;
+        sp.w = weights;
+        sp.m = momentum;
+        sums = reinterpret_cast<float*>(w8 + S.scratch);
+        accumulate = 0;
+    }
 
-    CallTimer tm(timer, stream, ADACOMP_STAGE_DECODE_CALL);
+    CallTimer tm(timer, stream, call_stage);
     {
         hipLaunchKernelGGL(adacomp::k_decode_count, dim3(DC, K), dim3(256), 0, stream, mp,
                            plan->d_segs, plan->ddt.chunk_tile_begin, plan->ddt.chunk_seg, DT, DC,
@@ -457,14 +505,22 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
             if (v == 0) {   // the tile fits in LDS
                 const uint32_t acc_words = L.dt.max_span_vecs[0] * 4;
                 const uint32_t lds = adacomp::decode_lds_bytes(acc_words, K, KG, ps, 4);
-                hipLaunchKernelGGL((adacomp::k_decode_apply<256, true>), dim3(n), dim3(256), lds,
-                                   stream, mp, K, KG, ps, plan->ddesc[0], DT, DC, L.nseg, dw, out,
-                                   accumulate, acc_words);
-            } else {        // long bins, accumulated in place in out
+                if (sgd)
+                    hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, true>), dim3(n), dim3(256),
+                                       lds, stream, mp, K, KG, ps, plan->ddesc[0], DT, DC, L.nseg, dw,
+                                       nullptr, 0, acc_words, sp);
+                else
+                    hipLaunchKernelGGL((adacomp::k_decode_apply<256, true>), dim3(n), dim3(256), lds,
+                                       stream, mp, K, KG, ps, plan->ddesc[0], DT, DC, L.nseg, dw, out,
+                                       accumulate, acc_words, sp);
+            } else {        // long bins, accumulated in place (in out, or the scratch)
                 const uint32_t lds = adacomp::decode_lds_bytes(0, K, KG, ps, 16);
                 hipLaunchKernelGGL((adacomp::k_decode_apply<1024, false>), dim3(n), dim3(1024), lds,
-                                   stream, mp, K, KG, ps, plan->ddesc[1], DT, DC, L.nseg, dw, out,
-                                   accumulate, 0u);
+                                   stream, mp, K, KG, ps, plan->ddesc[1], DT, DC, L.nseg, dw, sums,
+                                   accumulate, 0u, sp);
+                if (sgd && launch_status() == ADACOMP_OK)
+                    hipLaunchKernelGGL(adacomp::k_sgd_tiles, dim3(n), dim3(256), 0, stream,
+                                       plan->ddesc[1], sums, sp);
             }
             if ((st = launch_status()) != ADACOMP_OK) return st;
         }
@@ -474,11 +530,45 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
     return ADACOMP_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                                    float* out, uint64_t n_elems, int accumulate, void* ws,
+                                    uint64_t ws_bytes, void* stream, adacomp_timer* timer) {
+    return decode_impl(plan, msgs, K, out, accumulate, nullptr, nullptr, nullptr, n_elems, ws,
+                       ws_bytes, stream, timer, ADACOMP_STAGE_DECODE_CALL);
+}
+
 int adacomp_decode_accumulate(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
                               float* out, uint64_t n_elems, int accumulate, void* ws,
                               uint64_t ws_bytes, void* stream) {
     return adacomp_decode_accumulate_timed(plan, msgs, K, out, n_elems, accumulate, ws, ws_bytes,
                                            stream, nullptr);
+}
+
+int adacomp_decode_sgd_workspace_bytes(const adacomp_plan* plan, uint32_t K, uint64_t* bytes) {
+    if (plan == nullptr || bytes == nullptr || K == 0 || K > ADACOMP_MAX_MESSAGES)
+        return ADACOMP_ERR_INVALID_ARGUMENT;
+    *bytes = sgd_layout(plan->L, K).total;
+    return ADACOMP_OK;
+}
+
+int adacomp_decode_sgd_timed(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                             float* weights, float* momentum, uint64_t n_elems,
+                             const adacomp_sgd* sgd, void* ws, uint64_t ws_bytes, void* stream,
+                             adacomp_timer* timer) {
+    if (sgd == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+    return decode_impl(plan, msgs, K, nullptr, 0, sgd, weights, momentum, n_elems, ws, ws_bytes,
+                       stream, timer, ADACOMP_STAGE_DECODE_SGD_CALL);
+}
+
+int adacomp_decode_sgd(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                       float* weights, float* momentum, uint64_t n_elems, const adacomp_sgd* sgd,
+                       void* ws, uint64_t ws_bytes, void* stream) {
+    return adacomp_decode_sgd_timed(plan, msgs, K, weights, momentum, n_elems, sgd, ws, ws_bytes,
+                                    stream, nullptr);
 }
 
 int adacomp_timer_create(adacomp_timer** timer) {

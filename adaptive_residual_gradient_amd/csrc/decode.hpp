@@ -163,11 +163,33 @@ __device__ __forceinline__ uint32_t word_at(uint64_t a, uint32_t wb) {
 // floats s][NW*(KG+1) u32 per-wavefront flat prefixes][KG*pstride u32 bin
 // prefixes].  Everything else about the tile comes from its descriptor.
 
-template <int THREADS, bool LDS_ACC>
+// One step of SGD with momentum on the summed gradient (no dampening, no
+// Nesterov), every operation rounded to float32:
+//   g = scale * sum (+ weight_decay * w),  m = momentum * m + g,  w = w - lr * m.
+struct SgdParams {
+    float lr, momentum, weight_decay, scale;
+    float* w;
+    float* m;
+};
+
+__device__ __forceinline__ void sgd_step(float sum, float& w, float& m, const SgdParams& p) {
+    float g = p.scale * sum;
+    if (p.weight_decay != 0.0f) g = g + p.weight_decay * w;
+    m = p.momentum * m + g;
+    w = w - p.lr * m;
+}
+
+constexpr uint32_t kSgdSlots = kDecCap / 4 / 256;   // float4 per thread of an LDS tile
+
+// SGD: instead of writing the tile's sums to out, the tile's weights and
+// momentum (loaded when the tile starts, kept in registers) take one step.
+template <int THREADS, bool LDS_ACC, bool SGD = false>
 __global__ void __launch_bounds__(THREADS)
 k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                const DecDesc* __restrict__ descs, uint32_t DT, uint32_t DC, uint32_t nseg,
-               DecodeWs ws, float* __restrict__ out, int accumulate, uint32_t acc_words) {
+               DecodeWs ws, float* __restrict__ out, int accumulate, uint32_t acc_words,
+               SgdParams sp) {
+    static_assert(!SGD || (LDS_ACC && THREADS == 256), "the SGD step is fused into LDS tiles");
     constexpr int NW = THREADS / 64;
     extern __shared__ uint64_t dyn64[];
     uint32_t* dyn = reinterpret_cast<uint32_t*>(dyn64);
@@ -190,6 +212,17 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
     uint32_t* wfk = wfk_all + wv * (KG + 1);
 
     for (uint32_t k = tid; k < K; k += THREADS) ks[k] = ws.dseg_s[uint64_t(k) * nseg + dd.si];
+    f32x4 wv4[SGD ? kSgdSlots : 1], mv4[SGD ? kSgdSlots : 1];
+    if (SGD) {   // weights and momentum of this thread's float4 slots, requested early
+#pragma unroll
+        for (uint32_t j = 0; j < kSgdSlots; ++j) {
+            const uint32_t vi = uint32_t(tid) + THREADS * j;
+            if (vi < nvec) {
+                wv4[j] = load4<true>(sp.w + v0 + uint64_t(vi) * 4u);
+                mv4[j] = load4<true>(sp.m + v0 + uint64_t(vi) * 4u);
+            }
+        }
+    }
     // Initial values: +0, or out.
     for (uint32_t vi = tid; vi < nvec; vi += THREADS) {
         const int x0 = int(vi * 4) - int(lead);
@@ -327,7 +360,7 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
             }
         }
     }
-    if (LDS_ACC) {
+    if (LDS_ACC && !SGD) {
         __syncthreads();
         for (uint32_t vi = tid; vi < nvec; vi += THREADS) {
             const int x0 = int(vi * 4) - int(lead);
@@ -338,6 +371,74 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                 for (int c = 0; c < 4; ++c) {
                     const int x = x0 + c;
                     if (x >= 0 && x < int(tlen)) out[e0 + c] = acc[vi * 4 + c];
+                }
+            }
+        }
+    }
+    if (SGD) {
+        __syncthreads();
+#pragma unroll
+        for (uint32_t j = 0; j < kSgdSlots; ++j) {
+            const uint32_t vi = uint32_t(tid) + THREADS * j;
+            if (vi >= nvec) continue;
+            const int x0 = int(vi * 4) - int(lead);
+            const uint64_t e0 = v0 + uint64_t(vi) * 4u;
+            f32x4 wq = wv4[j], mq = mv4[j];
+            const f32x4 a = *reinterpret_cast<const f32x4*>(acc + vi * 4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float wc = wq[c], mc = mq[c];
+                sgd_step(a[c], wc, mc, sp);
+                wq[c] = wc;
+                mq[c] = mc;
+            }
+            if (x0 >= 0 && x0 + 4 <= int(tlen)) {
+                store4<true>(sp.w + e0, wq);
+                store4<true>(sp.m + e0, mq);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int x = x0 + c;
+                    if (x >= 0 && x < int(tlen)) {
+                        sp.w[e0 + c] = wq[c];
+                        sp.m[e0 + c] = mq[c];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// The SGD step for long-bin decode tiles, whose sums were accumulated in a
+// dense scratch buffer (same flat indexing as the weights).
+__global__ void __launch_bounds__(256)
+k_sgd_tiles(const DecDesc* __restrict__ descs, const float* __restrict__ sums, SgdParams sp) {
+    const DecDesc dd = descs[blockIdx.x];
+    const uint64_t v0 = dd.t0 & ~uint64_t(3);
+    const uint32_t lead = uint32_t(dd.t0 - v0);
+    const uint32_t nvec = (lead + dd.tlen + 3u) >> 2;
+    for (uint32_t vi = threadIdx.x; vi < nvec; vi += 256) {
+        const int x0 = int(vi * 4) - int(lead);
+        const uint64_t e0 = v0 + uint64_t(vi) * 4u;
+        const f32x4 a = load4<true>(sums + e0);
+        f32x4 wq = load4<true>(sp.w + e0), mq = load4<true>(sp.m + e0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float wc = wq[c], mc = mq[c];
+            sgd_step(a[c], wc, mc, sp);
+            wq[c] = wc;
+            mq[c] = mc;
+        }
+        if (x0 >= 0 && x0 + 4 <= int(dd.tlen)) {
+            store4<true>(sp.w + e0, wq);
+            store4<true>(sp.m + e0, mq);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int x = x0 + c;
+                if (x >= 0 && x < int(dd.tlen)) {
+                    sp.w[e0 + c] = wq[c];
+                    sp.m[e0 + c] = mq[c];
                 }
             }
         }

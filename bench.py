@@ -91,6 +91,47 @@ def cpu_baseline(wl, dws_host_fn, max_steps: int, seconds: float = 15.0):
     }
 
 
+def measure_decode_sgd(A, plan, msgs, n_alloc, N, K, dev):
+    """After the timed steps: decode fused with one SGD-with-momentum step
+    (reads and writes weights and momentum, 16 B/element + messages) against
+    decode_accumulate followed by the same step as separate torch operations
+    (which also write and re-read the sum: 24 B/element + messages)."""
+    import torch
+    w = torch.zeros(n_alloc, dtype=torch.float32, device=dev)
+    m = torch.zeros(n_alloc, dtype=torch.float32, device=dev)
+    out = torch.empty(n_alloc, dtype=torch.float32, device=dev)
+    ws = plan.decode_sgd_workspace(K, dev)
+    lr, mu, scale = 0.01, 0.9, 1.0 / K
+
+    def fused():
+        A.decode_sgd(plan, msgs, w, m, lr, mu, ws, scale=scale)
+
+    def unfused():
+        A.decode_accumulate(plan, msgs, out, False, ws)
+        m.mul_(mu).add_(out, alpha=scale)
+        w.add_(m, alpha=-lr)
+
+    def time_it(fn, reps=6):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_f, t_u = time_it(fused), time_it(unfused)
+    mbytes = float(sum(x.numel() for x in msgs))
+    del w, m, out, ws
+    torch.cuda.empty_cache()
+    return {"messages": K, "fused_ms": round(t_f, 4),
+            "fused_GBps": round((mbytes + 16.0 * N) / (t_f * 1e-3) / 1e9, 1),
+            "decode_then_torch_sgd_ms": round(t_u, 4)}
+
+
 def lt_sweep(args):
     """Bin-length sweep (not the default run): the same 64 x 4096 x 4096
     layers and the same gradient stream compressed with L_T = 50, 500 and 5000
@@ -308,6 +349,7 @@ def main():
                          "payload_ratio": round(pr, 2), "wire_ratio": round(wr, 2)},
     }
     timer.close()
+    res["decode_sgd"] = measure_decode_sgd(A, plan, learner_msgs, n_alloc, N, K, dev)
 
     if not args.no_cpu_baseline:
         def host_dw(step_idx, length):

@@ -152,6 +152,34 @@ int adacomp_decode_accumulate(const adacomp_plan* plan, const void* const* msgs,
                               float* out, uint64_t n_elems, int accumulate, void* ws,
                               uint64_t ws_bytes, void* stream);
 
+/* One step of SGD with momentum (no dampening, no Nesterov), the optimizer the
+ * paper's abstract names for its training runs, taken on the summed messages:
+ *   g = scale * sum (+ weight_decay * w when weight_decay != 0)
+ *   m = momentum * m + g
+ *   w = w - lr * m
+ * each operation one float32 operation rounded to nearest. */
+typedef struct adacomp_sgd {
+    float lr;
+    float momentum;
+    float weight_decay;
+    float scale;    /* e.g. 1/K to average the learners' gradients */
+} adacomp_sgd;
+
+/* Sum K messages exactly as adacomp_decode_accumulate with accumulate = 0 and
+ * take one adacomp_sgd step on every element of every segment, without
+ * writing the sum to memory (one dense pass instead of decode + optimizer).
+ *   weights, momentum  [span] float32 each, updated in place; elements
+ *               outside every segment are not written.
+ *   sgd         HOST pointer to the step's parameters.
+ *   ws          ws_bytes >= adacomp_decode_sgd_workspace_bytes(plan, K); plans
+ *               with bins longer than 4093 elements need a dense scratch of
+ *               4 * span bytes in it.
+ * Foreign messages are skipped and counted as in adacomp_decode_accumulate. */
+int adacomp_decode_sgd(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                       float* weights, float* momentum, uint64_t n_elems, const adacomp_sgd* sgd,
+                       void* ws, uint64_t ws_bytes, void* stream);
+int adacomp_decode_sgd_workspace_bytes(const adacomp_plan* plan, uint32_t K, uint64_t* bytes);
+
 /* Same calls with a timer: device time of each kernel stage is recorded with
  * HIP events on `stream` and summed in the timer.  timer may be NULL. */
 int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float* dW,
@@ -162,6 +190,10 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
                                     uint32_t K, float* out, uint64_t n_elems, int accumulate,
                                     void* ws, uint64_t ws_bytes, void* stream,
                                     adacomp_timer* timer);
+int adacomp_decode_sgd_timed(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                             float* weights, float* momentum, uint64_t n_elems,
+                             const adacomp_sgd* sgd, void* ws, uint64_t ws_bytes, void* stream,
+                             adacomp_timer* timer);
 
 /* Kernel stages a timer reports, in this order. */
 #define ADACOMP_STAGE_TILE_PASS 0   /* dense pass: G, H, bin maxima, selection, counts */
@@ -173,7 +205,8 @@ int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const*
 #define ADACOMP_STAGE_DECODE_APPLY 6
 #define ADACOMP_STAGE_COMPRESS_CALL 7  /* a whole adacomp_compress call, gaps between kernels included */
 #define ADACOMP_STAGE_DECODE_CALL 8    /* a whole adacomp_decode_accumulate call */
-#define ADACOMP_NUM_STAGES 9
+#define ADACOMP_STAGE_DECODE_SGD_CALL 9  /* a whole adacomp_decode_sgd call (its kernels: stages 4-6) */
+#define ADACOMP_NUM_STAGES 10
 
 int adacomp_timer_create(adacomp_timer** timer);
 int adacomp_timer_destroy(adacomp_timer* timer);

@@ -197,3 +197,123 @@ def test_decode_rejects_too_many_messages():
         A.decode_accumulate(plan, [m], out, False, plan.decode_workspace(1, DEV)[:16])
     assert e.value.status == -5
     plan.close()
+
+
+# --------------------------------------------------------------------------
+# decode fused with one SGD-with-momentum step
+# --------------------------------------------------------------------------
+
+def _sgd_check(plan, segs, msgs, host_msgs, w_host, m_host, lr, mu, wd, scale, steps=3):
+    """Run `steps` fused steps on the GPU and the oracle from the same w, m;
+    compare bit for bit after each step (the oracle consumes its own state,
+    which stays equal to the GPU's while they agree)."""
+    K = len(msgs)
+    ws = plan.decode_sgd_workspace(K, DEV)
+    w_dev = torch.from_numpy(w_host.copy()).to(DEV)
+    m_dev = torch.from_numpy(m_host.copy()).to(DEV)
+    w_ref, m_ref = w_host.copy(), m_host.copy()
+    for step in range(steps):
+        A.decode_sgd(plan, msgs, w_dev, m_dev, lr, mu, ws, weight_decay=wd, scale=scale)
+        oracle.decode_sgd(segs, host_msgs, w_ref, m_ref, lr, mu, wd, scale)
+        np.testing.assert_array_equal(bits(host(m_dev)), bits(m_ref), err_msg=f"momentum, step {step}")
+        np.testing.assert_array_equal(bits(host(w_dev)), bits(w_ref), err_msg=f"weights, step {step}")
+    assert int(host(ws[:4]).view(np.uint32)[0]) == 0
+
+
+@pytest.mark.parametrize("name,K,wd", [("fc", 2, 0.0), ("conv", 4, 1e-4), ("resnet50", 16, 5e-4),
+                                       ("fc_lstm", 3, 0.0)])
+def test_decode_sgd_parity(name, K, wd):
+    wl = W.workload(name)
+    plan = A.Plan(wl.segments)
+    n = W.alloc_len(wl)
+    msgs = learner_messages(wl, plan, K)
+    host_msgs = [host(m) for m in msgs]
+    rng = np.random.default_rng(K)
+    w = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    say(f"  decode+SGD {name} K={K} wd={wd}")
+    _sgd_check(plan, wl.segments, msgs, host_msgs, w, m, 0.01, 0.9, wd, 1.0 / K)
+    plan.close()
+
+
+@pytest.mark.parametrize("lt", [1, 7, 50, 500, 4093, 4094, 32768])
+def test_decode_sgd_edge_tables(lt):
+    """Every bin-length class, including bins longer than 4093 (summed in the
+    workspace scratch, then stepped), ragged sizes and gaps between layers
+    (never written)."""
+    segs, off = [], 4
+    for n in (1, 5, 63, 4097, 40003):
+        segs.append((off, n, lt))
+        off += (n + 3) // 4 * 4 + 8
+    span = off + 4
+    plan = A.Plan(segs)
+    rng = np.random.default_rng(lt + 1)
+    cws = plan.compress_workspace(DEV)
+    msgs, host_msgs = [], []
+    for k in range(3):
+        r = torch.from_numpy((rng.standard_normal(span) * 1e-3).astype(np.float32)).to(DEV)
+        d = torch.from_numpy((rng.standard_normal(span) * 1e-3).astype(np.float32)).to(DEV)
+        mm = plan.message_buffer(DEV)
+        A.compress(plan, r, d, mm, cws)
+        total, _, _ = A.message_header(plan, mm)
+        msgs.append(mm[:total].clone())
+        host_msgs.append(host(msgs[-1]))
+    w = rng.standard_normal(span).astype(np.float32)
+    m = (rng.standard_normal(span) * 1e-2).astype(np.float32)
+    say(f"  decode+SGD L_T={lt}")
+    _sgd_check(plan, segs, msgs, host_msgs, w, m, 0.05, 0.5, 1e-3, 1.0 / 3.0)
+    plan.close()
+
+
+def test_decode_sgd_large_workload_sampled():
+    """K = 16 on the 1.07-billion-element workload in one call; three layers
+    checked bit for bit against the oracle on their own."""
+    wl = W.workload("large")
+    plan = A.Plan(wl.segments)
+    K = 16
+    say("  building 16 learner messages at full size")
+    msgs = learner_messages(wl, plan, K, steps=2)
+    n = W.alloc_len(wl)
+    w = torch.empty(n, dtype=torch.float32, device=DEV)
+    w.normal_(0.0, 0.05, generator=torch.Generator(device=DEV).manual_seed(5))
+    m = torch.zeros(n, dtype=torch.float32, device=DEV)
+    w0 = {i: host(w[o:o + c]) for i, (o, c, _) in enumerate(wl.segments) if i in (0, 31, 63)}
+    ws = plan.decode_sgd_workspace(K, DEV)
+    say("  decode+SGD K=16 full size")
+    A.decode_sgd(plan, msgs, w, m, 0.01, 0.9, ws, scale=1.0 / K)
+    torch.cuda.synchronize()
+    host_msgs = []
+    for mm in msgs:
+        total, _, _ = A.message_header(plan, mm)
+        host_msgs.append(host(mm[:total]))
+    for i in (0, 31, 63):
+        o, c, lt = wl.segments[i]
+        sub = [(0, c, lt)]
+        w_ref, m_ref = w0[i].copy(), np.zeros(c, np.float32)
+        oracle.decode_sgd(sub, [mp.single_segment_message(hm, wl.segments, i) for hm in host_msgs],
+                          w_ref, m_ref, 0.01, 0.9, 0.0, 1.0 / K)
+        np.testing.assert_array_equal(bits(host(w[o:o + c])), bits(w_ref))
+        np.testing.assert_array_equal(bits(host(m[o:o + c])), bits(m_ref))
+        say(f"    segment {i} ok")
+    plan.close()
+    del msgs, w, m, ws
+    torch.cuda.empty_cache()
+
+
+def test_decode_sgd_argument_errors():
+    segs = [(0, 100, 50)]
+    plan = A.Plan(segs)
+    mm = plan.message_buffer(DEV)
+    w = torch.zeros(100, dtype=torch.float32, device=DEV)
+    m = torch.zeros(100, dtype=torch.float32, device=DEV)
+    ws = plan.decode_sgd_workspace(1, DEV)
+    with pytest.raises(A.AdaCompError) as e:
+        A.decode_sgd(plan, [mm], w, m, 0.1, 0.9, ws[:16])
+    assert e.value.status == -5
+    with pytest.raises(A.AdaCompError) as e:
+        A.decode_sgd(plan, [mm], w, w, 0.1, 0.9, ws)
+    assert e.value.status == -1
+    with pytest.raises(A.AdaCompError) as e:
+        A.decode_sgd(plan, [mm], w[1:], m[1:], 0.1, 0.9, ws)
+    assert e.value.status == -3
+    plan.close()
