@@ -62,8 +62,12 @@ def traffic_from_profiles(workload: str):
 
 
 def cpu_baseline(wl, dws_host_fn, max_steps: int, seconds: float = 15.0):
-    """Time the oracle (single thread) on whole layers of the workload."""
+    """Time the oracle on whole layers of the workload, as it stands: single
+    threaded, and with one call per layer on a pool of host threads (the
+    oracle call releases the interpreter lock, so layers run on separate
+    cores; at most 16 threads, the host share of one GPU)."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     segs = wl.segments
     take = min(24, len(segs))
@@ -71,23 +75,43 @@ def cpu_baseline(wl, dws_host_fn, max_steps: int, seconds: float = 15.0):
     for (_, n, lt) in segs[:take]:
         sub.append((off, n, lt))
         off += (n + 3) // 4 * 4
-    r = np.zeros(off, np.float32)
-    steps, elems, t_used = 0, 0, 0.0
-    while t_used < seconds and steps < max_steps:
-        d = dws_host_fn(steps, off)
-        t0 = time.perf_counter()
-        oracle.compress(sub, r, d)
-        t_used += time.perf_counter() - t0
-        steps += 1
-        elems += sum(n for _, n, _ in sub)
+    per_layer = [[(0, n, lt)] for (_, n, lt) in sub]
+    elems_per_step = sum(n for _, n, _ in sub)
+
+    def run(threads):
+        r = np.zeros(off, np.float32)
+        steps, t_used = 0, 0.0
+        pool = ThreadPoolExecutor(max_workers=threads) if threads > 1 else None
+        while t_used < seconds / 2 and steps < max_steps:
+            d = dws_host_fn(steps, off)
+            t0 = time.perf_counter()
+            if pool is None:
+                oracle.compress(sub, r, d)
+            else:
+                views = [(r[o:o + n], d[o:o + n]) for (o, n, _) in sub]
+                list(pool.map(lambda i: oracle.compress(per_layer[i], views[i][0], views[i][1]),
+                              range(len(sub))))
+            t_used += time.perf_counter() - t0
+            steps += 1
+        if pool is not None:
+            pool.shutdown()
+        return steps, t_used
+
+    threads = max(1, min(16, os.cpu_count() or 1, take))
+    s1, t1 = run(1)
+    sn, tn = run(threads) if threads > 1 else (s1, t1)
+    v1, vn = s1 * elems_per_step / t1 / 1e9, sn * elems_per_step / tn / 1e9
+    best, cores = (vn, threads) if vn > v1 else (v1, 1)   # whichever the host does faster
     return {
-        "value": round(elems / t_used / 1e9, 4),
+        "value": round(best, 4),
         "unit": "Gelem/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{take} of {len(segs)} layers ({sum(n for _, n, _ in sub)} elements), "
-                  f"{steps} compress steps from zero residue on the benchmark's own gradients, "
-                  f"{t_used:.1f} s single-threaded",
+        "single_thread_value": round(v1, 4),
+        "threaded_value": round(vn, 4),
+        "sample": f"{take} of {len(segs)} layers ({elems_per_step} elements), compress steps from zero "
+                  f"residue on the benchmark's own gradients: {sn} steps in {tn:.1f} s with one layer "
+                  f"per thread on {threads} threads; single-threaded {s1} steps in {t1:.1f} s",
     }
 
 

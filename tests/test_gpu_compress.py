@@ -232,6 +232,57 @@ def test_local_selection_conv_workload():
     plan.close()
 
 
+def test_table_order_differs_from_memory_order():
+    """Layers listed in another order than they lie in memory (message
+    regions follow the table, elements the offsets), with gaps; compress and
+    a decode of two such messages."""
+    segs = [(60000, 5003, 50), (0, 40001, 500), (48008, 7, 3), (40004, 8000, 4094)]
+    span = 65004
+    plan = A.Plan(segs)
+    msg, ws = plan.message_buffer(DEV), plan.compress_workspace(DEV)
+    gmax = torch.empty(int(plan.info.total_bins), dtype=torch.float32, device=DEV)
+    rng = np.random.default_rng(23)
+    host_msgs, dev_msgs = [], []
+    for k in range(2):
+        r = (rng.standard_normal(span) * 1e-3).astype(np.float32)
+        d = (rng.standard_normal(span) * 1e-3).astype(np.float32)
+        m, r_out, g = run_gpu_step(plan, torch.from_numpy(r.copy()).to(DEV),
+                                   torch.from_numpy(d).to(DEV), msg, ws, gmax)
+        compare_step(segs, r, d, r_out, m, g)
+        host_msgs.append(m.copy())
+        dev_msgs.append(torch.from_numpy(m.copy()).to(DEV))
+    out = torch.full((span,), 7.0, dtype=torch.float32, device=DEV)
+    A.decode_accumulate(plan, dev_msgs, out, False, plan.decode_workspace(2, DEV))
+    want = np.full(span, 7.0, np.float32)
+    oracle.decode_accumulate(segs, host_msgs, want, False)
+    np.testing.assert_array_equal(bits(out.cpu().numpy()), bits(want))
+    plan.close()
+
+
+def test_one_layer_of_many_scan_chunks():
+    """A single layer of 2^28 elements (131072 tiles, 128 scan chunks in one
+    layer): the chunk-level offsets and the encode's start search across
+    chunks, checked in full against the oracle over two steps."""
+    n = 1 << 28
+    segs = [(0, n, 500)]
+    plan = A.Plan(segs)
+    msg, ws = plan.message_buffer(DEV), plan.compress_workspace(DEV)
+    gmax = torch.empty(int(plan.info.total_bins), dtype=torch.float32, device=DEV)
+    r_dev = torch.zeros(n, dtype=torch.float32, device=DEV)
+    d_dev = torch.empty(n, dtype=torch.float32, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(29)
+    for step in range(2):
+        d_dev.normal_(0.0, 1e-3, generator=gen)
+        r_in, d = r_dev.cpu().numpy(), d_dev.cpu().numpy()
+        say(f"  one layer of {n} elements, step {step}")
+        m, r_out, g = run_gpu_step(plan, r_dev, d_dev, msg, ws, gmax)
+        rep = compare_step(segs, r_in, d, r_out, m, g)
+        say(f"    survivors {rep.survivors}")
+    plan.close()
+    del r_dev, d_dev, msg, ws, gmax
+    torch.cuda.empty_cache()
+
+
 def test_determinism_and_resume():
     """Two runs give the same bits; 5 steps + residue checkpoint + 5 steps equal
     10 straight steps."""
