@@ -73,6 +73,10 @@ def _load():
                                           ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                           ctypes.c_float]
         lib.oracle_decode_sgd.restype = ctypes.c_int
+        lib.oracle_decode_adam.argtypes = [P(_Seg), ctypes.c_uint32, P(ctypes.c_void_p),
+                                           ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p] + [ctypes.c_float] * 6 + [ctypes.c_uint32]
+        lib.oracle_decode_adam.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -170,3 +174,25 @@ def decode_sgd(segments, messages, w: np.ndarray, m: np.ndarray, lr: float, mome
                                    float(lr), float(momentum), float(weight_decay), float(scale))
     if st != 0:
         raise OracleError(f"oracle_decode_sgd failed: {st}")
+
+
+def decode_adam(segments, messages, w: np.ndarray, m: np.ndarray, v: np.ndarray, lr: float,
+                beta1: float, beta2: float, eps: float, step: int, weight_decay: float = 0.0,
+                scale: float = 1.0) -> None:
+    """Sum the messages and take Adam step number ``step`` (>= 1) on w, m, v
+    (float32, in place); the formula is in ``adacomp_oracle.c``."""
+    for a in (w, m, v):
+        if a.dtype != np.float32 or not a.flags.c_contiguous:
+            raise TypeError("w, m and v must be contiguous float32")
+    arr, n = _segs(segments)
+    span = max(int(s[0]) + int(s[1]) for s in segments)
+    if min(w.size, m.size, v.size) < span:
+        raise ValueError("w, m or v shorter than the segment table's span")
+    keep = [np.frombuffer(bytes(x), dtype=np.uint8) if isinstance(x, (bytes, bytearray, memoryview))
+            else np.ascontiguousarray(x, dtype=np.uint8) for x in messages]
+    ptrs = (ctypes.c_void_p * max(1, len(keep)))(*[x.ctypes.data for x in keep])
+    st = _load().oracle_decode_adam(arr, n, ptrs, len(keep), w.ctypes.data, m.ctypes.data,
+                                    v.ctypes.data, float(lr), float(beta1), float(beta2), float(eps),
+                                    float(weight_decay), float(scale), int(step))
+    if st != 0:
+        raise OracleError(f"oracle_decode_adam failed: {st}")

@@ -47,6 +47,11 @@
  *     of SGD with momentum in its usual form (no dampening, no Nesterov):
  *     g = scale * sum (+ weight_decay * w when weight_decay != 0),
  *     m = momentum * m + g, w = w - lr * m, each operation rounded to float.
+ *   - decode + Adam step: Adam with bias-corrected moments in its textbook
+ *     form, each operation rounded to float: g as above, m = b1*m + (1-b1)*g,
+ *     v = b2*v + (1-b2)*(g*g), w = w - lr * ((m/c1) / (sqrt(v/c2) + eps))
+ *     with c1 = 1 - b1^t, c2 = 1 - b2^t for step t >= 1 (each computed in
+ *     double and rounded once to float; 1-b1, 1-b2 are float operations).
  *   - LS (segment flag 1): per bin exactly one element is transmitted, the
  *     first (lowest index) whose |G| equals the bin maximum, and none when
  *     the maximum is 0; it is quantized with the same layer-wide s and the
@@ -372,6 +377,46 @@ int oracle_decode_sgd(const oracle_segment *segs, uint32_t nseg, const uint8_t *
                 if (weight_decay != 0.0f) g = g + weight_decay * w[j];
                 m[j] = momentum * m[j] + g;
                 w[j] = w[j] - lr * m[j];
+            }
+        }
+    }
+    free(sum);
+    return st;
+}
+
+/*
+ * Sum K messages and apply one Adam step (step number t >= 1) to every
+ * element of every segment, [Opt]:
+ *   g = scale * sum;  if weight_decay != 0: g = g + weight_decay * w;
+ *   m = b1 * m + (1 - b1) * g;  v = b2 * v + (1 - b2) * (g * g);
+ *   w = w - lr * ((m / c1) / (sqrt(v / c2) + eps)),
+ *   c1 = 1 - b1^t, c2 = 1 - b2^t (double, rounded once to float).
+ */
+int oracle_decode_adam(const oracle_segment *segs, uint32_t nseg, const uint8_t *const *msgs,
+                       uint32_t K, float *w, float *m, float *v, float lr, float b1, float b2,
+                       float eps, float weight_decay, float scale, uint32_t t) {
+    int st = check_segments(segs, nseg);
+    if (st != ORACLE_OK) return st;
+    if (t == 0u) return ORACLE_BAD_ARG;
+    uint64_t span = 0;
+    for (uint32_t l = 0; l < nseg; ++l)
+        if (segs[l].offset + segs[l].numel > span) span = segs[l].offset + segs[l].numel;
+    float *sum = (float *)malloc((span ? span : 1) * sizeof(float));
+    if (!sum) return ORACLE_BAD_ARG;
+    st = oracle_decode_accumulate(segs, nseg, msgs, K, sum, 0);
+    if (st == ORACLE_OK) {
+        const float c1 = (float)(1.0 - pow((double)b1, (double)t));
+        const float c2 = (float)(1.0 - pow((double)b2, (double)t));
+        const float omb1 = 1.0f - b1, omb2 = 1.0f - b2;
+        for (uint32_t l = 0; l < nseg; ++l) {
+            for (uint64_t j = segs[l].offset; j < segs[l].offset + segs[l].numel; ++j) {
+                float g = scale * sum[j];
+                if (weight_decay != 0.0f) g = g + weight_decay * w[j];
+                m[j] = b1 * m[j] + omb1 * g;
+                v[j] = b2 * v[j] + omb2 * (g * g);
+                const float mh = m[j] / c1;
+                const float vh = v[j] / c2;
+                w[j] = w[j] - lr * (mh / (sqrtf(vh) + eps));
             }
         }
     }

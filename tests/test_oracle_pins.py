@@ -689,3 +689,96 @@ def test_decode_sgd_special_cases():
     for o, n, _ in segs:
         np.testing.assert_array_equal(m2[o:o + n], s32[o:o + n])
         np.testing.assert_array_equal(w2[o:o + n], (w[o:o + n] - np.float32(0.125) * s32[o:o + n]).astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# Decode fused with one Adam step (bias-corrected moments)
+# --------------------------------------------------------------------------
+
+def test_decode_adam_matches_torch_adam_in_float64():
+    """torch.optim.Adam (weight decay added to the gradient) in float64 from
+    the same state: the moments agree within float32 rounding bounds of
+    their terms, and the weight update agrees given the moments.  Catches:
+    moments without (1 - beta), missing bias correction, eps inside the
+    square root, the wrong sign, a missing scale."""
+    import torch
+    segs, span, msgs, w, m = _sgd_inputs(51)
+    rng = np.random.default_rng(52)
+    v = (rng.random(span) * 1e-5).astype(np.float32)
+    lr, b1, b2, eps, wd, scale, t = 1e-3, 0.9, 0.999, 1e-8, 1e-2, 1.0 / 3.0, 7
+    s32 = np.zeros(span, np.float32)
+    oracle.decode_accumulate(segs, msgs, s32, False)
+    w1, m1, v1 = w.copy(), m.copy(), v.copy()
+    oracle.decode_adam(segs, msgs, w1, m1, v1, lr, b1, b2, eps, t, wd, scale)
+    f = lambda x: float(np.float32(x))
+    p = torch.tensor(w.astype(np.float64), requires_grad=True)
+    p.grad = torch.tensor(s32.astype(np.float64) * f(scale))
+    opt = torch.optim.Adam([p], lr=f(lr), betas=(f(b1), f(b2)), eps=f(eps), weight_decay=f(wd))
+    opt.state[p] = {"step": torch.tensor(float(t - 1), dtype=torch.float64),
+                    "exp_avg": torch.tensor(m.astype(np.float64)),
+                    "exp_avg_sq": torch.tensor(v.astype(np.float64))}
+    opt.step()
+    inside = np.zeros(span, bool)
+    for o, n, _ in segs:
+        inside[o:o + n] = True
+    e32 = np.float64(np.finfo(np.float32).eps)
+    g = s32.astype(np.float64) * f(scale) + f(wd) * w.astype(np.float64)
+    g_mag = np.abs(s32.astype(np.float64) * f(scale)) + np.abs(f(wd) * w.astype(np.float64))
+    m_mag = np.abs(f(b1) * m) + (1 - f(b1)) * g_mag
+    v_mag = np.abs(f(b2) * v) + (1 - f(b2)) * g_mag ** 2
+    for got, ref, mag in ((m1, opt.state[p]["exp_avg"].numpy(), m_mag),
+                          (v1, opt.state[p]["exp_avg_sq"].numpy(), v_mag)):
+        err = np.abs(got[inside].astype(np.float64) - ref[inside])
+        assert np.all(err <= 4 * e32 * mag[inside] + 1e-45)
+    # the weight update, given the float32 moments
+    c1, c2 = 1 - f(b1) ** t, 1 - f(b2) ** t
+    r = (m1.astype(np.float64) / c1) / (np.sqrt(v1.astype(np.float64) / c2) + f(eps))
+    w_ref = w.astype(np.float64) - f(lr) * r
+    err = np.abs(w1[inside].astype(np.float64) - w_ref[inside])
+    assert np.all(err <= 8 * e32 * (np.abs(w[inside]) + f(lr) * np.abs(r[inside])))
+    # and torch's own weights agree to the same order
+    p_ref = p.detach().numpy()
+    assert np.max(np.abs(w1[inside] - p_ref[inside])) < 1e-3 * np.max(np.abs(p_ref[inside] - w[inside]))
+    for a, b in ((w1, w), (m1, m), (v1, v)):
+        np.testing.assert_array_equal(bits(a[~inside]), bits(b[~inside]))
+
+
+def test_decode_adam_dyadic_closed_form():
+    """s = 1 messages (q = +-1 on one element per bin), beta1 = 1/2, beta2 =
+    3/4, eps = 2^-40 (below half an ulp of 1), lr = 1/4, from m = v = 0: the
+    bias-corrected moments are exactly q and q^2 at steps 1 and 2, so each
+    step moves w by exactly -lr*q, and elements with q = 0 do not move."""
+    n, lt = 1000, 50
+    segs = [(0, n, lt)]
+    rng = np.random.default_rng(8)
+    r = (rng.integers(-7, 8, n) / 16.0).astype(np.float32)
+    ones = np.arange(0, n, lt) + rng.integers(0, lt, n // lt)
+    sign = rng.choice([-1.0, 1.0], ones.size).astype(np.float32)
+    r[ones] = sign
+    msg = run_oracle(segs, r, np.zeros(n, np.float32))[2]
+    w0 = (rng.integers(-64, 64, n) / 8.0).astype(np.float32)
+    w, m, v = w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in (1, 2):
+        oracle.decode_adam(segs, [msg], w, m, v, 0.25, 0.5, 0.75, 2.0 ** -40, t)
+    q = np.zeros(n, np.float32)
+    q[ones] = sign
+    np.testing.assert_array_equal(w, (w0 - np.float32(0.5) * q).astype(np.float32))
+    np.testing.assert_array_equal(m, (np.float32(0.75) * q).astype(np.float32))
+    np.testing.assert_array_equal(v, (np.float32(0.4375) * q * q).astype(np.float32))
+
+
+def test_decode_adam_special_cases():
+    """lr = 0 leaves w bit for bit; beta1 = beta2 = 0 (no weight decay, scale
+    1) make m the decoded sum and v its square, bit for bit."""
+    segs, span, msgs, w, m = _sgd_inputs(53)
+    v = np.abs(m).astype(np.float32)
+    s32 = np.zeros(span, np.float32)
+    oracle.decode_accumulate(segs, msgs, s32, False)
+    w1, m1, v1 = w.copy(), m.copy(), v.copy()
+    oracle.decode_adam(segs, msgs, w1, m1, v1, 0.0, 0.9, 0.999, 1e-8, 3)
+    np.testing.assert_array_equal(bits(w1), bits(w))
+    w2, m2, v2 = w.copy(), m.copy(), v.copy()
+    oracle.decode_adam(segs, msgs, w2, m2, v2, 1e-3, 0.0, 0.0, 1e-8, 1)
+    for o, n, _ in segs:
+        np.testing.assert_array_equal(m2[o:o + n], s32[o:o + n])
+        np.testing.assert_array_equal(v2[o:o + n], (s32[o:o + n] * s32[o:o + n]).astype(np.float32))
