@@ -20,10 +20,10 @@ _HERE = pathlib.Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libadacomp.so"
 
 OK = 0
-NUM_STAGES = 10
+NUM_STAGES = 11
 STAGES = ("tile_pass", "chunk_scan", "finalize", "encode",
           "decode_count", "decode_base", "decode_apply", "compress_call", "decode_call",
-          "decode_sgd_call")
+          "decode_sgd_call", "decode_adam_call")
 MAX_MESSAGES = 256
 MAX_BIN_LEN = 32768
 SEG_LS = 1   # segment flag: hard local selection (see include/adacomp.h)
@@ -67,6 +67,13 @@ class Sgd(ctypes.Structure):
                 ("weight_decay", ctypes.c_float), ("scale", ctypes.c_float)]
 
 
+class Adam(ctypes.Structure):
+    """One Adam step (bias-corrected moments); see include/adacomp.h."""
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("scale", ctypes.c_float), ("step", ctypes.c_uint32)]
+
+
 # Every exported symbol, with its C signature (argtypes, restype).
 _P = ctypes.c_void_p
 _U32, _U64, _INT = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int
@@ -85,6 +92,10 @@ SIGNATURES = {
     "adacomp_decode_sgd_timed": ([_P, ctypes.POINTER(_P), _U32, _P, _P, _U64, ctypes.POINTER(Sgd), _P,
                                   _U64, _P, _P], _INT),
     "adacomp_decode_sgd_workspace_bytes": ([_P, _U32, ctypes.POINTER(_U64)], _INT),
+    "adacomp_decode_adam": ([_P, ctypes.POINTER(_P), _U32, _P, _P, _P, _U64, ctypes.POINTER(Adam), _P,
+                             _U64, _P], _INT),
+    "adacomp_decode_adam_timed": ([_P, ctypes.POINTER(_P), _U32, _P, _P, _P, _U64, ctypes.POINTER(Adam),
+                                   _P, _U64, _P, _P], _INT),
     "adacomp_timer_create": ([ctypes.POINTER(_P)], _INT),
     "adacomp_timer_destroy": ([_P], _INT),
     "adacomp_timer_read": ([_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_U64), _U32], _INT),
@@ -279,6 +290,22 @@ def decode_sgd(plan: Plan, msgs: List, weights, momentum, lr: float, momentum_co
         n, ctypes.byref(p), _u8_ptr(ws, "ws"), ws.numel(), _stream_handle(stream),
         timer.handle if timer is not None else None)
     _check("adacomp_decode_sgd", st)
+
+
+def decode_adam(plan: Plan, msgs: List, weights, m, v, lr: float, beta1: float, beta2: float,
+                eps: float, step: int, ws, weight_decay: float = 0.0, scale: float = 1.0,
+                stream=None, timer: Optional[Timer] = None) -> None:
+    """Sum the messages (in list order) and take Adam step number ``step``
+    (>= 1) on weights, m and v (in place), without writing the sum.  ws as
+    for decode_sgd (Plan.decode_sgd_workspace)."""
+    ptrs = (_P * max(1, len(msgs)))(*[_u8_ptr(x, "msgs[k]") for x in msgs])
+    n = min(weights.numel(), m.numel(), v.numel())
+    p = Adam(lr, beta1, beta2, eps, weight_decay, scale, int(step))
+    st = lib().adacomp_decode_adam_timed(
+        plan.handle, ptrs, len(msgs), _f32_ptr(weights, "weights"), _f32_ptr(m, "m"),
+        _f32_ptr(v, "v"), n, ctypes.byref(p), _u8_ptr(ws, "ws"), ws.numel(),
+        _stream_handle(stream), timer.handle if timer is not None else None)
+    _check("adacomp_decode_adam", st)
 
 
 def message_header(plan: Plan, msg):

@@ -7,6 +7,7 @@
 // Application claim (Table 2).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -413,11 +414,12 @@ SgdLayout sgd_layout(const Layout& L, uint32_t K) {
     return o;
 }
 
-// Shared by decode_accumulate (out != nullptr) and decode + SGD (sgd != nullptr).
+// Shared by decode_accumulate (opt == kOptNone, out) and decode fused with
+// an optimizer step (op.w, op.m and, for Adam, op.v).
 int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, float* out,
-                int accumulate, const adacomp_sgd* sgd, float* weights, float* momentum,
-                uint64_t n_elems, void* ws, uint64_t ws_bytes, void* stream_, adacomp_timer* timer,
-                int call_stage) {
+                int accumulate, int opt, adacomp::OptParams op, uint64_t n_elems, void* ws,
+                uint64_t ws_bytes, void* stream_, adacomp_timer* timer, int call_stage) {
+    const bool fused = opt != adacomp::kOptNone;
     if (plan == nullptr || msgs == nullptr || ws == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
     if (K == 0 || K > ADACOMP_MAX_MESSAGES) return ADACOMP_ERR_INVALID_ARGUMENT;
     if (accumulate != 0 && accumulate != 1) return ADACOMP_ERR_INVALID_ARGUMENT;
@@ -425,18 +427,20 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
     const DecodeLayout D = decode_layout(L, K);
     const SgdLayout S = sgd_layout(L, K);
     std::vector<Range> dense;   // the dense buffers written
-    if (sgd == nullptr) {
+    if (!fused) {
         if (out == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
         if (!aligned16(out)) return ADACOMP_ERR_MISALIGNED;
         dense.push_back(range_of(out, 4 * L.span));
     } else {
-        if (weights == nullptr || momentum == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
-        if (!aligned16(weights) || !aligned16(momentum)) return ADACOMP_ERR_MISALIGNED;
-        dense.push_back(range_of(weights, 4 * L.span));
-        dense.push_back(range_of(momentum, 4 * L.span));
+        float* st_bufs[3] = {op.w, op.m, opt == adacomp::kOptAdam ? op.v : op.w};
+        for (int i = 0; i < (opt == adacomp::kOptAdam ? 3 : 2); ++i) {
+            if (st_bufs[i] == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+            if (!aligned16(st_bufs[i])) return ADACOMP_ERR_MISALIGNED;
+            dense.push_back(range_of(st_bufs[i], 4 * L.span));
+        }
     }
     if (!aligned16(ws)) return ADACOMP_ERR_MISALIGNED;
-    const uint64_t need = sgd ? S.total : std::max<uint64_t>(D.total, L.dws_fixed + uint64_t(K) * L.dws_per_msg);
+    const uint64_t need = fused ? S.total : std::max<uint64_t>(D.total, L.dws_fixed + uint64_t(K) * L.dws_per_msg);
     if (n_elems < L.span || ws_bytes < need) return ADACOMP_ERR_CAPACITY;
     const Range rw = range_of(ws, need);
     for (size_t i = 0; i < dense.size(); ++i) {
@@ -469,15 +473,8 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
     dw.dseg_eoff = reinterpret_cast<uint64_t*>(w8 + D.dseg_eoff);
     dw.dvalid = reinterpret_cast<uint32_t*>(w8 + D.dvalid);
     const uint32_t DT = static_cast<uint32_t>(L.dt.ntiles), DC = static_cast<uint32_t>(L.dt.nchunks);
-    adacomp::SgdParams sp{};
     float* sums = out;   // where long-bin tiles accumulate
-    if (sgd) {
-        sp.lr = sgd->lr;
-        sp.momentum = sgd->momentum;
-        sp.weight_decay = sgd->weight_decay;
-        sp.scale = sgd->scale;
-        sp.w = weights;
-        sp.m = momentum;
+    if (fused) {
         sums = reinterpret_cast<float*>(w8 + S.scratch);
         accumulate = 0;
     }
@@ -505,22 +502,31 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
             if (v == 0) {   // the tile fits in LDS
                 const uint32_t acc_words = L.dt.max_span_vecs[0] * 4;
                 const uint32_t lds = adacomp::decode_lds_bytes(acc_words, K, KG, ps, 4);
-                if (sgd)
-                    hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, true>), dim3(n), dim3(256),
-                                       lds, stream, mp, K, KG, ps, plan->ddesc[0], DT, DC, L.nseg, dw,
-                                       nullptr, 0, acc_words, sp);
+                if (opt == adacomp::kOptSgd)
+                    hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, adacomp::kOptSgd>), dim3(n),
+                                       dim3(256), lds, stream, mp, K, KG, ps, plan->ddesc[0], DT, DC,
+                                       L.nseg, dw, nullptr, 0, acc_words, op);
+                else if (opt == adacomp::kOptAdam)
+                    hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, adacomp::kOptAdam>), dim3(n),
+                                       dim3(256), lds, stream, mp, K, KG, ps, plan->ddesc[0], DT, DC,
+                                       L.nseg, dw, nullptr, 0, acc_words, op);
                 else
                     hipLaunchKernelGGL((adacomp::k_decode_apply<256, true>), dim3(n), dim3(256), lds,
                                        stream, mp, K, KG, ps, plan->ddesc[0], DT, DC, L.nseg, dw, out,
-                                       accumulate, acc_words, sp);
+                                       accumulate, acc_words, op);
             } else {        // long bins, accumulated in place (in out, or the scratch)
                 const uint32_t lds = adacomp::decode_lds_bytes(0, K, KG, ps, 16);
                 hipLaunchKernelGGL((adacomp::k_decode_apply<1024, false>), dim3(n), dim3(1024), lds,
                                    stream, mp, K, KG, ps, plan->ddesc[1], DT, DC, L.nseg, dw, sums,
-                                   accumulate, 0u, sp);
-                if (sgd && launch_status() == ADACOMP_OK)
-                    hipLaunchKernelGGL(adacomp::k_sgd_tiles, dim3(n), dim3(256), 0, stream,
-                                       plan->ddesc[1], sums, sp);
+                                   accumulate, 0u, op);
+                if (launch_status() == ADACOMP_OK) {
+                    if (opt == adacomp::kOptSgd)
+                        hipLaunchKernelGGL(adacomp::k_opt_tiles<adacomp::kOptSgd>, dim3(n), dim3(256), 0,
+                                           stream, plan->ddesc[1], sums, op);
+                    else if (opt == adacomp::kOptAdam)
+                        hipLaunchKernelGGL(adacomp::k_opt_tiles<adacomp::kOptAdam>, dim3(n), dim3(256),
+                                           0, stream, plan->ddesc[1], sums, op);
+                }
             }
             if ((st = launch_status()) != ADACOMP_OK) return st;
         }
@@ -537,8 +543,8 @@ extern "C" {
 int adacomp_decode_accumulate_timed(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
                                     float* out, uint64_t n_elems, int accumulate, void* ws,
                                     uint64_t ws_bytes, void* stream, adacomp_timer* timer) {
-    return decode_impl(plan, msgs, K, out, accumulate, nullptr, nullptr, nullptr, n_elems, ws,
-                       ws_bytes, stream, timer, ADACOMP_STAGE_DECODE_CALL);
+    return decode_impl(plan, msgs, K, out, accumulate, adacomp::kOptNone, adacomp::OptParams{},
+                       n_elems, ws, ws_bytes, stream, timer, ADACOMP_STAGE_DECODE_CALL);
 }
 
 int adacomp_decode_accumulate(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
@@ -560,8 +566,46 @@ int adacomp_decode_sgd_timed(const adacomp_plan* plan, const void* const* msgs, 
                              const adacomp_sgd* sgd, void* ws, uint64_t ws_bytes, void* stream,
                              adacomp_timer* timer) {
     if (sgd == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
-    return decode_impl(plan, msgs, K, nullptr, 0, sgd, weights, momentum, n_elems, ws, ws_bytes,
+    adacomp::OptParams op{};
+    op.lr = sgd->lr;
+    op.beta1 = sgd->momentum;
+    op.weight_decay = sgd->weight_decay;
+    op.scale = sgd->scale;
+    op.w = weights;
+    op.m = momentum;
+    return decode_impl(plan, msgs, K, nullptr, 0, adacomp::kOptSgd, op, n_elems, ws, ws_bytes,
                        stream, timer, ADACOMP_STAGE_DECODE_SGD_CALL);
+}
+
+int adacomp_decode_adam_timed(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                              float* weights, float* m, float* v, uint64_t n_elems,
+                              const adacomp_adam* adam, void* ws, uint64_t ws_bytes, void* stream,
+                              adacomp_timer* timer) {
+    if (adam == nullptr || adam->step == 0) return ADACOMP_ERR_INVALID_ARGUMENT;
+    adacomp::OptParams op{};
+    op.lr = adam->lr;
+    op.beta1 = adam->beta1;
+    op.beta2 = adam->beta2;
+    op.eps = adam->eps;
+    op.weight_decay = adam->weight_decay;
+    op.scale = adam->scale;
+    // bias corrections in double, rounded once; 1 - beta as float operations
+    op.c1 = static_cast<float>(1.0 - std::pow(static_cast<double>(adam->beta1), static_cast<double>(adam->step)));
+    op.c2 = static_cast<float>(1.0 - std::pow(static_cast<double>(adam->beta2), static_cast<double>(adam->step)));
+    op.omb1 = 1.0f - adam->beta1;
+    op.omb2 = 1.0f - adam->beta2;
+    op.w = weights;
+    op.m = m;
+    op.v = v;
+    return decode_impl(plan, msgs, K, nullptr, 0, adacomp::kOptAdam, op, n_elems, ws, ws_bytes,
+                       stream, timer, ADACOMP_STAGE_DECODE_ADAM_CALL);
+}
+
+int adacomp_decode_adam(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                        float* weights, float* m, float* v, uint64_t n_elems,
+                        const adacomp_adam* adam, void* ws, uint64_t ws_bytes, void* stream) {
+    return adacomp_decode_adam_timed(plan, msgs, K, weights, m, v, n_elems, adam, ws, ws_bytes,
+                                     stream, nullptr);
 }
 
 int adacomp_decode_sgd(const adacomp_plan* plan, const void* const* msgs, uint32_t K,

@@ -163,33 +163,82 @@ __device__ __forceinline__ uint32_t word_at(uint64_t a, uint32_t wb) {
 // floats s][NW*(KG+1) u32 per-wavefront flat prefixes][KG*pstride u32 bin
 // prefixes].  Everything else about the tile comes from its descriptor.
 
-// One step of SGD with momentum on the summed gradient (no dampening, no
-// Nesterov), every operation rounded to float32:
-//   g = scale * sum (+ weight_decay * w),  m = momentum * m + g,  w = w - lr * m.
-struct SgdParams {
-    float lr, momentum, weight_decay, scale;
+// Optimizer steps fused into decode, on the summed gradient, every operation
+// one float32 operation rounded to nearest (no contraction):
+//   SGD with momentum (no dampening, no Nesterov):
+//     g = scale * sum (+ weight_decay * w),  m = beta1 * m + g,  w = w - lr * m
+//   Adam with bias-corrected moments (c1 = 1 - beta1^t, c2 = 1 - beta2^t):
+//     m = beta1 * m + (1 - beta1) * g,  v = beta2 * v + (1 - beta2) * (g * g),
+//     w = w - lr * ((m / c1) / (sqrt(v / c2) + eps))
+constexpr int kOptNone = 0, kOptSgd = 1, kOptAdam = 2;
+
+struct OptParams {
+    float lr, beta1, beta2, eps, weight_decay, scale;
+    float c1, c2, omb1, omb2;   // Adam: bias corrections, 1 - beta1, 1 - beta2
     float* w;
     float* m;
+    float* v;
 };
 
-__device__ __forceinline__ void sgd_step(float sum, float& w, float& m, const SgdParams& p) {
+template <int OPT>
+__device__ __forceinline__ void opt_step(float sum, float& w, float& m, float& v, const OptParams& p) {
     float g = p.scale * sum;
     if (p.weight_decay != 0.0f) g = g + p.weight_decay * w;
-    m = p.momentum * m + g;
-    w = w - p.lr * m;
+    if (OPT == kOptSgd) {
+        m = p.beta1 * m + g;
+        w = w - p.lr * m;
+    } else {
+        m = p.beta1 * m + p.omb1 * g;
+        v = p.beta2 * v + p.omb2 * (g * g);
+        const float mh = m / p.c1;
+        const float vh = v / p.c2;
+        w = w - p.lr * (mh / (sqrtf(vh) + p.eps));
+    }
 }
 
-constexpr uint32_t kSgdSlots = kDecCap / 4 / 256;   // float4 per thread of an LDS tile
+// One float4 of weights and state: step the four elements and store those
+// inside the tile (whole float4 when the tile covers it).
+template <int OPT>
+__device__ __forceinline__ void opt_apply(const f32x4& a, f32x4& wq, f32x4& mq, f32x4& vq,
+                                          const OptParams& op, uint64_t e0, int x0, int tlen) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        float wc = wq[c], mc = mq[c], vc = vq[c];
+        opt_step<OPT>(a[c], wc, mc, vc, op);
+        wq[c] = wc;
+        mq[c] = mc;
+        vq[c] = vc;
+    }
+    if (x0 >= 0 && x0 + 4 <= tlen) {
+        store4<true>(op.w + e0, wq);
+        store4<true>(op.m + e0, mq);
+        if (OPT == kOptAdam) store4<true>(op.v + e0, vq);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int x = x0 + c;
+            if (x >= 0 && x < tlen) {
+                op.w[e0 + c] = wq[c];
+                op.m[e0 + c] = mq[c];
+                if (OPT == kOptAdam) op.v[e0 + c] = vq[c];
+            }
+        }
+    }
+}
 
-// SGD: instead of writing the tile's sums to out, the tile's weights and
-// momentum (loaded when the tile starts, kept in registers) take one step.
-template <int THREADS, bool LDS_ACC, bool SGD = false>
+constexpr uint32_t kOptSlots = kDecCap / 4 / 256;   // float4 per thread of an LDS tile
+
+// OPT != kOptNone: instead of writing the tile's sums to out, the tile's
+// weights and optimizer state (loaded when the tile starts, kept in
+// registers) take one step.
+template <int THREADS, bool LDS_ACC, int OPT = kOptNone>
 __global__ void __launch_bounds__(THREADS)
 k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                const DecDesc* __restrict__ descs, uint32_t DT, uint32_t DC, uint32_t nseg,
                DecodeWs ws, float* __restrict__ out, int accumulate, uint32_t acc_words,
-               SgdParams sp) {
-    static_assert(!SGD || (LDS_ACC && THREADS == 256), "the SGD step is fused into LDS tiles");
+               OptParams op) {
+    constexpr bool FUSED = OPT != kOptNone;
+    static_assert(!FUSED || (LDS_ACC && THREADS == 256), "optimizer steps are fused into LDS tiles");
     constexpr int NW = THREADS / 64;
     extern __shared__ uint64_t dyn64[];
     uint32_t* dyn = reinterpret_cast<uint32_t*>(dyn64);
@@ -212,14 +261,16 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
     uint32_t* wfk = wfk_all + wv * (KG + 1);
 
     for (uint32_t k = tid; k < K; k += THREADS) ks[k] = ws.dseg_s[uint64_t(k) * nseg + dd.si];
-    f32x4 wv4[SGD ? kSgdSlots : 1], mv4[SGD ? kSgdSlots : 1];
-    if (SGD) {   // weights and momentum of this thread's float4 slots, requested early
+    constexpr uint32_t NS = FUSED ? kOptSlots : 1;
+    f32x4 wv4[NS], mv4[NS], vv4[OPT == kOptAdam ? NS : 1];
+    if (FUSED) {   // weights and state of this thread's float4 slots, requested early
 #pragma unroll
-        for (uint32_t j = 0; j < kSgdSlots; ++j) {
+        for (uint32_t j = 0; j < NS; ++j) {
             const uint32_t vi = uint32_t(tid) + THREADS * j;
             if (vi < nvec) {
-                wv4[j] = load4<true>(sp.w + v0 + uint64_t(vi) * 4u);
-                mv4[j] = load4<true>(sp.m + v0 + uint64_t(vi) * 4u);
+                wv4[j] = load4<true>(op.w + v0 + uint64_t(vi) * 4u);
+                mv4[j] = load4<true>(op.m + v0 + uint64_t(vi) * 4u);
+                if (OPT == kOptAdam) vv4[OPT == kOptAdam ? j : 0] = load4<true>(op.v + v0 + uint64_t(vi) * 4u);
             }
         }
     }
@@ -360,7 +411,7 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
             }
         }
     }
-    if (LDS_ACC && !SGD) {
+    if (LDS_ACC && !FUSED) {
         __syncthreads();
         for (uint32_t vi = tid; vi < nvec; vi += THREADS) {
             const int x0 = int(vi * 4) - int(lead);
@@ -375,73 +426,35 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
             }
         }
     }
-    if (SGD) {
+    if (FUSED) {
         __syncthreads();
 #pragma unroll
-        for (uint32_t j = 0; j < kSgdSlots; ++j) {
+        for (uint32_t j = 0; j < NS; ++j) {
             const uint32_t vi = uint32_t(tid) + THREADS * j;
             if (vi >= nvec) continue;
-            const int x0 = int(vi * 4) - int(lead);
-            const uint64_t e0 = v0 + uint64_t(vi) * 4u;
-            f32x4 wq = wv4[j], mq = mv4[j];
             const f32x4 a = *reinterpret_cast<const f32x4*>(acc + vi * 4);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float wc = wq[c], mc = mq[c];
-                sgd_step(a[c], wc, mc, sp);
-                wq[c] = wc;
-                mq[c] = mc;
-            }
-            if (x0 >= 0 && x0 + 4 <= int(tlen)) {
-                store4<true>(sp.w + e0, wq);
-                store4<true>(sp.m + e0, mq);
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int x = x0 + c;
-                    if (x >= 0 && x < int(tlen)) {
-                        sp.w[e0 + c] = wq[c];
-                        sp.m[e0 + c] = mq[c];
-                    }
-                }
-            }
+            f32x4 wq = wv4[j], mq = mv4[j], vq = vv4[OPT == kOptAdam ? j : 0];
+            opt_apply<OPT>(a, wq, mq, vq, op, v0 + uint64_t(vi) * 4u, int(vi * 4) - int(lead),
+                           int(tlen));
         }
     }
 }
 
-// The SGD step for long-bin decode tiles, whose sums were accumulated in a
-// dense scratch buffer (same flat indexing as the weights).
+// The optimizer step for long-bin decode tiles, whose sums were accumulated
+// in a dense scratch buffer (same flat indexing as the weights).
+template <int OPT>
 __global__ void __launch_bounds__(256)
-k_sgd_tiles(const DecDesc* __restrict__ descs, const float* __restrict__ sums, SgdParams sp) {
+k_opt_tiles(const DecDesc* __restrict__ descs, const float* __restrict__ sums, OptParams op) {
     const DecDesc dd = descs[blockIdx.x];
     const uint64_t v0 = dd.t0 & ~uint64_t(3);
     const uint32_t lead = uint32_t(dd.t0 - v0);
     const uint32_t nvec = (lead + dd.tlen + 3u) >> 2;
     for (uint32_t vi = threadIdx.x; vi < nvec; vi += 256) {
-        const int x0 = int(vi * 4) - int(lead);
         const uint64_t e0 = v0 + uint64_t(vi) * 4u;
         const f32x4 a = load4<true>(sums + e0);
-        f32x4 wq = load4<true>(sp.w + e0), mq = load4<true>(sp.m + e0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float wc = wq[c], mc = mq[c];
-            sgd_step(a[c], wc, mc, sp);
-            wq[c] = wc;
-            mq[c] = mc;
-        }
-        if (x0 >= 0 && x0 + 4 <= int(dd.tlen)) {
-            store4<true>(sp.w + e0, wq);
-            store4<true>(sp.m + e0, mq);
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int x = x0 + c;
-                if (x >= 0 && x < int(dd.tlen)) {
-                    sp.w[e0 + c] = wq[c];
-                    sp.m[e0 + c] = mq[c];
-                }
-            }
-        }
+        f32x4 wq = load4<true>(op.w + e0), mq = load4<true>(op.m + e0), vq = {0.f, 0.f, 0.f, 0.f};
+        if (OPT == kOptAdam) vq = load4<true>(op.v + e0);
+        opt_apply<OPT>(a, wq, mq, vq, op, e0, int(vi * 4) - int(lead), int(dd.tlen));
     }
 }
 

@@ -119,7 +119,8 @@ def measure_decode_sgd(A, plan, msgs, n_alloc, N, K, dev):
     """After the timed steps: decode fused with one SGD-with-momentum step
     (reads and writes weights and momentum, 16 B/element + messages) against
     decode_accumulate followed by the same step as separate torch operations
-    (which also write and re-read the sum: 24 B/element + messages)."""
+    (which also write and re-read the sum: 24 B/element + messages), and
+    decode fused with one Adam step (24 B/element + messages)."""
     import torch
     w = torch.zeros(n_alloc, dtype=torch.float32, device=dev)
     m = torch.zeros(n_alloc, dtype=torch.float32, device=dev)
@@ -147,13 +148,22 @@ def measure_decode_sgd(A, plan, msgs, n_alloc, N, K, dev):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    t_f, t_u = time_it(fused), time_it(unfused)
+    v = torch.zeros(n_alloc, dtype=torch.float32, device=dev)
+    step = [0]
+
+    def adam():
+        step[0] += 1
+        A.decode_adam(plan, msgs, w, m, v, 1e-3, 0.9, 0.999, 1e-8, step[0], ws, scale=scale)
+
+    t_f, t_u, t_a = time_it(fused), time_it(unfused), time_it(adam)
     mbytes = float(sum(x.numel() for x in msgs))
-    del w, m, out, ws
+    del w, m, v, out, ws
     torch.cuda.empty_cache()
     return {"messages": K, "fused_ms": round(t_f, 4),
             "fused_GBps": round((mbytes + 16.0 * N) / (t_f * 1e-3) / 1e9, 1),
-            "decode_then_torch_sgd_ms": round(t_u, 4)}
+            "decode_then_torch_sgd_ms": round(t_u, 4),
+            "fused_adam_ms": round(t_a, 4),
+            "fused_adam_GBps": round((mbytes + 24.0 * N) / (t_a * 1e-3) / 1e9, 1)}
 
 
 def lt_sweep(args):

@@ -180,6 +180,32 @@ int adacomp_decode_sgd(const adacomp_plan* plan, const void* const* msgs, uint32
                        void* ws, uint64_t ws_bytes, void* stream);
 int adacomp_decode_sgd_workspace_bytes(const adacomp_plan* plan, uint32_t K, uint64_t* bytes);
 
+/* One Adam step with bias-corrected moments (the other optimizer the paper's
+ * abstract names), in its textbook form, each operation one float32
+ * operation rounded to nearest (division and square root correctly rounded):
+ *   g = scale * sum (+ weight_decay * w when weight_decay != 0)
+ *   m = beta1 * m + (1 - beta1) * g;   v = beta2 * v + (1 - beta2) * (g * g)
+ *   w = w - lr * ((m / c1) / (sqrt(v / c2) + eps))
+ * c1 = 1 - beta1^step, c2 = 1 - beta2^step, each computed in double on the
+ * host and rounded once to float; 1 - beta1 and 1 - beta2 are float
+ * operations.  step >= 1 counts the calls made so far, this one included. */
+typedef struct adacomp_adam {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;
+    float scale;
+    uint32_t step;
+} adacomp_adam;
+
+/* As adacomp_decode_sgd, with one Adam step on weights, m and v ([span]
+ * float32 each, updated in place).  ws as for adacomp_decode_sgd
+ * (adacomp_decode_sgd_workspace_bytes).  step = 0 is an invalid argument. */
+int adacomp_decode_adam(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                        float* weights, float* m, float* v, uint64_t n_elems,
+                        const adacomp_adam* adam, void* ws, uint64_t ws_bytes, void* stream);
+
 /* Same calls with a timer: device time of each kernel stage is recorded with
  * HIP events on `stream` and summed in the timer.  timer may be NULL. */
 int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float* dW,
@@ -194,6 +220,10 @@ int adacomp_decode_sgd_timed(const adacomp_plan* plan, const void* const* msgs, 
                              float* weights, float* momentum, uint64_t n_elems,
                              const adacomp_sgd* sgd, void* ws, uint64_t ws_bytes, void* stream,
                              adacomp_timer* timer);
+int adacomp_decode_adam_timed(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
+                              float* weights, float* m, float* v, uint64_t n_elems,
+                              const adacomp_adam* adam, void* ws, uint64_t ws_bytes, void* stream,
+                              adacomp_timer* timer);
 
 /* Kernel stages a timer reports, in this order. */
 #define ADACOMP_STAGE_TILE_PASS 0   /* dense pass: G, H, bin maxima, selection, counts */
@@ -206,7 +236,8 @@ int adacomp_decode_sgd_timed(const adacomp_plan* plan, const void* const* msgs, 
 #define ADACOMP_STAGE_COMPRESS_CALL 7  /* a whole adacomp_compress call, gaps between kernels included */
 #define ADACOMP_STAGE_DECODE_CALL 8    /* a whole adacomp_decode_accumulate call */
 #define ADACOMP_STAGE_DECODE_SGD_CALL 9  /* a whole adacomp_decode_sgd call (its kernels: stages 4-6) */
-#define ADACOMP_NUM_STAGES 10
+#define ADACOMP_STAGE_DECODE_ADAM_CALL 10 /* a whole adacomp_decode_adam call (its kernels: stages 4-6) */
+#define ADACOMP_NUM_STAGES 11
 
 int adacomp_timer_create(adacomp_timer** timer);
 int adacomp_timer_destroy(adacomp_timer* timer);

@@ -317,3 +317,79 @@ def test_decode_sgd_argument_errors():
         A.decode_sgd(plan, [mm], w[1:], m[1:], 0.1, 0.9, ws)
     assert e.value.status == -3
     plan.close()
+
+
+# --------------------------------------------------------------------------
+# decode fused with one Adam step
+# --------------------------------------------------------------------------
+
+def _adam_check(plan, segs, msgs, host_msgs, w_host, m_host, v_host, lr, b1, b2, eps, wd, scale,
+                steps=3):
+    K = len(msgs)
+    ws = plan.decode_sgd_workspace(K, DEV)
+    dev = [torch.from_numpy(a.copy()).to(DEV) for a in (w_host, m_host, v_host)]
+    ref = [a.copy() for a in (w_host, m_host, v_host)]
+    for t in range(1, steps + 1):
+        A.decode_adam(plan, msgs, dev[0], dev[1], dev[2], lr, b1, b2, eps, t, ws,
+                      weight_decay=wd, scale=scale)
+        oracle.decode_adam(segs, host_msgs, ref[0], ref[1], ref[2], lr, b1, b2, eps, t, wd, scale)
+        for name, d, r in zip(("weights", "m", "v"), dev, ref):
+            np.testing.assert_array_equal(bits(host(d)), bits(r), err_msg=f"{name}, step {t}")
+
+
+@pytest.mark.parametrize("name,K,wd", [("fc", 2, 0.0), ("conv", 4, 1e-4), ("resnet50", 16, 1e-2),
+                                       ("fc_lstm", 3, 0.0)])
+def test_decode_adam_parity(name, K, wd):
+    wl = W.workload(name)
+    plan = A.Plan(wl.segments)
+    n = W.alloc_len(wl)
+    msgs = learner_messages(wl, plan, K)
+    host_msgs = [host(x) for x in msgs]
+    rng = np.random.default_rng(K + 100)
+    w = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (rng.random(n) * 1e-7).astype(np.float32)
+    say(f"  decode+Adam {name} K={K} wd={wd}")
+    _adam_check(plan, wl.segments, msgs, host_msgs, w, m, v, 1e-3, 0.9, 0.999, 1e-8, wd, 1.0 / K)
+    plan.close()
+
+
+@pytest.mark.parametrize("lt", [1, 50, 4093, 4094, 32768])
+def test_decode_adam_edge_tables(lt):
+    segs, off = [], 4
+    for n in (1, 5, 63, 4097, 40003):
+        segs.append((off, n, lt))
+        off += (n + 3) // 4 * 4 + 8
+    span = off + 4
+    plan = A.Plan(segs)
+    rng = np.random.default_rng(lt + 7)
+    cws = plan.compress_workspace(DEV)
+    msgs, host_msgs = [], []
+    for k in range(2):
+        r = torch.from_numpy((rng.standard_normal(span) * 1e-3).astype(np.float32)).to(DEV)
+        d = torch.from_numpy((rng.standard_normal(span) * 1e-3).astype(np.float32)).to(DEV)
+        mm = plan.message_buffer(DEV)
+        A.compress(plan, r, d, mm, cws)
+        total, _, _ = A.message_header(plan, mm)
+        msgs.append(mm[:total].clone())
+        host_msgs.append(host(msgs[-1]))
+    w = rng.standard_normal(span).astype(np.float32)
+    m = np.zeros(span, np.float32)
+    v = np.zeros(span, np.float32)
+    say(f"  decode+Adam L_T={lt}")
+    _adam_check(plan, segs, msgs, host_msgs, w, m, v, 1e-2, 0.9, 0.99, 1e-6, 0.0, 0.5)
+    plan.close()
+
+
+def test_decode_adam_argument_errors():
+    plan = A.Plan([(0, 100, 50)])
+    mm = plan.message_buffer(DEV)
+    w, m, v = (torch.zeros(100, dtype=torch.float32, device=DEV) for _ in range(3))
+    ws = plan.decode_sgd_workspace(1, DEV)
+    with pytest.raises(A.AdaCompError) as e:
+        A.decode_adam(plan, [mm], w, m, v, 1e-3, 0.9, 0.999, 1e-8, 0, ws)
+    assert e.value.status == -1
+    with pytest.raises(A.AdaCompError) as e:
+        A.decode_adam(plan, [mm], w, m, m, 1e-3, 0.9, 0.999, 1e-8, 1, ws)
+    assert e.value.status == -1
+    plan.close()
