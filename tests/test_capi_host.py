@@ -153,3 +153,17 @@ def test_tile_geometry_on_cpu(tmp_path):
     fails = [(i, l) for i, l in enumerate(out) if not l.startswith("OK")]
     assert not fails, fails[:5]
     assert r.returncode == 0
+
+
+def test_header_is_plain_c_and_host_calls_work(tmp_path):
+    """include/adacomp.h compiles as C99 with warnings as errors, and a plain
+    C program linked against the library makes the host-only calls (plan
+    query, argument errors, status strings, an empty timer) without a GPU."""
+    exe = tmp_path / "c_abi_check"
+    lib_dir = ROOT / "adaptive_residual_gradient_amd"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-o", str(exe),
+                    str(ROOT / "tests" / "cpu" / "c_abi_check.c"), f"-L{lib_dir}", "-ladacomp",
+                    f"-Wl,-rpath,{lib_dir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "OK host-only calls" in out.stdout
