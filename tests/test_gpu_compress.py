@@ -283,6 +283,40 @@ def test_one_layer_of_many_scan_chunks():
     torch.cuda.empty_cache()
 
 
+def test_layer_past_two_to_the_31():
+    """One layer of 2^31 + 5 elements (ragged last bin): every element index,
+    tile offset and survivor count past the signed 32-bit range, compared in
+    full with the oracle; then decoded (K = 1) and compared."""
+    n = (1 << 31) + 5
+    segs = [(0, n, 500)]
+    plan = A.Plan(segs)
+    span = int(plan.info.span)
+    msg, ws = plan.message_buffer(DEV), plan.compress_workspace(DEV)
+    r_dev = torch.empty(span, dtype=torch.float32, device=DEV)
+    d_dev = torch.empty(span, dtype=torch.float32, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(31)
+    r_dev.normal_(0.0, 1e-3, generator=gen)
+    d_dev.normal_(0.0, 1e-3, generator=gen)
+    r_in, d = r_dev.cpu().numpy(), d_dev.cpu().numpy()
+    say(f"  one layer of {n} elements")
+    A.compress(plan, r_dev, d_dev, msg, ws)
+    torch.cuda.synchronize()
+    total, surv, _ = A.message_header(plan, msg)
+    m = msg[:total].cpu().numpy()
+    del ws
+    rep = compare_step(segs, r_in, d, r_dev.cpu().numpy(), m)
+    say(f"    survivors {rep.survivors}, message {total} bytes")
+    del r_dev, d_dev, r_in, d
+    out = torch.empty(span, dtype=torch.float32, device=DEV)
+    A.decode_accumulate(plan, [msg], out, False, plan.decode_workspace(1, DEV))
+    want = np.empty(span, np.float32)
+    oracle.decode_accumulate(segs, [m], want, False)
+    np.testing.assert_array_equal(bits(out[:n].cpu().numpy()), bits(want[:n]))
+    plan.close()
+    del out, msg
+    torch.cuda.empty_cache()
+
+
 def test_determinism_and_resume():
     """Two runs give the same bits; 5 steps + residue checkpoint + 5 steps equal
     10 straight steps."""
