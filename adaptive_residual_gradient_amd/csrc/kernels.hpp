@@ -30,7 +30,8 @@
 //               G - sign(G) * s.
 // Decode, per call, three launches: per-tile counts of every message, chunk
 // bases and message validity, then the per-tile apply that sums the messages
-// in order in LDS (large tiles: directly in out) and writes each tile once.
+// in order in LDS (long bins: directly in out) and writes each tile once, or,
+// fused with an optimizer, takes one SGD or Adam step on the weights instead.
 #pragma once
 
 #include "common.hpp"

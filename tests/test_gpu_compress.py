@@ -80,8 +80,9 @@ EDGE_NUMEL = [1, 2, 3, 5, 7, 63, 65, 4093, 4097, 36861, 40003]
 @pytest.mark.parametrize("lt", EDGE_BINS)
 def test_edge_bin_lengths(lt):
     """Every bin length class (per-element path L_T < 4, two-run path, 8/16-bit
-    switch at 64, small/large tiles at 4093/4094, the 16-bit maximum), ragged
-    last bins, tiny segments, gaps between segments, ties and +-0."""
+    switch at 64, register tiles / streamed long bins at 4093/4094, the 16-bit
+    maximum), ragged last bins, tiny segments, gaps between segments, ties
+    and +-0."""
     rng = np.random.default_rng(lt)
     segs, off = [], 4
     for n in EDGE_NUMEL:
