@@ -27,6 +27,10 @@ STAGES = ("tile_pass", "chunk_scan", "finalize", "encode",
 MAX_MESSAGES = 256
 MAX_BIN_LEN = 32768
 SEG_LS = 1   # segment flag: hard local selection (see include/adacomp.h)
+PLAN_SEPARATE_FINISH = 1   # plan flag: finish with three kernels even for a small table
+PLAN_SINGLE_LAUNCH = 2     # plan flag: a small table in one launch (slower; for comparison)
+SMALL_TABLE_MAX_SPAN = 1 << 21     # tables up to this span and this many segments
+SMALL_TABLE_MAX_SEGMENTS = 256     # finish in one launch after the tile pass
 
 
 class HipLibraryMissing(RuntimeError):
@@ -51,7 +55,8 @@ class PlanInfo(ctypes.Structure):
                 ("header_bytes", ctypes.c_uint64), ("message_capacity", ctypes.c_uint64),
                 ("compress_workspace_bytes", ctypes.c_uint64),
                 ("decode_workspace_bytes_per_message", ctypes.c_uint64),
-                ("decode_workspace_bytes_fixed", ctypes.c_uint64)]
+                ("decode_workspace_bytes_fixed", ctypes.c_uint64),
+                ("compress_launches", ctypes.c_uint64)]
 
     def as_dict(self):
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
@@ -80,6 +85,7 @@ _U32, _U64, _INT = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int
 SIGNATURES = {
     "adacomp_plan_query": ([ctypes.POINTER(_Segment), _U32, ctypes.POINTER(PlanInfo)], _INT),
     "adacomp_plan_create": ([ctypes.POINTER(_Segment), _U32, ctypes.POINTER(_P)], _INT),
+    "adacomp_plan_create_ex": ([ctypes.POINTER(_Segment), _U32, _U32, ctypes.POINTER(_P)], _INT),
     "adacomp_plan_destroy": ([_P], _INT),
     "adacomp_plan_get_info": ([_P, ctypes.POINTER(PlanInfo)], _INT),
     "adacomp_compress": ([_P, _P, _P, _U64, _P, _U64, _P, _U64, _P, _P], _INT),
@@ -205,13 +211,16 @@ class Plan:
 
     ``segments``: (offset, numel, bin_len) or (offset, numel, bin_len, flags)
     per layer, offsets in elements of the flat float32 buffers (multiples of
-    4); flags 0 (AdaComp) or SEG_LS."""
+    4); flags 0 (AdaComp) or SEG_LS.  ``plan_flags``: 0, PLAN_SEPARATE_FINISH
+    or PLAN_SINGLE_LAUNCH (``info.compress_launches`` says how many launches
+    a compress call makes)."""
 
-    def __init__(self, segments):
+    def __init__(self, segments, plan_flags: int = 0):
         self.segments = [tuple(int(x) for x in s) for s in segments]
         arr, n = _segments(self.segments)
         h = _P()
-        _check("adacomp_plan_create", lib().adacomp_plan_create(arr, n, ctypes.byref(h)))
+        _check("adacomp_plan_create_ex",
+               lib().adacomp_plan_create_ex(arr, n, int(plan_flags), ctypes.byref(h)))
         self.handle = h
         info = PlanInfo()
         _check("adacomp_plan_get_info", lib().adacomp_plan_get_info(h, ctypes.byref(info)))

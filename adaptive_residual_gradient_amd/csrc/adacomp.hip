@@ -36,6 +36,10 @@ struct adacomp_plan {
     DevTiling dct, ddt;                                        // compress and decode tiles
     adacomp::DecDesc* ddesc[adacomp::kDecVariants] = {nullptr, nullptr};   // decode tiles in launch order
     uint32_t tile_lds_words[adacomp::kVariants] = {0, 0, 0};  // one tile's LDS words
+    adacomp::Finish finish = adacomp::Finish::kSeparate;
+    uint32_t* tile_t0 = nullptr;    // small-table finish: first element of each compress tile
+    uint32_t small_lds_bytes = 0;   // k_finish_small's dynamic LDS
+    uint32_t single_lds_bytes = 0;  // k_compress_single's: tile or finish tables, the larger
 };
 
 namespace adacomp {
@@ -116,6 +120,8 @@ struct CallTimer {
     }
     void finish() {
         if (!t) return;
+        if (c.stage.empty()) record();   // a call without stages: its end event
+        if (!t) return;                  // that event failed
         t->calls.push_back(std::move(c));
         c = adacomp_timer::Call{};
         t = nullptr;
@@ -190,7 +196,7 @@ int adacomp_plan_query(const adacomp_segment* segs, uint32_t nseg, adacomp_plan_
         Layout L;
         const int st = adacomp::build_layout(segs, nseg, L);
         if (st != ADACOMP_OK) return st;
-        adacomp::fill_info(L, info);
+        adacomp::fill_info(L, adacomp::choose_finish(L, 0u), info);
         return ADACOMP_OK;
     } catch (...) {
         return ADACOMP_ERR_INVALID_ARGUMENT;
@@ -198,8 +204,16 @@ int adacomp_plan_query(const adacomp_segment* segs, uint32_t nseg, adacomp_plan_
 }
 
 int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan** out) {
+    return adacomp_plan_create_ex(segs, nseg, 0u, out);
+}
+
+int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t plan_flags,
+                           adacomp_plan** out) {
     if (out == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
     *out = nullptr;
+    if (plan_flags != 0u && plan_flags != ADACOMP_PLAN_SEPARATE_FINISH &&
+        plan_flags != ADACOMP_PLAN_SINGLE_LAUNCH)
+        return ADACOMP_ERR_INVALID_ARGUMENT;
     adacomp_plan* p = nullptr;
     try {
         p = new adacomp_plan();
@@ -254,6 +268,16 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
             const std::vector<adacomp::DecDesc> d = adacomp::decode_descs(L, v);
             o_desc[v] = put(d.data(), sizeof(adacomp::DecDesc) * d.size());
         }
+        p->finish = adacomp::choose_finish(L, plan_flags);
+        uint64_t o_t0 = 0;
+        if (p->finish != adacomp::Finish::kSeparate) {
+            std::vector<uint32_t> t0(L.ct.ntiles);
+            for (uint64_t t = 0; t < L.ct.ntiles; ++t) {
+                const SegDev& sg = L.segs[L.ct.tile_seg[t]];
+                t0[t] = static_cast<uint32_t>(adacomp::tile_geom(sg, sg.ct, uint32_t(t)).t0);
+            }
+            o_t0 = put(t0.data(), 4 * t0.size());
+        }
         if (hipMalloc(&p->dmem, host.size()) != hipSuccess) {
             p->dmem = nullptr;
             delete p;
@@ -277,10 +301,18 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
         bind(p->ddt, od);
         for (int v = 0; v < adacomp::kDecVariants; ++v)
             p->ddesc[v] = reinterpret_cast<adacomp::DecDesc*>(base + o_desc[v]);
+        if (p->finish != adacomp::Finish::kSeparate)
+            p->tile_t0 = reinterpret_cast<uint32_t*>(base + o_t0);
         // Per tile: bin maxima, bin boundaries, and for hard local selection
         // the first index of each bin's maximum.
         for (int v = 0; v < adacomp::kVariants; ++v)
             p->tile_lds_words[v] = (L.has_ls ? 3 : 2) * L.ct.max_bpt[v] + 1;
+        p->small_lds_bytes = static_cast<uint32_t>(
+            adacomp::round_up(adacomp::small_lds_bytes(L.ct.ntiles, L.ct.nchunks, L.nseg), 8));
+        p->single_lds_bytes = std::max<uint32_t>(
+            4 * std::max(L.ct.by_variant[0].empty() ? 0u : p->tile_lds_words[0],
+                         L.ct.by_variant[1].empty() ? 0u : p->tile_lds_words[1]),
+            p->small_lds_bytes);
         *out = p;
         return ADACOMP_OK;
     } catch (...) {
@@ -302,7 +334,7 @@ int adacomp_plan_destroy(adacomp_plan* plan) {
 
 int adacomp_plan_get_info(const adacomp_plan* plan, adacomp_plan_info* info) {
     if (plan == nullptr || info == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
-    adacomp::fill_info(plan->L, info);
+    adacomp::fill_info(plan->L, plan->finish, info);
     return ADACOMP_OK;
 }
 
@@ -346,6 +378,36 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     uint8_t* m8 = static_cast<uint8_t*>(msg);
 
     CallTimer tm(timer, stream, ADACOMP_STAGE_COMPRESS_CALL);
+    adacomp::SmallArgs sa{};
+    if (plan->finish != adacomp::Finish::kSeparate) {
+        sa.segs = plan->d_segs;
+        sa.tile_seg = plan->dct.tile_seg;
+        sa.tile_t0 = plan->tile_t0;
+        sa.vtiles0 = plan->dct.vtiles[0];
+        sa.vtiles1 = plan->dct.vtiles[1];
+        sa.chunk_tile_begin = plan->dct.chunk_tile_begin;
+        sa.residue = residue;
+        sa.dW = dW;
+        sa.msg = m8;
+        sa.stage = stage;
+        sa.tile_cnt = tile_cnt;
+        sa.tile_gsum = tile_gsum;
+        sa.bin_max_out = bin_max_out;
+        sa.sync = reinterpret_cast<uint64_t*>(w8 + L.ws_sync);
+        sa.entries_begin = L.entries_begin;
+        sa.n0 = static_cast<uint32_t>(L.ct.by_variant[0].size());
+        sa.ntiles = static_cast<uint32_t>(L.ct.ntiles);
+        sa.nchunks = static_cast<uint32_t>(L.ct.nchunks);
+        sa.nseg = L.nseg;
+        sa.plan_hash = L.plan_hash;
+    }
+    if (plan->finish == adacomp::Finish::kSingle) {
+        hipLaunchKernelGGL(adacomp::k_compress_single, dim3(sa.ntiles), dim3(256),
+                           plan->single_lds_bytes, stream, sa);
+        if ((st = launch_status()) != ADACOMP_OK) return st;
+        tm.finish();
+        return ADACOMP_OK;
+    }
     {
         for (int v = 0; v < adacomp::kVariants; ++v) {
             if (L.ct.by_variant[v].empty()) continue;
@@ -362,6 +424,14 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
             if (e != hipSuccess) return ADACOMP_ERR_HIP;
         }
         tm.mark(ADACOMP_STAGE_TILE_PASS);
+    }
+    if (plan->finish == adacomp::Finish::kSmall) {
+        hipLaunchKernelGGL(adacomp::k_finish_small, dim3(encode_blocks(L)), dim3(256),
+                           plan->small_lds_bytes, stream, sa);
+        if ((st = launch_status()) != ADACOMP_OK) return st;
+        tm.mark(ADACOMP_STAGE_ENCODE);
+        tm.finish();
+        return ADACOMP_OK;
     }
     {
         hipLaunchKernelGGL(adacomp::k_chunk_scan, dim3(static_cast<uint32_t>(L.ct.nchunks)), dim3(256),

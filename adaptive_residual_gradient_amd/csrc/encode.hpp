@@ -38,26 +38,71 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* l
     return before + inc - v;
 }
 
-// Chunk scan: tiles [chunk_tile_begin[c], chunk_tile_begin[c+1]) <= 1024.
-__global__ void __launch_bounds__(256)
-k_chunk_scan(const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ tile_cnt,
-             const double* __restrict__ tile_gsum, uint32_t* __restrict__ tile_off,
-             uint32_t* __restrict__ chunk_cnt, double* __restrict__ chunk_gsum) {
-    __shared__ uint32_t lw[4];
-    __shared__ double lg[4];
+// The float64 sum of a scan chunk's tile sums (tiles [tb, tb + n), 1 <= n
+// <= 1024) in the one fixed order every compress path uses: partial v
+// (0..255) adds tiles 4v..4v+3 in order; the partials 64q..64q+63 are
+// reduced by an xor butterfly over a wavefront (lane 0's result is used);
+// the four results are added in order q = 0, 1, 2, 3.  Every term is >= +0,
+// so adding +0.0 in place of a missing tile changes nothing.
+__device__ __forceinline__ double chunk_partial(const double* __restrict__ tile_gsum, uint32_t tb,
+                                                uint32_t n, uint32_t v) {
+    double gs = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = v * 4u + i;
+        const double x = tile_gsum[tb + min(t, n - 1u)];   // branch-free: clamped, then dropped
+        gs += t < n ? x : 0.0;
+    }
+    return gs;
+}
+__device__ __forceinline__ double wave_xor_sum(double gs) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) gs += __shfl_xor(gs, d);
+    return gs;
+}
+__device__ __forceinline__ double combine4(double a, double b, double c, double d) {
+    return ((a + b) + c) + d;
+}
+// The same sum by one thread for a chunk of at most 32 tiles.  Partials
+// 8..255 are then +0.0, so the butterfly levels 32, 16 and 8 add +0.0 to
+// lanes 0..7 and the results of wavefronts 1..3 are +0.0: all exact.  What
+// remains for lane 0 is levels 4, 2, 1 over partials 0..7, i.e. the fold
+// a[i] += a[i + d] for d = 4, 2, 1 and i < d (the same binary tree; a sum
+// of two doubles does not depend on the order of its operands).
+__device__ __forceinline__ double chunk_sum_short(const double* __restrict__ tile_gsum,
+                                                  uint32_t tb, uint32_t n) {
+    double a[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) a[v] = chunk_partial(tile_gsum, tb, n, uint32_t(v));
+#pragma unroll
+    for (int d = 4; d >= 1; d >>= 1)
+#pragma unroll
+        for (int i = 0; i < d; ++i) a[i] = a[i] + a[i + d];
+    return a[0];
+}
+constexpr uint32_t kShortChunkTiles = 32;
+
+// Chunk scan of scan chunk c by one block of 256 threads: tiles
+// [chunk_tile_begin[c], chunk_tile_begin[c+1]) <= 1024.  lw: 4 LDS words,
+// lg: 4 LDS doubles.
+__device__ __forceinline__ void chunk_scan_block(uint32_t c, const uint32_t* __restrict__ chunk_tile_begin,
+                                                 const uint32_t* __restrict__ tile_cnt,
+                                                 const double* __restrict__ tile_gsum,
+                                                 uint32_t* __restrict__ tile_off,
+                                                 uint32_t* __restrict__ chunk_cnt,
+                                                 double* __restrict__ chunk_gsum, uint32_t* lw,
+                                                 double* lg) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const uint32_t c = blockIdx.x;
     const uint32_t tb = chunk_tile_begin[c], n = chunk_tile_begin[c + 1] - tb;
     uint32_t cnt[4];
     uint32_t mine = 0;
-    double gs = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t t = uint32_t(tid) * 4u + i;
         cnt[i] = t < n ? tile_cnt[tb + t] : 0u;
-        if (t < n) gs += tile_gsum[tb + t];
         mine += cnt[i];
     }
+    double gs = chunk_partial(tile_gsum, tb, n, uint32_t(tid));
     uint32_t total;
     uint32_t run = block_exclusive_scan<256>(mine, lw, &total);
 #pragma unroll
@@ -66,25 +111,39 @@ k_chunk_scan(const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __re
         if (t < n) tile_off[tb + t] = run;
         run += cnt[i];
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) gs += __shfl_xor(gs, d);
+    gs = wave_xor_sum(gs);
     if (lane == 0) lg[wv] = gs;
     __syncthreads();
     if (tid == 0) {
         chunk_cnt[c] = total;
-        chunk_gsum[c] = ((lg[0] + lg[1]) + lg[2]) + lg[3];
+        chunk_gsum[c] = combine4(lg[0], lg[1], lg[2], lg[3]);
     }
 }
 
-// Finalize: one block of 256 threads.
 __global__ void __launch_bounds__(256)
-k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
-           uint64_t entries_begin, const uint32_t* __restrict__ chunk_cnt,
-           const double* __restrict__ chunk_gsum, uint32_t* __restrict__ chunk_base,
-           float* __restrict__ seg_s, uint32_t* __restrict__ seg_nsurv,
-           uint64_t* __restrict__ seg_eoff, uint64_t* __restrict__ seg_sbase,
-           uint8_t* __restrict__ msg) {
-    __shared__ uint64_t lsz[4], lns[4];
+k_chunk_scan(const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ tile_cnt,
+             const double* __restrict__ tile_gsum, uint32_t* __restrict__ tile_off,
+             uint32_t* __restrict__ chunk_cnt, double* __restrict__ chunk_gsum) {
+    __shared__ uint32_t lw[4];
+    __shared__ double lg[4];
+    chunk_scan_block(blockIdx.x, chunk_tile_begin, tile_cnt, tile_gsum, tile_off, chunk_cnt,
+                     chunk_gsum, lw, lg);
+}
+
+// Finalize, by one block of 256 threads: s and survivor totals per segment,
+// chunk bases, entry regions, and (write_msg) the directory, header and
+// padding bytes of the message.  lsz, lns: 4 LDS words (64-bit) each.
+__device__ __forceinline__ void finalize_block(const SegDev* __restrict__ segs, uint32_t nseg,
+                                               uint32_t plan_hash, uint64_t entries_begin,
+                                               const uint32_t* __restrict__ chunk_cnt,
+                                               const double* __restrict__ chunk_gsum,
+                                               uint32_t* __restrict__ chunk_base,
+                                               float* __restrict__ seg_s,
+                                               uint32_t* __restrict__ seg_nsurv,
+                                               uint64_t* __restrict__ seg_eoff,
+                                               uint64_t* __restrict__ seg_sbase,
+                                               uint8_t* __restrict__ msg, uint64_t* lsz,
+                                               uint64_t* lns, bool write_msg = true) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // s and survivor totals per segment; chunk bases within the segment.
     for (uint32_t l = tid; l < nseg; l += 256) {
@@ -102,7 +161,8 @@ k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
         seg_nsurv[l] = run;
         // Zero the padding after the count region.
         const uint64_t cend = sg.count_off + uint64_t(sg.nbins) * sg.wb;
-        for (uint64_t p = cend; p < rup16(cend); ++p) msg[p] = 0;
+        if (write_msg)
+            for (uint64_t p = cend; p < rup16(cend); ++p) msg[p] = 0;
     }
     __syncthreads();
     // Entry regions in table order, each 16-byte aligned, and the number of
@@ -136,17 +196,19 @@ k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
             const uint64_t eoff = entries_begin + carry + bsz + isz - sz;
             seg_eoff[l] = eoff;
             seg_sbase[l] = surv + bns + ins - ns;
-            uint8_t* d = msg + 32 + 16 * uint64_t(l);
-            *reinterpret_cast<float*>(d) = seg_s[l];
-            *reinterpret_cast<uint32_t*>(d + 4) = uint32_t(ns);
-            *reinterpret_cast<uint64_t*>(d + 8) = eoff;
-            const uint64_t wend = eoff + ns * segs[l].wb;
-            for (uint64_t p = wend; p < eoff + sz; ++p) msg[p] = 0;
+            if (write_msg) {
+                uint8_t* d = msg + 32 + 16 * uint64_t(l);
+                *reinterpret_cast<float*>(d) = seg_s[l];
+                *reinterpret_cast<uint32_t*>(d + 4) = uint32_t(ns);
+                *reinterpret_cast<uint64_t*>(d + 8) = eoff;
+                const uint64_t wend = eoff + ns * segs[l].wb;
+                for (uint64_t p = wend; p < eoff + sz; ++p) msg[p] = 0;
+            }
         }
         carry += asz;
         surv += ans;
     }
-    if (tid == 0) {
+    if (tid == 0 && write_msg) {
         *reinterpret_cast<uint32_t*>(msg) = 0x43414441u;
         *reinterpret_cast<uint16_t*>(msg + 4) = 1;
         *reinterpret_cast<uint16_t*>(msg + 6) = 0;
@@ -154,8 +216,20 @@ k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
         *reinterpret_cast<uint32_t*>(msg + 12) = plan_hash;
         *reinterpret_cast<uint64_t*>(msg + 16) = entries_begin + carry;
         *reinterpret_cast<uint64_t*>(msg + 24) = surv;
-        seg_sbase[nseg] = surv;
     }
+    if (tid == 0) seg_sbase[nseg] = surv;
+}
+
+__global__ void __launch_bounds__(256)
+k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
+           uint64_t entries_begin, const uint32_t* __restrict__ chunk_cnt,
+           const double* __restrict__ chunk_gsum, uint32_t* __restrict__ chunk_base,
+           float* __restrict__ seg_s, uint32_t* __restrict__ seg_nsurv,
+           uint64_t* __restrict__ seg_eoff, uint64_t* __restrict__ seg_sbase,
+           uint8_t* __restrict__ msg) {
+    __shared__ uint64_t lsz[4], lns[4];
+    finalize_block(segs, nseg, plan_hash, entries_begin, chunk_cnt, chunk_gsum, chunk_base, seg_s,
+                   seg_nsurv, seg_eoff, seg_sbase, msg, lsz, lns);
 }
 
 // Encode + residue fix-up, balanced over survivors.  The survivors of the
@@ -195,15 +269,19 @@ __device__ __forceinline__ uint32_t wave_last_le(uint32_t n, uint64_t x, Key key
     return lo;
 }
 
-__global__ void __launch_bounds__(256)
-k_encode(const SegDev* __restrict__ segs, uint32_t nseg, const uint32_t* __restrict__ tile_seg,
-         const uint2* __restrict__ stage, const uint32_t* __restrict__ tile_cnt,
-         const uint32_t* __restrict__ tile_off, const uint32_t* __restrict__ chunk_base,
-         const float* __restrict__ seg_s, const uint64_t* __restrict__ seg_eoff,
-         const uint64_t* __restrict__ seg_sbase, uint8_t* __restrict__ msg,
-         float* __restrict__ residue, uint32_t ntiles) {
+// Wavefront w of W: its share of the survivors (wavefront-uniform arguments).
+__device__ __forceinline__ void encode_wave(uint32_t w, uint32_t W, const SegDev* __restrict__ segs,
+                                            uint32_t nseg, const uint32_t* __restrict__ tile_seg,
+                                            const uint2* __restrict__ stage,
+                                            const uint32_t* __restrict__ tile_cnt,
+                                            const uint32_t* __restrict__ tile_off,
+                                            const uint32_t* __restrict__ chunk_base,
+                                            const float* __restrict__ seg_s,
+                                            const uint64_t* __restrict__ seg_eoff,
+                                            const uint64_t* __restrict__ seg_sbase,
+                                            uint8_t* __restrict__ msg, float* __restrict__ residue,
+                                            uint32_t ntiles) {
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t W = gridDim.x * 4u, w = blockIdx.x * 4u + (threadIdx.x >> 6);
     const uint64_t S = seg_sbase[nseg];
     const uint64_t a = S * w / W, b = S * (w + 1) / W;
     if (a >= b) return;   // wavefront-uniform
@@ -300,6 +378,17 @@ k_encode(const SegDev* __restrict__ segs, uint32_t nseg, const uint32_t* __restr
         tile0 += 64u;
         r0 = 0;
     }
+}
+
+__global__ void __launch_bounds__(256)
+k_encode(const SegDev* __restrict__ segs, uint32_t nseg, const uint32_t* __restrict__ tile_seg,
+         const uint2* __restrict__ stage, const uint32_t* __restrict__ tile_cnt,
+         const uint32_t* __restrict__ tile_off, const uint32_t* __restrict__ chunk_base,
+         const float* __restrict__ seg_s, const uint64_t* __restrict__ seg_eoff,
+         const uint64_t* __restrict__ seg_sbase, uint8_t* __restrict__ msg,
+         float* __restrict__ residue, uint32_t ntiles) {
+    encode_wave(blockIdx.x * 4u + (threadIdx.x >> 6), gridDim.x * 4u, segs, nseg, tile_seg, stage,
+                tile_cnt, tile_off, chunk_base, seg_s, seg_eoff, seg_sbase, msg, residue, ntiles);
 }
 
 }  // namespace adacomp

@@ -9,10 +9,12 @@
 // moved), so the kernels are built around coalesced 16-byte accesses, whole
 // bins per workgroup and compaction in LDS; no matrix cores are involved.
 //
-// The kernels live in common.hpp (shared helpers), tile_pass.hpp, encode.hpp
-// and decode.hpp; this header includes them all.
+// The kernels live in common.hpp (shared helpers), tile_pass.hpp, encode.hpp,
+// small_table.hpp and decode.hpp; this header includes them all.
 //
-// Compress, per call, four stream-ordered launches:
+// Compress, per call, four stream-ordered launches (small tables: the tile
+// pass and one finish kernel that does the work of the last three, see
+// small_table.hpp):
 //   tile pass   (dense, one workgroup per tile of whole bins; bins longer than
 //               4093 elements one per workgroup, streamed twice): reads residue
 //               and dW once as float4, forms G and H, bin maxima by a
@@ -37,4 +39,5 @@
 #include "common.hpp"
 #include "tile_pass.hpp"
 #include "encode.hpp"
+#include "small_table.hpp"
 #include "decode.hpp"

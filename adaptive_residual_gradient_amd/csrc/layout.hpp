@@ -178,7 +178,9 @@ struct Layout {
     uint64_t span = 0;   // max(offset + numel) rounded up to 4: the flat buffers' minimum length
     uint64_t counts_begin = 0, entries_begin = 0, capacity = 0;
 
-    // Compress workspace (byte offsets).
+    // Compress workspace (byte offsets).  ws_sync: the single-launch path's
+    // ticket word, in a slot of its own that no other kernel writes.
+    uint64_t ws_sync = 0;
     uint64_t ws_stage = 0, ws_tile_cnt = 0, ws_tile_gsum = 0, ws_tile_off = 0;
     uint64_t ws_chunk_cnt = 0, ws_chunk_gsum = 0, ws_chunk_base = 0;
     uint64_t ws_seg_s = 0, ws_seg_nsurv = 0, ws_seg_eoff = 0, ws_seg_sbase = 0, ws_compress = 0;
@@ -325,6 +327,7 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
         w = round_up(w + bytes, kAlign);
         return at;
     };
+    L.ws_sync = take(8);
     L.ws_stage = take(8 * L.span);     // (key, G) pair per possible survivor
     L.ws_tile_cnt = take(4 * tiles);
     L.ws_tile_gsum = take(8 * tiles);
@@ -370,7 +373,55 @@ inline std::vector<DecDesc> decode_descs(const Layout& L, int v) {
     return out;
 }
 
-inline void fill_info(const Layout& L, adacomp_plan_info* info) {
+// LDS bytes of the small-table finish for T tiles, C scan chunks and S
+// segments: per tile a double and three words (plus one total), per chunk a
+// double and three words (plus one), per segment two 64-bit and four 32-bit
+// words (plus one 64-bit total).
+ADACOMP_HD constexpr uint64_t small_lds_bytes(uint64_t T, uint64_t C, uint64_t S) {
+    return 8 * T + 4 * (T + 1) + 8 * T + 8 * C + 4 * (C + 1) + 8 * C + 16 * S + 8 + 16 * S;
+}
+constexpr uint64_t kSmallLdsMax = 65536;
+// A tile that is not its segment's last holds at least 1023 elements
+// (bins_per_tile), so a table within the span limit has at most
+// span / 1000 + nseg tiles and nseg + tiles / 1024 scan chunks: its tables
+// always fit.
+constexpr uint64_t kSmallMaxTiles = ADACOMP_SMALL_TABLE_MAX_SPAN / 1000 + ADACOMP_SMALL_TABLE_MAX_SEGMENTS;
+static_assert(small_lds_bytes(kSmallMaxTiles, ADACOMP_SMALL_TABLE_MAX_SEGMENTS + kSmallMaxTiles / 1024 + 1,
+                              ADACOMP_SMALL_TABLE_MAX_SEGMENTS) <= kSmallLdsMax,
+              "small tables: the finish's tables fit the LDS budget");
+// Tables whose compress ends with k_finish_small (and may take the single
+// launch): small span, few segments; the LDS tables and the 16-bit ticket
+// count are checked as well.
+inline bool small_table_fits(const Layout& L) {
+    return L.ct.ntiles >= 1 && L.ct.ntiles < 65536 && L.nseg <= ADACOMP_SMALL_TABLE_MAX_SEGMENTS &&
+           L.span <= ADACOMP_SMALL_TABLE_MAX_SPAN &&
+           small_lds_bytes(L.ct.ntiles, L.ct.nchunks, L.nseg) <= kSmallLdsMax;
+}
+// The single launch also needs every bin held in registers (tile shapes 0, 1).
+inline bool single_launch_fits(const Layout& L) {
+    return small_table_fits(L) && L.ct.by_variant[2].empty() &&
+           L.ct.by_variant[0].size() + L.ct.by_variant[1].size() == L.ct.ntiles;
+}
+
+// How a plan compresses.
+enum class Finish { kSeparate, kSmall, kSingle };
+
+// The finish a plan made with plan_flags uses (flags already validated).
+inline Finish choose_finish(const Layout& L, uint32_t plan_flags) {
+    if ((plan_flags & ADACOMP_PLAN_SINGLE_LAUNCH) != 0u && single_launch_fits(L)) return Finish::kSingle;
+    if ((plan_flags & ADACOMP_PLAN_SEPARATE_FINISH) == 0u && small_table_fits(L)) return Finish::kSmall;
+    return Finish::kSeparate;
+}
+
+// Kernel launches of one compress call.
+inline uint64_t compress_launches(const Layout& L, Finish f) {
+    if (f == Finish::kSingle) return 1;
+    uint64_t n = f == Finish::kSmall ? 1 : 3;   // finish kernels
+    for (int v = 0; v < kVariants; ++v) n += L.ct.by_variant[v].empty() ? 0 : 1;
+    return n;
+}
+
+inline void fill_info(const Layout& L, Finish f, adacomp_plan_info* info) {
     info->nseg = L.nseg;
     info->plan_hash = L.plan_hash;
     info->total_numel = L.total_numel;
@@ -382,6 +433,7 @@ inline void fill_info(const Layout& L, adacomp_plan_info* info) {
     info->compress_workspace_bytes = L.ws_compress;
     info->decode_workspace_bytes_per_message = L.dws_per_msg;
     info->decode_workspace_bytes_fixed = L.dws_fixed;
+    info->compress_launches = compress_launches(L, f);
 }
 
 }  // namespace adacomp

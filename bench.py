@@ -166,6 +166,46 @@ def measure_decode_sgd(A, plan, msgs, n_alloc, N, K, dev):
             "fused_adam_GBps": round((mbytes + 24.0 * N) / (t_a * 1e-3) / 1e9, 1)}
 
 
+def measure_small_table(A, W, dev):
+    """The 100 x 1000 layer (L_T 500), launch-latency bound: one compress call
+    per step over its 10 seeded gradients, timed per call with events
+    (median of 100 calls) and back to back (mean of 500), for each finish:
+    the default small-table finish (tile pass + one finish kernel), the
+    three-kernel finish and the single launch."""
+    import time
+
+    import torch
+    wl = W.workload("fc")
+    n = W.alloc_len(wl)
+    dws = [W.make_dw(wl, 0, s, dev) for s in range(1, wl.steps + 1)]
+    out = {"workload": "fc_100x1000", "elements": wl.numel}
+    for label, flags in (("default", 0), ("separate_finish", A.PLAN_SEPARATE_FINISH),
+                         ("single_launch", A.PLAN_SINGLE_LAUNCH)):
+        plan = A.Plan(wl.segments, plan_flags=flags)
+        msg, ws = plan.message_buffer(dev), plan.compress_workspace(dev)
+        r = torch.zeros(n, dtype=torch.float32, device=dev)
+        for i in range(20):
+            A.compress(plan, r, dws[i % len(dws)], msg, ws)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(100)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            A.compress(plan, r, dws[i % len(dws)], msg, ws)
+            b.record()
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        t0 = time.perf_counter()
+        for i in range(500):
+            A.compress(plan, r, dws[i % len(dws)], msg, ws)
+        torch.cuda.synchronize()
+        b2b = (time.perf_counter() - t0) * 1e6 / 500
+        out[label] = {"launches": int(plan.info.compress_launches), "call_us": round(per[50], 2),
+                      "back_to_back_us": round(b2b, 2)}
+        plan.close()
+    return out
+
+
 def lt_sweep(args):
     """Bin-length sweep (not the default run): the same 64 x 4096 x 4096
     layers and the same gradient stream compressed with L_T = 50, 500 and 5000
@@ -258,6 +298,9 @@ def main():
     ap.add_argument("--lt-sweep", action="store_true",
                     help="instead of the benchmark, compress the workload with L_T = 50, 500 "
                          "and 5000 and print one JSON line per bin length")
+    ap.add_argument("--small-table", action="store_true",
+                    help="instead of the benchmark, time the compress of the 100 x 1000 layer "
+                         "with each finish (default, three-kernel, single launch); one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device copy of 1 GiB (a known-size reference "
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -269,6 +312,15 @@ def main():
         sys.exit(2)
     if args.lt_sweep:
         lt_sweep(args)
+        return
+    if args.small_table:
+        import torch
+
+        import adaptive_residual_gradient_amd as A
+        import workloads as W
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        print(json.dumps(measure_small_table(A, W, dev)), flush=True)
         return
 
     import numpy as np
@@ -384,6 +436,7 @@ def main():
     }
     timer.close()
     res["decode_sgd"] = measure_decode_sgd(A, plan, learner_msgs, n_alloc, N, K, dev)
+    res["small_table"] = measure_small_table(A, W, dev)
 
     if not args.no_cpu_baseline:
         def host_dw(step_idx, length):

@@ -104,6 +104,7 @@ typedef struct adacomp_plan_info {
     uint64_t compress_workspace_bytes;
     uint64_t decode_workspace_bytes_per_message;
     uint64_t decode_workspace_bytes_fixed; /* decode ws for K messages = fixed + K * per_message */
+    uint64_t compress_launches;         /* kernel launches of one adacomp_compress call */
 } adacomp_plan_info;
 
 typedef struct adacomp_plan adacomp_plan;   /* opaque, immutable once created */
@@ -116,8 +117,35 @@ int adacomp_plan_query(const adacomp_segment* segs, uint32_t nseg, adacomp_plan_
 /* Validate the table, build the work tiles and copy the small tile tables to
  * the current device.  The plan owns that device memory until
  * adacomp_plan_destroy.  An immutable plan may be used from several streams
- * at once (with separate buffers). */
+ * at once (with separate buffers).
+ *
+ * Compress is one tile-pass launch per tile shape used (bins up to 2045,
+ * up to 4093, longer), then the finish: survivor offsets, s, header and
+ * directory, entry words and residue of the sent elements.  For a small
+ * table -- span <= ADACOMP_SMALL_TABLE_MAX_SPAN elements and at most
+ * ADACOMP_SMALL_TABLE_MAX_SEGMENTS segments -- the finish is one launch
+ * whose every workgroup holds the table's tile counts in LDS; otherwise it is
+ * three (chunk scan, finalize, encode).  info.compress_launches reports the
+ * total.  Every path writes the same bytes.  plan_query reports the sizes of
+ * a plan made with no flags. */
+#define ADACOMP_SMALL_TABLE_MAX_SPAN (1u << 21)
+#define ADACOMP_SMALL_TABLE_MAX_SEGMENTS 256u
 int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan** plan);
+
+/* Plan flags (adacomp_plan_create_ex).
+ * SEPARATE_FINISH: finish with the three kernels even for a small table.
+ * SINGLE_LAUNCH: compress a small table whose bins are all <= 4093 in one
+ *   launch: the workgroup that finishes its tile last completes the message
+ *   alone.  Correct, but slower on MI355X than the default (the release of
+ *   every tile and one CU's scattered stores cost more than the launches it
+ *   saves); built for comparison.  Other tables ignore it.
+ * The two flags are exclusive. */
+#define ADACOMP_PLAN_SEPARATE_FINISH 1u
+#define ADACOMP_PLAN_SINGLE_LAUNCH 2u
+/* adacomp_plan_create with plan flags (0, or one of the above; any other
+ * value is ADACOMP_ERR_INVALID_ARGUMENT). */
+int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t plan_flags,
+                           adacomp_plan** plan);
 int adacomp_plan_destroy(adacomp_plan* plan);
 int adacomp_plan_get_info(const adacomp_plan* plan, adacomp_plan_info* info);
 
@@ -128,7 +156,11 @@ int adacomp_plan_get_info(const adacomp_plan* plan, adacomp_plan_info* info);
  *   msg      message output, msg_bytes >= info.message_capacity.  Its length
  *            is the header's total_bytes (read it after the stream syncs).
  *   ws       workspace, ws_bytes >= info.compress_workspace_bytes; no
- *            initial contents required, contents undefined afterwards.
+ *            initial contents required, contents undefined afterwards, except
+ *            that with ADACOMP_PLAN_SINGLE_LAUNCH its first 8 bytes hold a
+ *            ticket counter: a 48-bit tag above a 16-bit count, left with
+ *            count 0.  Any other initial value is accepted; only the tag with
+ *            a nonzero count (a call stopped part way) would miscount.
  *   bin_max_out  nullable device float32[total_bins]: every g_max, segments
  *            in table order, bins in order (a testing aid).
  * Determinism: s is the bin maxima summed in float64 in a fixed order, divided
@@ -233,7 +265,9 @@ int adacomp_decode_adam_timed(const adacomp_plan* plan, const void* const* msgs,
 #define ADACOMP_STAGE_DECODE_COUNT 4
 #define ADACOMP_STAGE_DECODE_BASE 5
 #define ADACOMP_STAGE_DECODE_APPLY 6
-#define ADACOMP_STAGE_COMPRESS_CALL 7  /* a whole adacomp_compress call, gaps between kernels included */
+#define ADACOMP_STAGE_COMPRESS_CALL 7  /* a whole adacomp_compress call, gaps between kernels included
+                                          (a small-table finish is recorded under stage 3, a single
+                                          launch only here) */
 #define ADACOMP_STAGE_DECODE_CALL 8    /* a whole adacomp_decode_accumulate call */
 #define ADACOMP_STAGE_DECODE_SGD_CALL 9  /* a whole adacomp_decode_sgd call (its kernels: stages 4-6) */
 #define ADACOMP_STAGE_DECODE_ADAM_CALL 10 /* a whole adacomp_decode_adam call (its kernels: stages 4-6) */

@@ -24,8 +24,15 @@ int main(void) {
     if (info.nseg != 3 || info.total_numel != 104100 || info.span != 104104) return fail("info sizes");
     if (info.total_bins != 200 + 82 + 1) return fail("total_bins");
     if (info.header_bytes != 32 + 16 * 3) return fail("header_bytes");
-    printf("OK plan_query nseg=%u bins=%llu capacity=%llu\n", info.nseg,
-           (unsigned long long)info.total_bins, (unsigned long long)info.message_capacity);
+    /* shapes 0 (L_T 500, 50) and 2 (L_T 32768): two tile passes, one finish */
+    if (info.compress_launches != 3) return fail("compress_launches");
+    printf("OK plan_query nseg=%u bins=%llu capacity=%llu launches=%llu\n", info.nseg,
+           (unsigned long long)info.total_bins, (unsigned long long)info.message_capacity,
+           (unsigned long long)info.compress_launches);
+    adacomp_plan* plan = NULL;
+    if (adacomp_plan_create_ex(segs, 3, ADACOMP_PLAN_SEPARATE_FINISH | ADACOMP_PLAN_SINGLE_LAUNCH,
+                               &plan) != ADACOMP_ERR_INVALID_ARGUMENT || plan != NULL)
+        return fail("exclusive plan flags");
     segs[1].flags = 2;
     if (adacomp_plan_query(segs, 3, &info) != ADACOMP_ERR_INVALID_ARGUMENT) return fail("flags 2");
     segs[1].flags = 0;

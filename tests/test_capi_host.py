@@ -90,6 +90,29 @@ def test_ls_flag_enters_plan_hash():
     assert info.message_capacity == oracle.message_capacity(segs)
 
 
+def test_compress_launches_rule():
+    """Tables of span <= 2^21 and <= 256 segments finish in one launch after
+    one tile-pass launch per tile shape; others in three."""
+    launches = {name: A.plan_query(W.workload(name).segments).compress_launches
+                for name in W.WORKLOADS}
+    assert launches == {"fc": 2, "conv": 4, "fc_lstm": 4, "resnet50": 4, "large": 4}
+    assert A.plan_query([(0, 1 << 21, 500)]).compress_launches == 2
+    assert A.plan_query([(0, (1 << 21) + 4, 500)]).compress_launches == 4
+    assert A.plan_query([(4 * i, 4, 4) for i in range(256)]).compress_launches == 2
+    assert A.plan_query([(4 * i, 4, 4) for i in range(257)]).compress_launches == 4
+    # three tile shapes (L_T 50, 4093, 5000): three tile-pass launches
+    assert A.plan_query([(0, 1000, 50), (1000, 8186, 4093), (9188, 10000, 5000)]).compress_launches == 4
+
+
+def test_plan_flags_rejected_before_any_device_call():
+    L = A.lib()
+    arr, n = A._segments([(0, 1000, 50)])
+    h = ctypes.c_void_p()
+    for flags in (3, 4, 0x80000000):
+        assert L.adacomp_plan_create_ex(arr, n, flags, ctypes.byref(h)) == -1
+        assert h.value is None
+
+
 def test_null_plan_calls_fail_cleanly():
     L = A.lib()
     assert L.adacomp_compress(None, None, None, 0, None, 0, None, 0, None, None) == -1

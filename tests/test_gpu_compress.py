@@ -77,8 +77,14 @@ EDGE_BINS = [1, 2, 3, 4, 5, 7, 50, 63, 64, 65, 500, 4093, 4094, 5000, 32767, 327
 EDGE_NUMEL = [1, 2, 3, 5, 7, 63, 65, 4093, 4097, 36861, 40003]
 
 
-@pytest.mark.parametrize("lt", EDGE_BINS)
-def test_edge_bin_lengths(lt):
+# Tables this small finish with one kernel by default; they also run with the
+# three-kernel finish and (bins held in registers, L_T <= 4093) in one launch.
+EDGE_CASES = ([(lt, 0) for lt in EDGE_BINS] + [(lt, A.PLAN_SEPARATE_FINISH) for lt in EDGE_BINS] +
+              [(lt, A.PLAN_SINGLE_LAUNCH) for lt in EDGE_BINS if lt <= 4093])
+
+
+@pytest.mark.parametrize("lt,plan_flags", EDGE_CASES)
+def test_edge_bin_lengths(lt, plan_flags):
     """Every bin length class (per-element path L_T < 4, two-run path, 8/16-bit
     switch at 64, register tiles / streamed long bins at 4093/4094, the 16-bit
     maximum), ragged last bins, tiny segments, gaps between segments, ties
@@ -89,7 +95,8 @@ def test_edge_bin_lengths(lt):
         segs.append((off, n, lt))
         off += (n + 3) // 4 * 4 + 8
     span = off + 4
-    plan = A.Plan(segs)
+    plan = A.Plan(segs, plan_flags=plan_flags)
+    say(f"  L_T={lt}: {plan.info.compress_launches} compress launches")
     msg, ws = plan.message_buffer(DEV), plan.compress_workspace(DEV)
     gmax = torch.empty(int(plan.info.total_bins), dtype=torch.float32, device=DEV)
     for kind in ("normal", "ties"):
@@ -374,9 +381,13 @@ def test_argument_errors():
     plan.close()
 
 
-def test_timer_reports_every_stage():
+@pytest.mark.parametrize("plan_flags", [A.PLAN_SEPARATE_FINISH, 0, A.PLAN_SINGLE_LAUNCH])
+def test_timer_reports_every_stage(plan_flags):
+    """The three-kernel finish reports its four kernels and the whole call;
+    the small-table finish the tile pass, its one finish kernel (as the
+    encode stage) and the call; the single launch only the call."""
     wl = W.workload("fc")
-    plan = A.Plan(wl.segments)
+    plan = A.Plan(wl.segments, plan_flags=plan_flags)
     r = torch.zeros(W.alloc_len(wl), dtype=torch.float32, device=DEV)
     d = W.make_dw(wl, 0, 1, DEV)
     msg, ws = plan.message_buffer(DEV), plan.compress_workspace(DEV)
@@ -384,9 +395,16 @@ def test_timer_reports_every_stage():
     for _ in range(3):
         A.compress(plan, r, d, msg, ws, timer=t)
     rd = t.read()
-    for st in ("tile_pass", "chunk_scan", "finalize", "encode", "compress_call"):
-        assert rd[st][1] == 3 and rd[st][0] > 0
-    parts = sum(rd[st][0] for st in ("tile_pass", "chunk_scan", "finalize", "encode"))
+    kernels = ("tile_pass", "chunk_scan", "finalize", "encode")
+    recorded = {A.PLAN_SEPARATE_FINISH: kernels, 0: ("tile_pass", "encode"),
+                A.PLAN_SINGLE_LAUNCH: ()}[plan_flags]
+    assert rd["compress_call"][1] == 3 and rd["compress_call"][0] > 0
+    for st in kernels:
+        if st in recorded:
+            assert rd[st][1] == 3 and rd[st][0] > 0
+        else:
+            assert rd[st][1] == 0 and rd[st][0] == 0
+    parts = sum(rd[st][0] for st in kernels)
     assert rd["compress_call"][0] >= 0.9 * parts
     t.close()
     plan.close()

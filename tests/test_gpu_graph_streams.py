@@ -21,13 +21,19 @@ def say(*a):
     sys.stdout.flush()
 
 
-def test_compress_and_decode_in_a_graph():
+@pytest.mark.parametrize("name,flags,launches", [("conv", 0, 4), ("fc", 0, 2),
+                                                  ("fc", A.PLAN_SINGLE_LAUNCH, 1)])
+def test_compress_and_decode_in_a_graph(name, flags, launches):
     """compress then decode_accumulate captured once and replayed five times
     on new gradients (copied into the captured input buffer between replays,
     with eager work and synchronisations in between); every replay's residue,
-    message and decoded sum equal the eager calls'."""
-    wl = W.workload("conv")
-    plan = A.Plan(wl.segments)
+    message and decoded sum equal the eager calls'.  The 100x1000 table takes
+    the small-table finish (or, with its flag, the single launch, whose
+    ticket word lives in the captured workspace), the conv table the
+    three-kernel one."""
+    wl = W.workload(name)
+    plan = A.Plan(wl.segments, plan_flags=flags)
+    assert plan.info.compress_launches == launches
     n = W.alloc_len(wl)
     msg, ws = plan.message_buffer(DEV), plan.compress_workspace(DEV)
     dws = plan.decode_workspace(1, DEV)
@@ -68,12 +74,15 @@ def test_compress_and_decode_in_a_graph():
     plan.close()
 
 
-def test_one_plan_on_two_streams():
+@pytest.mark.parametrize("name,launches", [("fc_lstm", 4), ("fc", 2)])
+def test_one_plan_on_two_streams(name, launches):
     """Two learners compress with one shared plan on two streams at once (each
     with its own buffers), then decode on the two streams; results equal the
-    same calls made one after the other."""
-    wl = W.workload("fc_lstm")
+    same calls made one after the other (the 100x1000 table with the
+    small-table finish, fc_lstm with the three-kernel one)."""
+    wl = W.workload(name)
     plan = A.Plan(wl.segments)
+    assert plan.info.compress_launches == launches
     n = W.alloc_len(wl)
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     bufs = []
