@@ -298,6 +298,9 @@ def main():
     ap.add_argument("--lt-sweep", action="store_true",
                     help="instead of the benchmark, compress the workload with L_T = 50, 500 "
                          "and 5000 and print one JSON line per bin length")
+    ap.add_argument("--no-small-table", action="store_true",
+                    help="leave the small-table timing out of the default run (profiling runs that "
+                         "select the benchmark's own tile-pass dispatches by order)")
     ap.add_argument("--small-table", action="store_true",
                     help="instead of the benchmark, time the compress of the 100 x 1000 layer "
                          "with each finish (default, three-kernel, single launch); one JSON line")
@@ -436,7 +439,7 @@ def main():
     }
     timer.close()
     res["decode_sgd"] = measure_decode_sgd(A, plan, learner_msgs, n_alloc, N, K, dev)
-    res["small_table"] = measure_small_table(A, W, dev)
+    res["small_table"] = None if args.no_small_table else measure_small_table(A, W, dev)
 
     if not args.no_cpu_baseline:
         def host_dw(step_idx, length):
