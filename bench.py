@@ -206,6 +206,43 @@ def measure_small_table(A, W, dev):
     return out
 
 
+def measure_other_workloads(A, W, dev):
+    """The three other parity workloads at full size (context; the metric is
+    the 1.07e9-element workload's): each runs its first 10 steps from zero
+    residue on its own seeded gradients, all resident before timing; steps
+    6-10 are timed one call at a time with events (median)."""
+    import torch
+    out = {}
+    for name in ("conv", "fc_lstm", "resnet50"):
+        wl = W.workload(name)
+        n = W.alloc_len(wl)
+        plan = A.Plan(wl.segments)
+        dws = [W.make_dw(wl, 0, s, dev) for s in range(1, 11)]
+        msg, ws = plan.message_buffer(dev), plan.compress_workspace(dev)
+        r = torch.zeros(n, dtype=torch.float32, device=dev)
+        times = []
+        for s, d in enumerate(dws):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            A.compress(plan, r, d, msg, ws)
+            b.record()
+            torch.cuda.synchronize()
+            if s >= 5:
+                times.append(a.elapsed_time(b))
+        t = sorted(times)[len(times) // 2]
+        total, surv, _ = A.message_header(plan, msg)
+        out[wl.name] = {"elements": wl.numel, "layers": len(wl.segments),
+                        "compress_launches": int(plan.info.compress_launches),
+                        "compress_us": round(t * 1e3, 1),
+                        "Gelem_per_s": round(wl.numel / (t * 1e-3) / 1e9, 1),
+                        "GBps": round((12.0 * wl.numel + total) / (t * 1e-3) / 1e9, 1),
+                        "survivors_step10": int(surv)}
+        plan.close()
+        del dws, r, msg, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def lt_sweep(args):
     """Bin-length sweep (not the default run): the same 64 x 4096 x 4096
     layers and the same gradient stream compressed with L_T = 50, 500 and 5000
@@ -299,8 +336,8 @@ def main():
                     help="instead of the benchmark, compress the workload with L_T = 50, 500 "
                          "and 5000 and print one JSON line per bin length")
     ap.add_argument("--no-small-table", action="store_true",
-                    help="leave the small-table timing out of the default run (profiling runs that "
-                         "select the benchmark's own tile-pass dispatches by order)")
+                    help="leave the small-table and other-workload timings out of the default run "
+                         "(profiling runs that select the benchmark's own tile-pass dispatches by order)")
     ap.add_argument("--small-table", action="store_true",
                     help="instead of the benchmark, time the compress of the 100 x 1000 layer "
                          "with each finish (default, three-kernel, single launch); one JSON line")
@@ -440,6 +477,7 @@ def main():
     timer.close()
     res["decode_sgd"] = measure_decode_sgd(A, plan, learner_msgs, n_alloc, N, K, dev)
     res["small_table"] = None if args.no_small_table else measure_small_table(A, W, dev)
+    res["other_workloads"] = None if args.no_small_table else measure_other_workloads(A, W, dev)
 
     if not args.no_cpu_baseline:
         def host_dw(step_idx, length):
