@@ -432,6 +432,7 @@ def main():
 
     # Message of the last timed step (for the compression ratio).
     total, surv, dirs = A.message_header(plan, msg)
+    bin_lens = sorted({int(seg[2]) for seg in wl.segments})
     pr, wr, _, _ = stats.message_ratios(wl.segments, bytes(msg[: int(info.header_bytes)].cpu().numpy()))
 
     ms = {k: v[0] / max(v[1], 1) for k, v in st.items()}
@@ -458,8 +459,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": len(wl.segments), "numel": N,
-                   "bin_len": 500, "index_bits": 16, "decode_messages": K,
-                   "learner_steps": args.learner_steps},
+                   "bin_len": bin_lens[0] if len(bin_lens) == 1 else bin_lens,
+                   "index_bits": sorted({8 if b < 64 else 16 for b in bin_lens}) if len(bin_lens) > 1
+                   else (8 if bin_lens[0] < 64 else 16),
+                   "decode_messages": K, "learner_steps": args.learner_steps},
         "roofline": {"bound": "hbm", "kernel": "tile_pass",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -44,6 +44,25 @@ def test_exports_every_declared_function():
     assert set(names) <= exported
 
 
+def test_binding_constants_match_the_header():
+    text = HEADER.read_text()
+
+    def macro(name):   # "N", "Nu" or "(Au << B)"
+        m = re.search(r"#define\s+" + name + r"\s+(?:\((\d+)u?\s*<<\s*(\d+)\)|(\d+)u?)\b", text)
+        assert m, name
+        return int(m.group(1)) << int(m.group(2)) if m.group(1) else int(m.group(3))
+
+    assert macro("ADACOMP_SEG_LS") == A.SEG_LS
+    assert macro("ADACOMP_PLAN_SEPARATE_FINISH") == A.PLAN_SEPARATE_FINISH
+    assert macro("ADACOMP_PLAN_SINGLE_LAUNCH") == A.PLAN_SINGLE_LAUNCH
+    assert macro("ADACOMP_SMALL_TABLE_MAX_SPAN") == A.SMALL_TABLE_MAX_SPAN
+    assert macro("ADACOMP_SMALL_TABLE_MAX_SEGMENTS") == A.SMALL_TABLE_MAX_SEGMENTS
+    assert macro("ADACOMP_MAX_MESSAGES") == A.MAX_MESSAGES
+    assert macro("ADACOMP_MAX_BIN_LEN") == A.MAX_BIN_LEN
+    assert macro("ADACOMP_NUM_STAGES") == A.NUM_STAGES == len(A.STAGES)
+    assert ctypes.sizeof(A.PlanInfo) == 8 + 10 * 8
+
+
 def test_status_strings():
     for st in range(0, -8, -1):
         assert A.status_str(st) != "unknown status"
