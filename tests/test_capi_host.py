@@ -48,7 +48,7 @@ def test_binding_constants_match_the_header():
     text = HEADER.read_text()
 
     def macro(name):   # "N", "Nu" or "(Au << B)"
-        m = re.search(r"#define\s+" + name + r"\s+(?:\((\d+)u?\s*<<\s*(\d+)\)|(\d+)u?)\b", text)
+        m = re.search(r"#define\s+" + name + r"\s+(?:\((\d+)u?\s*<<\s*(\d+)\)|(\d+)u?\b)", text)
         assert m, name
         return int(m.group(1)) << int(m.group(2)) if m.group(1) else int(m.group(3))
 
