@@ -243,12 +243,17 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
     extern __shared__ uint64_t dyn64[];
     uint32_t* dyn = reinterpret_cast<uint32_t*>(dyn64);
     const uint32_t accw = LDS_ACC ? (acc_words + 1u) & ~1u : 0u;   // keep 8-byte alignment
-    uint64_t* eaddr = reinterpret_cast<uint64_t*>(dyn + accw);
+    uint64_t* mptr = reinterpret_cast<uint64_t*>(dyn + accw);   // [K] message, 0 if foreign
+    uint64_t* eaddr = mptr + K;
     float* ks = reinterpret_cast<float*>(eaddr + KG);
     uint32_t* wfk_all = reinterpret_cast<uint32_t*>(ks + K);   // [NW][KG + 1]
     uint32_t* pref = wfk_all + NW * (KG + 1);             // [KG][pstride]
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // Message addresses first: they do not depend on the descriptor, so the
+    // count words below wait for one round trip, not two.
+    for (uint32_t k = tid; k < K; k += THREADS)
+        mptr[k] = ws.dvalid[k] ? reinterpret_cast<uint64_t>(msgs.p[k]) : 0u;
     const DecDesc dd = descs[blockIdx.x];
     const uint64_t v0 = dd.t0 & ~uint64_t(3);
     const uint32_t lead = uint32_t(dd.t0 - v0);
@@ -300,23 +305,18 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
     for (uint32_t k0 = 0; k0 < K; k0 += KG) {
         const uint32_t kn = min(KG, K - k0);
         __syncthreads();   // bases staged; the previous group is done with pref
-        // Count words of the tile's bins for this group of messages (the
-        // message pointer and validity are read directly, not from LDS, so
-        // these loads wait only for the descriptor).
+        // Count words of the tile's bins for this group of messages (a
+        // foreign message counts nothing and is never read).
         for (uint32_t i = tid; i < kn * nb; i += THREADS) {
             const uint32_t kk = i / nb, b = i - kk * nb;
-            const uint32_t k = k0 + kk;
-            uint32_t cw = 0;
-            if (ws.dvalid[k])
-                cw = word_at(reinterpret_cast<uint64_t>(msgs.p[k]) + dd.count_at + uint64_t(b) * wb, wb);
-            pref[kk * pstride + b + 1] = cw;
+            const uint64_t mb = mptr[k0 + kk];
+            pref[kk * pstride + b + 1] = mb != 0u ? word_at(mb + dd.count_at + uint64_t(b) * wb, wb) : 0u;
         }
         if (tid < int(kn)) {
             const uint32_t k = k0 + tid;
             const uint64_t base = uint64_t(ws.dchunk_base[uint64_t(k) * DC + dd.chunk]) +
                                   ws.doff[uint64_t(k) * DT + dd.tile];
-            eaddr[tid] = reinterpret_cast<uint64_t>(msgs.p[k]) +
-                         ws.dseg_eoff[uint64_t(k) * nseg + dd.si] + base * wb;
+            eaddr[tid] = mptr[k] + ws.dseg_eoff[uint64_t(k) * nseg + dd.si] + base * wb;
         }
         __syncthreads();
         // Per-message exclusive prefix over the tile's bins.

@@ -149,13 +149,14 @@ constexpr int kDecVariants = 2;
 constexpr uint32_t kDecThreads[kDecVariants] = {256, 1024};
 
 // Dynamic LDS bytes of the decode apply kernel: the tile accumulator
-// (acc_words floats, rounded to even), per group message a u64 entry
-// address, per message s, the per-wavefront flat prefixes and the bin
-// prefixes of KG messages.
+// (acc_words floats, rounded to even), per message a u64 message address
+// (0 for a foreign message), per group message a u64 entry address, per
+// message s, the per-wavefront flat prefixes and the bin prefixes of KG
+// messages.
 inline uint32_t decode_lds_bytes(uint32_t acc_words, uint32_t K, uint32_t KG, uint32_t pstride,
                                  uint32_t nw) {
     const uint32_t accw = (acc_words + 1u) & ~1u;
-    return 4u * (accw + 2u * KG + K + nw * (KG + 1u) + KG * pstride);
+    return 4u * (accw + 2u * K + 2u * KG + K + nw * (KG + 1u) + KG * pstride);
 }
 
 // Messages per decode group: at most 64 (one wavefront lane each) and as many
