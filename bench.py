@@ -243,6 +243,59 @@ def measure_other_workloads(A, W, dev):
     return out
 
 
+def measure_ls(A, W, dev, wl, dws, n_alloc):
+    """Hard local selection (segment flag SEG_LS), after the timed steps:
+    (1) compress of the benchmark workload with every layer flagged, on the
+    benchmark's own resident gradients (steps 1-5 from zero residue; steps
+    3-5 timed one call at a time with events, median); (2) the residue
+    contrast the AIMech page's Mechanism claim "self-adjusting sparsity
+    prevents residual explosion" draws: the FC/LSTM workload for 50 steps
+    from zero residue under AdaComp and under LS on the same seeded
+    gradients, max |residue| after steps 1, 10, 20, 30, 40, 50."""
+    import torch
+    plan = A.Plan([(o, n, b, A.SEG_LS) for (o, n, b) in wl.segments])
+    msg, ws = plan.message_buffer(dev), plan.compress_workspace(dev)
+    r = torch.zeros(n_alloc, dtype=torch.float32, device=dev)
+    times = []
+    for i in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        A.compress(plan, r, dws[i % len(dws)], msg, ws)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(a.elapsed_time(b))
+    t = sorted(times)[1]
+    total, surv, _ = A.message_header(plan, msg)
+    out = {"workload": wl.name, "compress_ms": round(t, 4),
+           "Gelem_per_s": round(wl.numel / (t * 1e-3) / 1e9, 1),
+           "compress_frac_of_peak": round(12.0 * wl.numel / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "survivors_step5": int(surv)}
+    plan.close()
+    del r, msg, ws
+    torch.cuda.empty_cache()
+
+    demo = W.workload("fc_lstm")
+    n = W.alloc_len(demo)
+    growth = {}
+    for label, flag in (("adacomp", 0), ("ls", A.SEG_LS)):
+        plan = A.Plan([(o, k, b, flag) for (o, k, b) in demo.segments])
+        msg, ws = plan.message_buffer(dev), plan.compress_workspace(dev)
+        r = torch.zeros(n, dtype=torch.float32, device=dev)
+        d = torch.empty(n, dtype=torch.float32, device=dev)
+        trace = {}
+        for step in range(1, 51):
+            W.fill_dw(d, demo, 0, step)
+            A.compress(plan, r, d, msg, ws)
+            if step in (1, 10, 20, 30, 40, 50):
+                trace[step] = float(r.abs().max())
+        growth[label] = trace
+        plan.close()
+        del r, d, msg, ws
+    out["residue_growth"] = {"workload": demo.name, "max_abs_residue": growth}
+    return out
+
+
 def lt_sweep(args):
     """Bin-length sweep (not the default run): the same 64 x 4096 x 4096
     layers and the same gradient stream compressed with L_T = 50, 500 and 5000
@@ -336,7 +389,7 @@ def main():
                     help="instead of the benchmark, compress the workload with L_T = 50, 500 "
                          "and 5000 and print one JSON line per bin length")
     ap.add_argument("--no-small-table", action="store_true",
-                    help="leave the small-table and other-workload timings out of the default run "
+                    help="leave the small-table, other-workload and LS measurements out of the default run "
                          "(profiling runs that select the benchmark's own tile-pass dispatches by order)")
     ap.add_argument("--small-table", action="store_true",
                     help="instead of the benchmark, time the compress of the 100 x 1000 layer "
@@ -481,6 +534,7 @@ def main():
     res["decode_sgd"] = measure_decode_sgd(A, plan, learner_msgs, n_alloc, N, K, dev)
     res["small_table"] = None if args.no_small_table else measure_small_table(A, W, dev)
     res["other_workloads"] = None if args.no_small_table else measure_other_workloads(A, W, dev)
+    res["ls"] = None if args.no_small_table else measure_ls(A, W, dev, wl, dws, n_alloc)
 
     if not args.no_cpu_baseline:
         def host_dw(step_idx, length):
