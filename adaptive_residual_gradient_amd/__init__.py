@@ -27,10 +27,11 @@ STAGES = ("tile_pass", "chunk_scan", "finalize", "encode",
 MAX_MESSAGES = 256
 MAX_BIN_LEN = 32768
 SEG_LS = 1   # segment flag: hard local selection (see include/adacomp.h)
-PLAN_SEPARATE_FINISH = 1   # plan flag: finish with three kernels even for a small table
+PLAN_SEPARATE_FINISH = 1   # plan flag: finish with three kernels whatever the table
 PLAN_SINGLE_LAUNCH = 2     # plan flag: a small table in one launch (slower; for comparison)
 SMALL_TABLE_MAX_SPAN = 1 << 21     # tables up to this span and this many segments
 SMALL_TABLE_MAX_SEGMENTS = 256     # finish in one launch after the tile pass
+CHUNK_FINISH_MAX_TILES = 1 << 20   # larger tables of <= 256 segments and this many tiles: two
 
 
 class HipLibraryMissing(RuntimeError):

@@ -40,6 +40,7 @@ struct adacomp_plan {
     uint32_t* tile_t0 = nullptr;    // small-table finish: first element of each compress tile
     uint32_t small_lds_bytes = 0;   // k_finish_small's dynamic LDS
     uint32_t single_lds_bytes = 0;  // k_compress_single's: tile or finish tables, the larger
+    uint32_t chunk_lds_bytes = 0;   // k_finish_chunks' dynamic LDS
 };
 
 namespace adacomp {
@@ -270,7 +271,7 @@ int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t 
         }
         p->finish = adacomp::choose_finish(L, plan_flags);
         uint64_t o_t0 = 0;
-        if (p->finish != adacomp::Finish::kSeparate) {
+        if (adacomp::uses_small_tables(p->finish)) {
             std::vector<uint32_t> t0(L.ct.ntiles);
             for (uint64_t t = 0; t < L.ct.ntiles; ++t) {
                 const SegDev& sg = L.segs[L.ct.tile_seg[t]];
@@ -301,7 +302,7 @@ int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t 
         bind(p->ddt, od);
         for (int v = 0; v < adacomp::kDecVariants; ++v)
             p->ddesc[v] = reinterpret_cast<adacomp::DecDesc*>(base + o_desc[v]);
-        if (p->finish != adacomp::Finish::kSeparate)
+        if (adacomp::uses_small_tables(p->finish))
             p->tile_t0 = reinterpret_cast<uint32_t*>(base + o_t0);
         // Per tile: bin maxima, bin boundaries, and for hard local selection
         // the first index of each bin's maximum.
@@ -313,6 +314,8 @@ int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t 
             4 * std::max(L.ct.by_variant[0].empty() ? 0u : p->tile_lds_words[0],
                          L.ct.by_variant[1].empty() ? 0u : p->tile_lds_words[1]),
             p->small_lds_bytes);
+        p->chunk_lds_bytes = static_cast<uint32_t>(
+            adacomp::round_up(adacomp::chunk_finish_lds_bytes(L.ct.nchunks, L.nseg), 8));
         *out = p;
         return ADACOMP_OK;
     } catch (...) {
@@ -379,7 +382,7 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
 
     CallTimer tm(timer, stream, ADACOMP_STAGE_COMPRESS_CALL);
     adacomp::SmallArgs sa{};
-    if (plan->finish != adacomp::Finish::kSeparate) {
+    if (adacomp::uses_small_tables(plan->finish)) {
         sa.segs = plan->d_segs;
         sa.tile_seg = plan->dct.tile_seg;
         sa.tile_t0 = plan->tile_t0;
@@ -439,6 +442,29 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
                            chunk_cnt, chunk_gsum);
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.mark(ADACOMP_STAGE_CHUNK_SCAN);
+    }
+    if (plan->finish == adacomp::Finish::kChunks) {
+        adacomp::ChunkFinishArgs ca{};
+        ca.segs = plan->d_segs;
+        ca.tile_seg = plan->dct.tile_seg;
+        ca.stage = stage;
+        ca.tile_cnt = tile_cnt;
+        ca.tile_off = tile_off;
+        ca.chunk_cnt = chunk_cnt;
+        ca.chunk_gsum = chunk_gsum;
+        ca.msg = m8;
+        ca.residue = residue;
+        ca.entries_begin = L.entries_begin;
+        ca.nchunks = static_cast<uint32_t>(L.ct.nchunks);
+        ca.nseg = L.nseg;
+        ca.ntiles = static_cast<uint32_t>(L.ct.ntiles);
+        ca.plan_hash = L.plan_hash;
+        hipLaunchKernelGGL(adacomp::k_finish_chunks, dim3(encode_blocks(L)), dim3(256),
+                           plan->chunk_lds_bytes, stream, ca);
+        if ((st = launch_status()) != ADACOMP_OK) return st;
+        tm.mark(ADACOMP_STAGE_ENCODE);
+        tm.finish();
+        return ADACOMP_OK;
     }
     {
         hipLaunchKernelGGL(adacomp::k_finalize, dim3(1), dim3(256), 0, stream, plan->d_segs, L.nseg,

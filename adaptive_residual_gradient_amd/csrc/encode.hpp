@@ -391,4 +391,54 @@ k_encode(const SegDev* __restrict__ segs, uint32_t nseg, const uint32_t* __restr
                 tile_cnt, tile_off, chunk_base, seg_s, seg_eoff, seg_sbase, msg, residue, ntiles);
 }
 
+// ---------------------------------------------------------------------------
+// Finalize + encode in one kernel (tables whose scan-chunk and segment tables
+// fit in LDS): every workgroup loads the chunk survivor counts and sums of
+// bin maxima, runs the finalize step on LDS arrays (workgroup 0 also writes
+// the directory, header and padding) and encodes its share of the survivors
+// with the segment and chunk levels of the search in LDS.  Same functions,
+// same order as k_finalize + k_encode, so the same bytes.
+// ---------------------------------------------------------------------------
+struct ChunkFinishArgs {
+    const SegDev* segs;
+    const uint32_t* tile_seg;
+    const uint2* stage;
+    const uint32_t* tile_cnt;
+    const uint32_t* tile_off;
+    const uint32_t* chunk_cnt;
+    const double* chunk_gsum;
+    uint8_t* msg;
+    float* residue;
+    uint64_t entries_begin;
+    uint32_t nchunks;
+    uint32_t nseg;
+    uint32_t ntiles;
+    uint32_t plan_hash;
+};
+
+__global__ void __launch_bounds__(256) k_finish_chunks(ChunkFinishArgs A) {
+    extern __shared__ uint64_t dyn64[];   // 8-byte aligned
+    __shared__ uint64_t lsz[4], lns[4];
+    const uint32_t C = A.nchunks, S = A.nseg;
+    // [C] chunk sums, [S] entry offsets, [S + 1] survivors before each
+    // segment (64-bit); [C] chunk counts, [C] chunk bases, [S] s, [S] survivors.
+    double* cgs = reinterpret_cast<double*>(dyn64);
+    uint64_t* seoff = reinterpret_cast<uint64_t*>(cgs + C);
+    uint64_t* ssbase = seoff + S;
+    uint32_t* ccnt = reinterpret_cast<uint32_t*>(ssbase + S + 1);
+    uint32_t* cbase = ccnt + C;
+    float* ss = reinterpret_cast<float*>(cbase + C);
+    uint32_t* sn = reinterpret_cast<uint32_t*>(ss + S);
+    for (uint32_t c = threadIdx.x; c < C; c += 256) {
+        ccnt[c] = A.chunk_cnt[c];
+        cgs[c] = A.chunk_gsum[c];
+    }
+    __syncthreads();
+    finalize_block(A.segs, S, A.plan_hash, A.entries_begin, ccnt, cgs, cbase, ss, sn, seoff, ssbase,
+                   A.msg, lsz, lns, blockIdx.x == 0);
+    __syncthreads();
+    encode_wave(blockIdx.x * 4u + (threadIdx.x >> 6), gridDim.x * 4u, A.segs, S, A.tile_seg, A.stage,
+                A.tile_cnt, A.tile_off, cbase, ss, seoff, ssbase, A.msg, A.residue, A.ntiles);
+}
+
 }  // namespace adacomp

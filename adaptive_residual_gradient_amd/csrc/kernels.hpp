@@ -12,9 +12,10 @@
 // The kernels live in common.hpp (shared helpers), tile_pass.hpp, encode.hpp,
 // small_table.hpp and decode.hpp; this header includes them all.
 //
-// Compress, per call, four stream-ordered launches (small tables: the tile
-// pass and one finish kernel that does the work of the last three, see
-// small_table.hpp):
+// Compress, per call, up to four stream-ordered launches (small tables: the
+// tile pass and one finish kernel that does the work of the last three, see
+// small_table.hpp; tables of up to 256 segments and 2^20 tiles: the tile
+// pass, the chunk scan and k_finish_chunks, finalize and encode in one):
 //   tile pass   (dense, one workgroup per tile of whole bins; bins longer than
 //               4093 elements one per workgroup, streamed twice): reads residue
 //               and dW once as float4, forms G and H, bin maxima by a

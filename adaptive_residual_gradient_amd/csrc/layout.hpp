@@ -404,20 +404,44 @@ inline bool single_launch_fits(const Layout& L) {
            L.ct.by_variant[0].size() + L.ct.by_variant[1].size() == L.ct.ntiles;
 }
 
+// LDS bytes of the chunk finish (finalize + encode in one kernel) for C
+// scan chunks and S segments: per chunk a double and two words, per segment
+// two 64-bit and two 32-bit words, plus one 64-bit total.
+ADACOMP_HD constexpr uint64_t chunk_finish_lds_bytes(uint64_t C, uint64_t S) {
+    return 8 * C + 8 * C + 16 * S + 8 + 8 * S;
+}
+// Kept to 32 KB, so that LDS allows the 5 workgroups per CU the kernel's
+// registers allow.  A segment of n tiles has ceil(n / 1024) scan chunks, so
+// a table within the limits has at most nseg + ntiles / 1024 of them.
+constexpr uint64_t kChunkLdsMax = 32768;
+static_assert(chunk_finish_lds_bytes(ADACOMP_SMALL_TABLE_MAX_SEGMENTS +
+                                         ADACOMP_CHUNK_FINISH_MAX_TILES / kChunkTiles,
+                                     ADACOMP_SMALL_TABLE_MAX_SEGMENTS) <= kChunkLdsMax,
+              "chunk finish: the chunk and segment tables fit the LDS budget");
+inline bool chunk_finish_fits(const Layout& L) {
+    return L.ct.ntiles >= 1 && L.ct.ntiles <= ADACOMP_CHUNK_FINISH_MAX_TILES &&
+           L.nseg <= ADACOMP_SMALL_TABLE_MAX_SEGMENTS;
+}
+
 // How a plan compresses.
-enum class Finish { kSeparate, kSmall, kSingle };
+enum class Finish { kSeparate, kSmall, kSingle, kChunks };
 
 // The finish a plan made with plan_flags uses (flags already validated).
 inline Finish choose_finish(const Layout& L, uint32_t plan_flags) {
     if ((plan_flags & ADACOMP_PLAN_SINGLE_LAUNCH) != 0u && single_launch_fits(L)) return Finish::kSingle;
-    if ((plan_flags & ADACOMP_PLAN_SEPARATE_FINISH) == 0u && small_table_fits(L)) return Finish::kSmall;
+    if ((plan_flags & ADACOMP_PLAN_SEPARATE_FINISH) != 0u) return Finish::kSeparate;
+    if (small_table_fits(L)) return Finish::kSmall;
+    if (chunk_finish_fits(L)) return Finish::kChunks;
     return Finish::kSeparate;
 }
+
+// Plans whose finish reads the per-tile tables of small_table_fits.
+inline bool uses_small_tables(Finish f) { return f == Finish::kSmall || f == Finish::kSingle; }
 
 // Kernel launches of one compress call.
 inline uint64_t compress_launches(const Layout& L, Finish f) {
     if (f == Finish::kSingle) return 1;
-    uint64_t n = f == Finish::kSmall ? 1 : 3;   // finish kernels
+    uint64_t n = f == Finish::kSmall ? 1 : f == Finish::kChunks ? 2 : 3;   // finish kernels
     for (int v = 0; v < kVariants; ++v) n += L.ct.by_variant[v].empty() ? 0 : 1;
     return n;
 }

@@ -124,16 +124,21 @@ int adacomp_plan_query(const adacomp_segment* segs, uint32_t nseg, adacomp_plan_
  * directory, entry words and residue of the sent elements.  For a small
  * table -- span <= ADACOMP_SMALL_TABLE_MAX_SPAN elements and at most
  * ADACOMP_SMALL_TABLE_MAX_SEGMENTS segments -- the finish is one launch
- * whose every workgroup holds the table's tile counts in LDS; otherwise it is
- * three (chunk scan, finalize, encode).  info.compress_launches reports the
- * total.  Every path writes the same bytes.  plan_query reports the sizes of
- * a plan made with no flags. */
+ * whose every workgroup holds the table's tile counts in LDS.  Otherwise, for
+ * a table of at most ADACOMP_SMALL_TABLE_MAX_SEGMENTS segments and at most
+ * ADACOMP_CHUNK_FINISH_MAX_TILES tiles (info.ntiles), it is two: the chunk
+ * scan, then one kernel whose every workgroup computes s and the entry
+ * regions from the chunk sums in LDS and encodes its share.  Any other table
+ * takes three (chunk scan, finalize, encode).  info.compress_launches reports
+ * the total.  Every path writes the same bytes.  plan_query reports the sizes
+ * of a plan made with no flags. */
 #define ADACOMP_SMALL_TABLE_MAX_SPAN (1u << 21)
 #define ADACOMP_SMALL_TABLE_MAX_SEGMENTS 256u
+#define ADACOMP_CHUNK_FINISH_MAX_TILES (1u << 20)
 int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan** plan);
 
 /* Plan flags (adacomp_plan_create_ex).
- * SEPARATE_FINISH: finish with the three kernels even for a small table.
+ * SEPARATE_FINISH: finish with the three kernels whatever the table.
  * SINGLE_LAUNCH: compress a small table whose bins are all <= 4093 in one
  *   launch: the workgroup that finishes its tile last completes the message
  *   alone.  Correct, but slower on MI355X than the default (the release of
@@ -260,14 +265,14 @@ int adacomp_decode_adam_timed(const adacomp_plan* plan, const void* const* msgs,
 /* Kernel stages a timer reports, in this order. */
 #define ADACOMP_STAGE_TILE_PASS 0   /* dense pass: G, H, bin maxima, selection, counts */
 #define ADACOMP_STAGE_CHUNK_SCAN 1  /* per-chunk survivor offsets and scale partial sums */
-#define ADACOMP_STAGE_FINALIZE 2    /* s per segment, message header and directory */
+#define ADACOMP_STAGE_FINALIZE 2    /* s per segment, message header and directory (three-kernel finish) */
 #define ADACOMP_STAGE_ENCODE 3      /* entry words and residue of transmitted elements */
 #define ADACOMP_STAGE_DECODE_COUNT 4
 #define ADACOMP_STAGE_DECODE_BASE 5
 #define ADACOMP_STAGE_DECODE_APPLY 6
 #define ADACOMP_STAGE_COMPRESS_CALL 7  /* a whole adacomp_compress call, gaps between kernels included
-                                          (a small-table finish is recorded under stage 3, a single
-                                          launch only here) */
+                                          (a small-table or two-kernel finish's last kernel is
+                                          recorded under stage 3, a single launch only here) */
 #define ADACOMP_STAGE_DECODE_CALL 8    /* a whole adacomp_decode_accumulate call */
 #define ADACOMP_STAGE_DECODE_SGD_CALL 9  /* a whole adacomp_decode_sgd call (its kernels: stages 4-6) */
 #define ADACOMP_STAGE_DECODE_ADAM_CALL 10 /* a whole adacomp_decode_adam call (its kernels: stages 4-6) */

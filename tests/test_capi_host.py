@@ -57,6 +57,7 @@ def test_binding_constants_match_the_header():
     assert macro("ADACOMP_PLAN_SINGLE_LAUNCH") == A.PLAN_SINGLE_LAUNCH
     assert macro("ADACOMP_SMALL_TABLE_MAX_SPAN") == A.SMALL_TABLE_MAX_SPAN
     assert macro("ADACOMP_SMALL_TABLE_MAX_SEGMENTS") == A.SMALL_TABLE_MAX_SEGMENTS
+    assert macro("ADACOMP_CHUNK_FINISH_MAX_TILES") == A.CHUNK_FINISH_MAX_TILES
     assert macro("ADACOMP_MAX_MESSAGES") == A.MAX_MESSAGES
     assert macro("ADACOMP_MAX_BIN_LEN") == A.MAX_BIN_LEN
     assert macro("ADACOMP_NUM_STAGES") == A.NUM_STAGES == len(A.STAGES)
@@ -110,15 +111,24 @@ def test_ls_flag_enters_plan_hash():
 
 
 def test_compress_launches_rule():
-    """Tables of span <= 2^21 and <= 256 segments finish in one launch after
-    one tile-pass launch per tile shape; others in three."""
+    """After one tile-pass launch per tile shape: tables of span <= 2^21 and
+    <= 256 segments finish in one launch; other tables of <= 256 segments and
+    <= 2^20 tiles in two; the rest in three."""
     launches = {name: A.plan_query(W.workload(name).segments).compress_launches
                 for name in W.WORKLOADS}
-    assert launches == {"fc": 2, "conv": 4, "fc_lstm": 4, "resnet50": 4, "large": 4}
+    assert launches == {"fc": 2, "conv": 3, "fc_lstm": 3, "resnet50": 3, "large": 3}
     assert A.plan_query([(0, 1 << 21, 500)]).compress_launches == 2
-    assert A.plan_query([(0, (1 << 21) + 4, 500)]).compress_launches == 4
+    assert A.plan_query([(0, (1 << 21) + 4, 500)]).compress_launches == 3
     assert A.plan_query([(4 * i, 4, 4) for i in range(256)]).compress_launches == 2
     assert A.plan_query([(4 * i, 4, 4) for i in range(257)]).compress_launches == 4
+    big = [(4 * i, 4, 4) for i in range(255)] + [(1020, 1 << 22, 500)]
+    assert A.plan_query(big).compress_launches == 3
+    assert A.plan_query(big + [(1020 + (1 << 22), 4, 4)]).compress_launches == 4
+    # L_T 1: 2048 bins of one element per tile, so 2^20 tiles are 2^31 elements
+    # (planned on the host only).
+    assert A.plan_query([(0, 1 << 31, 1)]).ntiles == A.CHUNK_FINISH_MAX_TILES
+    assert A.plan_query([(0, 1 << 31, 1)]).compress_launches == 3
+    assert A.plan_query([(0, (1 << 31) + 4, 1)]).compress_launches == 4
     # three tile shapes (L_T 50, 4093, 5000): three tile-pass launches
     assert A.plan_query([(0, 1000, 50), (1000, 8186, 4093), (9188, 10000, 5000)]).compress_launches == 4
 

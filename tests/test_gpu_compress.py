@@ -381,12 +381,15 @@ def test_argument_errors():
     plan.close()
 
 
-@pytest.mark.parametrize("plan_flags", [A.PLAN_SEPARATE_FINISH, 0, A.PLAN_SINGLE_LAUNCH])
-def test_timer_reports_every_stage(plan_flags):
+@pytest.mark.parametrize("name,plan_flags", [("fc", A.PLAN_SEPARATE_FINISH), ("fc", 0),
+                                             ("fc", A.PLAN_SINGLE_LAUNCH), ("conv", 0)])
+def test_timer_reports_every_stage(name, plan_flags):
     """The three-kernel finish reports its four kernels and the whole call;
-    the small-table finish the tile pass, its one finish kernel (as the
-    encode stage) and the call; the single launch only the call."""
-    wl = W.workload("fc")
+    the small-table finish (100x1000 table) the tile pass, its one finish
+    kernel (as the encode stage) and the call; the two-kernel finish (conv
+    table) the tile pass, the chunk scan, its finish kernel (as the encode
+    stage) and the call; the single launch only the call."""
+    wl = W.workload(name)
     plan = A.Plan(wl.segments, plan_flags=plan_flags)
     r = torch.zeros(W.alloc_len(wl), dtype=torch.float32, device=DEV)
     d = W.make_dw(wl, 0, 1, DEV)
@@ -398,6 +401,8 @@ def test_timer_reports_every_stage(plan_flags):
     kernels = ("tile_pass", "chunk_scan", "finalize", "encode")
     recorded = {A.PLAN_SEPARATE_FINISH: kernels, 0: ("tile_pass", "encode"),
                 A.PLAN_SINGLE_LAUNCH: ()}[plan_flags]
+    if name == "conv":
+        recorded = ("tile_pass", "chunk_scan", "encode")
     assert rd["compress_call"][1] == 3 and rd["compress_call"][0] > 0
     for st in kernels:
         if st in recorded:
