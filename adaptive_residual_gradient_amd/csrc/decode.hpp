@@ -36,25 +36,38 @@ __device__ __forceinline__ bool header_matches(const uint8_t* m, uint32_t nseg, 
 }
 
 // Sum of the count words in message bytes [a0, a1), read as the aligned
-// 32-bit words that cover them (count regions start 16-byte aligned and are
-// zero-padded to 16 bytes, so those words lie inside the message).
+// 16-byte blocks that cover them (count regions start 16-byte aligned and
+// are zero-padded to 16 bytes, so those blocks lie inside the message).
 __device__ __forceinline__ uint32_t sum_count_words(const uint8_t* m, uint64_t a0, uint64_t a1,
                                                     uint32_t wb) {
-    typedef const __attribute__((address_space(1))) uint32_t* gu32;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(1))) u32x4* gu4;
     uint32_t s = 0;
-#pragma unroll 4
-    for (uint64_t d = a0 & ~uint64_t(3); d < a1; d += 4) {
-        uint32_t v = *(gu32)(m + d);
-        if (d < a0) v &= ~0u << (8u * uint32_t(a0 - d));          // bytes before a0
-        if (d + 4 > a1) v &= ~0u >> (8u * uint32_t(d + 4 - a1));  // bytes from a1 on
-        s += wb == 1u ? (v & 0xFFu) + ((v >> 8) & 0xFFu) + ((v >> 16) & 0xFFu) + (v >> 24)
-                      : (v & 0xFFFFu) + (v >> 16);
+    for (uint64_t d = a0 & ~uint64_t(15); d < a1; d += 16) {
+        const u32x4 v = *(gu4)(m + d);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint64_t dj = d + 4u * uint32_t(j);
+            uint32_t x = w4[j];
+            if (dj + 4 <= a0 || dj >= a1) {
+                x = 0;   // no byte of [a0, a1)
+            } else {
+                if (dj < a0) x &= ~0u << (8u * uint32_t(a0 - dj));          // bytes before a0
+                if (dj + 4 > a1) x &= ~0u >> (8u * uint32_t(dj + 4 - a1));  // bytes from a1 on
+            }
+            s += wb == 1u ? (x & 0xFFu) + ((x >> 8) & 0xFFu) + ((x >> 16) & 0xFFu) + (x >> 24)
+                          : (x & 0xFFFFu) + (x >> 16);
+        }
     }
     return s;
 }
 
 // Per (chunk of decode tiles, message): survivors of each decode tile from
-// the count words, offsets within the chunk, chunk totals.
+// the count words, offsets within the chunk, chunk totals.  Thread t takes
+// tiles t, t + 256, t + 512, t + 768, so the lanes of a wavefront read
+// neighbouring tiles' count words together; one block scan per round of
+// 256 tiles gives the offsets in tile order.
 __global__ void __launch_bounds__(256)
 k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
                const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ chunk_seg,
@@ -67,10 +80,9 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
     const SegDev sg = segs[chunk_seg[c]];
     const uint32_t tb = chunk_tile_begin[c], n = chunk_tile_begin[c + 1] - tb;
     uint32_t cnt[4];
-    uint32_t mine = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t t = threadIdx.x * 4u + i;
+        const uint32_t t = uint32_t(i) * 256u + threadIdx.x;
         uint32_t s = 0;
         if (ok && t < n) {
             const uint32_t first_bin = (tb + t - sg.dt.tile_begin) * sg.dt.bpt;
@@ -79,20 +91,20 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
             s = sum_count_words(m, a0, a0 + uint64_t(nb) * sg.wb, sg.wb);
         }
         cnt[i] = s;
-        mine += s;
     }
-    uint32_t total;
-    uint32_t run = block_exclusive_scan<256>(mine, lw, &total);
+    uint32_t base = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t t = threadIdx.x * 4u + i;
+        const uint32_t t = uint32_t(i) * 256u + threadIdx.x;
+        uint32_t total;
+        const uint32_t ex = block_exclusive_scan<256>(cnt[i], lw, &total);
         if (t < n) {
             ws.dcnt[uint64_t(k) * DT + tb + t] = cnt[i];
-            ws.doff[uint64_t(k) * DT + tb + t] = run;
+            ws.doff[uint64_t(k) * DT + tb + t] = base + ex;
         }
-        run += cnt[i];
+        base += total;
     }
-    if (threadIdx.x == 0) ws.dchunk_cnt[uint64_t(k) * DC + c] = total;
+    if (threadIdx.x == 0) ws.dchunk_cnt[uint64_t(k) * DC + c] = base;
 }
 
 // One block: message validity, per-segment s and entry offsets, chunk bases.
@@ -122,11 +134,19 @@ k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, uint32_
         ws.dseg_s[i] = s;
         ws.dseg_eoff[i] = eoff;
         const SegDev sg = segs[l];
+        const uint64_t c0 = uint64_t(k) * DC + sg.dt.chunk_begin;
         uint32_t run = 0;
-        for (uint32_t c = 0; c < sg.dt.nchunks; ++c) {
-            const uint64_t ci = uint64_t(k) * DC + sg.dt.chunk_begin + c;
-            ws.dchunk_base[ci] = run;
-            run += ws.dchunk_cnt[ci];
+        // Chunk totals eight at a time, all requested before any is used.
+        for (uint32_t c = 0; c < sg.dt.nchunks; c += 8) {
+            uint32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = c + u < sg.dt.nchunks ? ws.dchunk_cnt[c0 + c + u] : 0u;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (c + u < sg.dt.nchunks) ws.dchunk_base[c0 + c + u] = run;
+                run += v[u];
+            }
         }
     }
     __syncthreads();
