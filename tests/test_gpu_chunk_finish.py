@@ -106,3 +106,30 @@ def test_survivor_extremes(kind):
         d[d == 0] = 1e-3
     surv = run_both(segs, np.zeros(span, np.float32), [d], oracle_steps=1)
     assert surv == [0 if kind == "no_survivors" else span]
+
+
+def test_tile_limit():
+    """The largest table the two-kernel finish takes: one layer of 2^20
+    tiles (L_T 1025, one bin per tile; 1024 scan chunks in the layer),
+    compared in full with the oracle; one tile more takes three kernels."""
+    n = (1 << 20) * 1025
+    segs = [(0, n, 1025)]
+    assert A.plan_query([(0, n + 4, 1025)]).compress_launches == 4
+    plan = A.Plan(segs)
+    assert plan.info.ntiles == A.CHUNK_FINISH_MAX_TILES and plan.info.compress_launches == 3
+    msg, ws = plan.message_buffer(DEV), plan.compress_workspace(DEV)
+    gmax = torch.empty(int(plan.info.total_bins), dtype=torch.float32, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(47)
+    r_dev = torch.empty(n, dtype=torch.float32, device=DEV).normal_(0.0, 1e-3, generator=gen)
+    d_dev = torch.empty(n, dtype=torch.float32, device=DEV).normal_(0.0, 1e-3, generator=gen)
+    r_in, d = r_dev.cpu().numpy(), d_dev.cpu().numpy()
+    say(f"  one layer of {n} elements, {plan.info.ntiles} tiles")
+    A.compress(plan, r_dev, d_dev, msg, ws, bin_max_out=gmax)
+    torch.cuda.synchronize()
+    total, surv, _ = A.message_header(plan, msg)
+    del ws, d_dev
+    rep = compare_step(segs, r_in, d, r_dev.cpu().numpy(), msg[:total].cpu().numpy(), gmax.cpu().numpy())
+    say(f"    survivors {rep.survivors}, message {total} bytes")
+    plan.close()
+    del r_dev, msg, gmax
+    torch.cuda.empty_cache()
