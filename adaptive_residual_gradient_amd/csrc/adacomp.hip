@@ -741,20 +741,36 @@ int adacomp_timer_destroy(adacomp_timer* timer) {
 
 int adacomp_timer_read(adacomp_timer* timer, double* ms, uint64_t* launches, uint32_t nstages) {
     if (timer == nullptr || ms == nullptr || launches == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
-    for (auto& c : timer->calls) {
-        if (hipEventSynchronize(c.ev.back()) != hipSuccess) return ADACOMP_ERR_HIP;
-        float t = 0.f;
-        for (size_t i = 0; i < c.stage.size(); ++i) {
-            if (hipEventElapsedTime(&t, c.ev[i], c.ev[i + 1]) != hipSuccess) return ADACOMP_ERR_HIP;
-            timer->ms[c.stage[i]] += t;
-            timer->n[c.stage[i]] += 1;
+    // Each call is added whole or not at all; a call whose events cannot be
+    // read is dropped (the calls before it stay counted), so no call is
+    // counted twice.
+    size_t done = 0;
+    int st = ADACOMP_OK;
+    std::vector<float> t;
+    for (; done < timer->calls.size(); ++done) {
+        adacomp_timer::Call& c = timer->calls[done];
+        t.assign(c.stage.size() + 1, 0.f);
+        bool ok = hipEventSynchronize(c.ev.back()) == hipSuccess;
+        for (size_t i = 0; ok && i < c.stage.size(); ++i)
+            ok = hipEventElapsedTime(&t[i], c.ev[i], c.ev[i + 1]) == hipSuccess;
+        ok = ok && hipEventElapsedTime(&t.back(), c.ev.front(), c.ev.back()) == hipSuccess;
+        if (ok) {
+            for (size_t i = 0; i < c.stage.size(); ++i) {
+                timer->ms[c.stage[i]] += t[i];
+                timer->n[c.stage[i]] += 1;
+            }
+            timer->ms[c.whole] += t.back();
+            timer->n[c.whole] += 1;
         }
-        if (hipEventElapsedTime(&t, c.ev.front(), c.ev.back()) != hipSuccess) return ADACOMP_ERR_HIP;
-        timer->ms[c.whole] += t;
-        timer->n[c.whole] += 1;
         for (hipEvent_t e : c.ev) (void)hipEventDestroy(e);
+        if (!ok) {
+            st = ADACOMP_ERR_HIP;
+            ++done;
+            break;
+        }
     }
-    timer->calls.clear();
+    timer->calls.erase(timer->calls.begin(), timer->calls.begin() + static_cast<std::ptrdiff_t>(done));
+    if (st != ADACOMP_OK) return st;
     for (uint32_t i = 0; i < nstages && i < ADACOMP_NUM_STAGES; ++i) {
         ms[i] = timer->ms[i];
         launches[i] = timer->n[i];

@@ -278,10 +278,15 @@ int adacomp_decode_adam_timed(const adacomp_plan* plan, const void* const* msgs,
 #define ADACOMP_STAGE_DECODE_ADAM_CALL 10 /* a whole adacomp_decode_adam call (its kernels: stages 4-6) */
 #define ADACOMP_NUM_STAGES 11
 
+/* A timer keeps the HIP events of every call recorded since the last read
+ * (one per stage boundary); one timer may serve calls on several streams,
+ * from one host thread at a time (it has no lock). */
 int adacomp_timer_create(adacomp_timer** timer);
 int adacomp_timer_destroy(adacomp_timer* timer);
 /* Wait for every recorded event, then report per stage the summed
- * milliseconds and the number of launches since the last reset. */
+ * milliseconds and the number of launches since the last reset.  On
+ * ADACOMP_ERR_HIP the calls read so far stay counted and the call whose
+ * events failed is dropped. */
 int adacomp_timer_read(adacomp_timer* timer, double* ms, uint64_t* launches, uint32_t nstages);
 int adacomp_timer_reset(adacomp_timer* timer);
 
