@@ -116,11 +116,29 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
         if (ls) sfirst[b] = kSentinel;
     }
 
+    // Per element, computed once for every pass below: G, its bin within
+    // the tile, whether it lies in the tile (bit c of vm[v]) and whether it
+    // starts its bin (bit c of fb[v]).
     float g[VPT][4];
+    uint32_t bn[VPT][4];
+    uint32_t vm[VPT], fb[VPT];
 #pragma unroll
-    for (int v = 0; v < VPT; ++v)
+    for (int v = 0; v < VPT; ++v) {
+        const int vi = v * THREADS + tid;
+        const int x0 = vi * 4 - int(tg.lead);
+        uint32_t prev = x0 > 0 ? div_bin(uint32_t(x0 - 1), lt, magic) : ~0u;   // bin of x0 - 1
+        vm[v] = 0u;
+        fb[v] = 0u;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) g[v][c] = in.rr[v][c] + in.dw[v][c];   // G = residue + dW
+        for (int c = 0; c < 4; ++c) {
+            const int x = x0 + c;
+            g[v][c] = in.rr[v][c] + in.dw[v][c];   // G = residue + dW
+            bn[v][c] = div_bin(uint32_t(max(x, 0)), lt, magic);
+            if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen)) vm[v] |= 1u << c;
+            if (x == 0 || (x > 0 && bn[v][c] != prev)) fb[v] |= 1u << c;   // a bin starts at x
+            prev = bn[v][c];
+        }
+    }
     __syncthreads();   // smax cleared
 
     // ---- bin maxima: g_max(i) = max |G| over bin i ----
@@ -128,14 +146,11 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
         // A float4 then spans at most two bins: a head run and a tail run.
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            const int vi = v * THREADS + tid;
-            const int x0 = vi * 4 - int(tg.lead);
             uint32_t hb = kSentinel, tb = kSentinel, mh = 0u, mt = 0u;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int x = x0 + c;
-                if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen)) {
-                    const uint32_t b = div_bin(uint32_t(x), lt, magic);
+                if ((vm[v] >> c) & 1u) {
+                    const uint32_t b = bn[v][c];
                     const uint32_t m = __float_as_uint(fabsf(g[v][c]));
                     if (hb == kSentinel) { hb = b; tb = b; mh = m; mt = m; }
                     else if (b == hb) { mh = max(mh, m); mt = max(mt, m); }
@@ -158,14 +173,10 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
     } else {
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            const int vi = v * THREADS + tid;
-            const int x0 = vi * 4 - int(tg.lead);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int x = x0 + c;
-                if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen))
-                    atomicMax(&smax[div_bin(uint32_t(x), lt, magic)],
-                              __float_as_uint(fabsf(g[v][c])));
+                if ((vm[v] >> c) & 1u)
+                    atomicMax(&smax[bn[v][c]], __float_as_uint(fabsf(g[v][c])));
             }
         }
     }
@@ -181,8 +192,8 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int x = x0 + c;
-                if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen)) {
-                    const uint32_t b = div_bin(uint32_t(x), lt, magic);
+                if ((vm[v] >> c) & 1u) {
+                    const uint32_t b = bn[v][c];
                     const uint32_t m = __float_as_uint(fabsf(g[v][c]));
                     if (m != 0u && m == smax[b]) atomicMin(&sfirst[b], uint32_t(x));
                 }
@@ -202,8 +213,8 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int x = x0 + c;
-            if (vi < int(tg.nvec) && x >= 0 && x < int(tg.tlen)) {
-                const uint32_t b = div_bin(uint32_t(x), lt, magic);
+            if ((vm[v] >> c) & 1u) {
+                const uint32_t b = bn[v][c];
                 const float gm = __uint_as_float(smax[b]);
                 const float h = g[v][c] + in.dw[v][c];      // H = G + dW
                 const bool take = ls ? sfirst[b] == uint32_t(x) : fabsf(h) >= gm && g[v][c] != 0.0f;
@@ -241,9 +252,9 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int x = x0 + c;
-            if (x >= 0 && x < int(tg.tlen)) {
-                const uint32_t b = div_bin(uint32_t(x), lt, magic);
-                if (uint32_t(x) == b * lt) sbound[b] = r;
+            if ((vm[v] >> c) & 1u) {
+                const uint32_t b = bn[v][c];
+                if ((fb[v] >> c) & 1u) sbound[b] = r;
                 if (sel[v] & (1u << c)) {
                     const uint32_t neg = g[v][c] < 0.0f ? 0x80000000u : 0u;
                     st[r] = make_uint2(neg | uint32_t(x), __float_as_uint(g[v][c]));
@@ -252,16 +263,14 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
             }
         }
         const uint64_t e0 = tg.v0 + uint64_t(vi) * 4u;
-        if (x0 >= 0 && x0 + 4 <= int(tg.tlen)) {
+        if (vm[v] == 15u) {
             f32x4 o;
             o.x = g[v][0]; o.y = g[v][1]; o.z = g[v][2]; o.w = g[v][3];
             store4<ADACOMP_NT_ST>(residue + e0, o);
         } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int x = x0 + c;
-                if (x >= 0 && x < int(tg.tlen)) residue[e0 + c] = g[v][c];
-            }
+            for (int c = 0; c < 4; ++c)
+                if ((vm[v] >> c) & 1u) residue[e0 + c] = g[v][c];
         }
     }
     if (tid == 0) sbound[tg.nb] = total;
