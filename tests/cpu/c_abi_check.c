@@ -29,6 +29,16 @@ int main(void) {
     printf("OK plan_query nseg=%u bins=%llu capacity=%llu launches=%llu\n", info.nseg,
            (unsigned long long)info.total_bins, (unsigned long long)info.message_capacity,
            (unsigned long long)info.compress_launches);
+    {   /* past the small-table span, within the two-kernel finish's limits */
+        adacomp_segment big;
+        memset(&big, 0, sizeof big);
+        big.numel = ADACOMP_SMALL_TABLE_MAX_SPAN + 4;
+        big.bin_len = 500;
+        adacomp_plan_info bi;
+        if (adacomp_plan_query(&big, 1, &bi) != ADACOMP_OK) return fail("plan_query big");
+        if (bi.ntiles > ADACOMP_CHUNK_FINISH_MAX_TILES || bi.compress_launches != 3)
+            return fail("two-kernel finish launches");
+    }
     adacomp_plan* plan = NULL;
     if (adacomp_plan_create_ex(segs, 3, ADACOMP_PLAN_SEPARATE_FINISH | ADACOMP_PLAN_SINGLE_LAUNCH,
                                &plan) != ADACOMP_ERR_INVALID_ARGUMENT || plan != NULL)
