@@ -241,10 +241,7 @@ k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
 // survivors, and the lanes take them 64 at a time, with the staged pairs of
 // kEncBatch rounds loaded before any of them is used.  Only wavefront-level
 // operations are used, so every wavefront ends on its own.
-#ifndef ADACOMP_ENC_BATCH
-#define ADACOMP_ENC_BATCH 8
-#endif
-constexpr int kEncBatch = ADACOMP_ENC_BATCH;
+constexpr int kEncBatch = 8;   // 4 and 6 measured within noise; 8 keeps the most loads in flight
 constexpr uint32_t kEncMaxBlocks = 2048;   // 8192 wavefronts: one per wavefront slot of the chip
 
 // Largest i in [0, n) with key(i) <= x, for key nondecreasing with

@@ -34,18 +34,12 @@ namespace adacomp {
 // first of them whose capacity holds one bin plus the up-to-3 leading
 // elements of an unaligned tile start.  Longer bins take shape 2: one bin
 // per tile, streamed twice by 256 threads in chunks of 256 x 2 float4.
-#ifndef ADACOMP_NARROW_VECS
-#define ADACOMP_NARROW_VECS 2
-#endif
-#ifndef ADACOMP_NARROW_THREADS
-#define ADACOMP_NARROW_THREADS 256
-#endif
+// Shape 0 at 2 float4 per thread is the fastest for L_T = 500 (3 or 4:
+// 2.07 and 2.11 ms against 1.97-2.01 ms on the 1.07e9-element workload;
+// 512- or 1024-thread tiles: 2.4-2.6 ms).
 constexpr int kVariants = 3;
-constexpr uint32_t kVarThreads[kVariants] = {ADACOMP_NARROW_THREADS, 256, 256};
-#ifndef ADACOMP_LONG_VECS
-#define ADACOMP_LONG_VECS 2
-#endif
-constexpr uint32_t kVarVecs[kVariants] = {ADACOMP_NARROW_VECS, 4, ADACOMP_LONG_VECS};   // shape 2: per chunk
+constexpr uint32_t kVarThreads[kVariants] = {256, 256, 256};
+constexpr uint32_t kVarVecs[kVariants] = {2, 4, 2};   // shape 2: per chunk
 constexpr uint32_t kLongCap = ADACOMP_MAX_BIN_LEN + 4;   // one bin and an unaligned start
 constexpr uint32_t var_cap(int v) { return v == 2 ? kLongCap : kVarThreads[v] * kVarVecs[v] * 4; }
 constexpr uint32_t kMaxCap = 1024 * 9 * 4;   // 36864 elements: long-bin decode tiles

@@ -81,8 +81,8 @@ __device__ __forceinline__ void load_tile(TileRegs<VPT>& t, const SegDev* __rest
     for (int v = 0; v < VPT; ++v) {
         const uint32_t vi = min(uint32_t(v * THREADS + tid), t.tg.nvec - 1u);
         const uint64_t e0 = t.tg.v0 + uint64_t(vi) * 4u;
-        const f32x4 a = load4<ADACOMP_NT_R>(residue + e0);
-        const f32x4 b = load4<ADACOMP_NT_DW>(dW + e0);
+        const f32x4 a = load4<kNtLoadResidue>(residue + e0);
+        const f32x4 b = load4<kNtLoadDw>(dW + e0);
         t.rr[v][0] = a.x; t.rr[v][1] = a.y; t.rr[v][2] = a.z; t.rr[v][3] = a.w;
         t.dw[v][0] = b.x; t.dw[v][1] = b.y; t.dw[v][2] = b.z; t.dw[v][3] = b.w;
     }
@@ -266,7 +266,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
         if (vm[v] == 15u) {
             f32x4 o;
             o.x = g[v][0]; o.y = g[v][1]; o.z = g[v][2]; o.w = g[v][3];
-            store4<ADACOMP_NT_ST>(residue + e0, o);
+            store4<kNtStoreResidue>(residue + e0, o);
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
@@ -384,9 +384,8 @@ k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ t
     const uint32_t first = m != 0u ? mi : kSentinel;   // LS: nothing in an all-zero bin
 
     // ---- pass 2: selection, compaction to staging, residue <- G ----
-#ifndef ADACOMP_LONG_NT2
-#define ADACOMP_LONG_NT2 1
-#endif
+    // The second read of a long bin is its last use: non-temporal.
+    constexpr bool kNtSecondRead = true;
     uint32_t carry = 0;
     uint2* st = stage + tg.t0;
     for (uint32_t c0 = 0; c0 < tg.nvec; c0 += CV) {
@@ -394,8 +393,8 @@ k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ t
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const uint32_t vi = min(c0 + uint32_t(v * THREADS + tid), tg.nvec - 1u);
-            a[v] = load4<ADACOMP_LONG_NT2>(residue + tg.v0 + uint64_t(vi) * 4u);
-            b[v] = load4<ADACOMP_LONG_NT2>(dW + tg.v0 + uint64_t(vi) * 4u);
+            a[v] = load4<kNtSecondRead>(residue + tg.v0 + uint64_t(vi) * 4u);
+            b[v] = load4<kNtSecondRead>(dW + tg.v0 + uint64_t(vi) * 4u);
         }
         uint32_t sel[VPT], wrank[VPT];
         float g[VPT][4];
@@ -450,7 +449,7 @@ k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ t
             if (x0 >= 0 && x0 + 4 <= tlen) {
                 f32x4 o;
                 o.x = g[v][0]; o.y = g[v][1]; o.z = g[v][2]; o.w = g[v][3];
-                store4<ADACOMP_NT_ST>(residue + e0, o);
+                store4<kNtStoreResidue>(residue + e0, o);
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
