@@ -146,17 +146,20 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
         // A float4 then spans at most two bins: a head run and a tail run.
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
-            uint32_t hb = kSentinel, tb = kSentinel, mh = 0u, mt = 0u;
+            // Head run: the bin of the first element in the tile; tail run:
+            // the bin of the last (a float4 spans at most two bins; elements
+            // before the tile have bin 0, the first element's, and elements
+            // past it are clamped to the tile's last bin, the last element's).
+            // Maxima without branches; no element in the tile: no runs.
+            const uint32_t valid = vm[v];
+            const uint32_t hb = valid != 0u ? bn[v][0] : kSentinel;
+            const uint32_t tb = valid != 0u ? min(bn[v][3], tg.nb - 1u) : kSentinel;
+            uint32_t mh = 0u, mt = 0u;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                if ((vm[v] >> c) & 1u) {
-                    const uint32_t b = bn[v][c];
-                    const uint32_t m = __float_as_uint(fabsf(g[v][c]));
-                    if (hb == kSentinel) { hb = b; tb = b; mh = m; mt = m; }
-                    else if (b == hb) { mh = max(mh, m); mt = max(mt, m); }
-                    else if (b == tb) { mt = max(mt, m); }
-                    else { tb = b; mt = m; }
-                }
+                const uint32_t m = ((valid >> c) & 1u) ? __float_as_uint(fabsf(g[v][c])) : 0u;
+                mh = max(mh, bn[v][c] == hb ? m : 0u);
+                mt = max(mt, bn[v][c] == tb ? m : 0u);
             }
             const bool two = hb != tb;
             // The head run of a two-run lane continues the previous lane's
