@@ -49,10 +49,17 @@ hipError_t launch_tile_pass(const adacomp_plan* plan, hipStream_t stream, float*
                             const float* dW, uint8_t* msg, uint2* stage, uint32_t* tile_cnt,
                             double* tile_gsum, float* bin_max_out) {
     const uint32_t n = static_cast<uint32_t>(plan->L.ct.by_variant[V].size());
-    if (V == 2)   // long bins: one bin per workgroup, streamed in chunks
-        hipLaunchKernelGGL((k_tile_pass_long<kVarThreads[V], kVarVecs[V]>), dim3(n),
-                           dim3(kVarThreads[V]), 0, stream, plan->d_segs, plan->dct.tile_seg,
-                           plan->dct.vtiles[V], residue, dW, msg, stage, tile_cnt, tile_gsum,
+    constexpr uint32_t CV = kVarThreads[2] * kVarVecs[2];   // float4 per chunk of shape 2
+    if (V == 2 && plan->L.ct.max_span_vecs[2] <= kLongRegChunks * CV)
+        // long bins of at most kLongRegChunks chunks: one bin per workgroup, held in registers
+        hipLaunchKernelGGL((k_tile_pass_long<kVarThreads[2], kVarVecs[2], kLongRegChunks>), dim3(n),
+                           dim3(kVarThreads[2]), 0, stream, plan->d_segs, plan->dct.tile_seg,
+                           plan->dct.vtiles[2], residue, dW, msg, stage, tile_cnt, tile_gsum,
+                           bin_max_out);
+    else if (V == 2)   // longer bins: one bin per workgroup, streamed twice in chunks
+        hipLaunchKernelGGL((k_tile_pass_long<kVarThreads[2], kVarVecs[2], 0>), dim3(n),
+                           dim3(kVarThreads[2]), 0, stream, plan->d_segs, plan->dct.tile_seg,
+                           plan->dct.vtiles[2], residue, dW, msg, stage, tile_cnt, tile_gsum,
                            bin_max_out);
     else
         hipLaunchKernelGGL((k_tile_pass<kVarThreads[V], kVarVecs[V]>), dim3(n), dim3(kVarThreads[V]),

@@ -41,6 +41,9 @@ constexpr int kVariants = 3;
 constexpr uint32_t kVarThreads[kVariants] = {256, 256, 256};
 constexpr uint32_t kVarVecs[kVariants] = {2, 4, 2};   // shape 2: per chunk
 constexpr uint32_t kLongCap = ADACOMP_MAX_BIN_LEN + 4;   // one bin and an unaligned start
+// Long bins that span at most this many chunks of shape 2 are held in
+// registers for both passes (4 chunks of 256 x 2 float4: L_T up to 8189).
+constexpr int kLongRegChunks = 4;
 constexpr uint32_t var_cap(int v) { return v == 2 ? kLongCap : kVarThreads[v] * kVarVecs[v] * 4; }
 constexpr uint32_t kMaxCap = 1024 * 9 * 4;   // 36864 elements: long-bin decode tiles
 constexpr uint32_t kChunkTiles = 1024;  // tiles per scan chunk (4 per thread of a 256-thread block)

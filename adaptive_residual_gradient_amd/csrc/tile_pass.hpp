@@ -320,15 +320,16 @@ k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_s
                                bin_max_out, ch_tot);
 }
 
-// Long bins (L_T > 4093): one workgroup per bin.  The bin is streamed twice
-// in chunks of THREADS x VPT float4: the first pass finds g_max (and, for
-// hard local selection, the first index holding it), the second forms G and
-// H again, selects, compacts and writes the residue.  The second pass reads
-// what the first one just brought on chip (non-temporal: it is the last use),
-// so HBM traffic stays near 12 B/element while bins fit the caches (L_T =
-// 5000: 40 KiB of residue and dW per workgroup) and only 2 float4 per array
-// live in registers.
-template <int THREADS, int VPT>
+// Long bins (L_T > 4093): one workgroup per bin, in chunks of THREADS x VPT
+// float4.  The first pass finds g_max (and, for hard local selection, the
+// first index holding it); the second forms G and H again, selects, compacts
+// and writes the residue.  NCR > 0 (bins of at most NCR chunks): every chunk
+// is loaded once, up front, and both passes run from registers (12 B per
+// element exactly).  NCR = 0 (longer bins): the bin is streamed twice; the
+// second pass reads what the first one just brought on chip (non-temporal:
+// it is the last use), so HBM traffic stays near 12 B per element while bins
+// fit the caches, and only one chunk lives in registers.
+template <int THREADS, int VPT, int NCR>
 __global__ void __launch_bounds__(THREADS)
 k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
                  const uint32_t* __restrict__ vtiles, float* __restrict__ residue,
@@ -347,16 +348,20 @@ k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ t
     const bool ls = (sg.flags & ADACOMP_SEG_LS) != 0u;
     const int lead = int(tg.lead), tlen = int(tg.tlen);
 
-    // ---- pass 1: g_max = max |G| over the bin, and its first index ----
-    uint32_t m = 0u, mi = kSentinel;
-    for (uint32_t c0 = 0; c0 < tg.nvec; c0 += CV) {
-        f32x4 a[VPT], b[VPT];
+    // One chunk's float4 (indexes past the bin clamped to its last float4,
+    // so every lane loads).
+    auto load_chunk = [&](uint32_t c0, f32x4 (&a)[VPT], f32x4 (&b)[VPT], auto nt) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const uint32_t vi = min(c0 + uint32_t(v * THREADS + tid), tg.nvec - 1u);
-            a[v] = load4<false>(residue + tg.v0 + uint64_t(vi) * 4u);
-            b[v] = load4<false>(dW + tg.v0 + uint64_t(vi) * 4u);
+            a[v] = load4<decltype(nt)::value>(residue + tg.v0 + uint64_t(vi) * 4u);
+            b[v] = load4<decltype(nt)::value>(dW + tg.v0 + uint64_t(vi) * 4u);
         }
+    };
+
+    // ---- pass 1 over one chunk: largest |G| and its first index ----
+    uint32_t m = 0u, mi = kSentinel;
+    auto pass1 = [&](const f32x4 (&a)[VPT], const f32x4 (&b)[VPT], uint32_t c0) {
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const uint32_t vi = c0 + uint32_t(v * THREADS + tid);
@@ -369,36 +374,31 @@ k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ t
                 }
             }
         }
-    }
-    // largest |G|, ties to the lowest index
+    };
+    // largest |G| over the workgroup, ties to the lowest index
+    float gm = 0.0f;
+    uint32_t first = kSentinel;
+    auto reduce = [&]() {
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        const uint32_t om = __shfl_xor(m, d), oi = __shfl_xor(mi, d);
-        if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
-    }
-    if (lane == 0) { red_m[wv] = m; red_i[wv] = mi; }
-    __syncthreads();
-    m = red_m[0];
-    mi = red_i[0];
+        for (int d = 32; d >= 1; d >>= 1) {
+            const uint32_t om = __shfl_xor(m, d), oi = __shfl_xor(mi, d);
+            if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
+        }
+        if (lane == 0) { red_m[wv] = m; red_i[wv] = mi; }
+        __syncthreads();
+        m = red_m[0];
+        mi = red_i[0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w)
-        if (red_m[w] > m || (red_m[w] == m && red_i[w] < mi)) { m = red_m[w]; mi = red_i[w]; }
-    const float gm = __uint_as_float(m);
-    const uint32_t first = m != 0u ? mi : kSentinel;   // LS: nothing in an all-zero bin
+        for (int w = 1; w < NW; ++w)
+            if (red_m[w] > m || (red_m[w] == m && red_i[w] < mi)) { m = red_m[w]; mi = red_i[w]; }
+        gm = __uint_as_float(m);
+        first = m != 0u ? mi : kSentinel;   // LS: nothing in an all-zero bin
+    };
 
-    // ---- pass 2: selection, compaction to staging, residue <- G ----
-    // The second read of a long bin is its last use: non-temporal.
-    constexpr bool kNtSecondRead = true;
+    // ---- pass 2 over one chunk: selection, compaction to staging, residue <- G ----
     uint32_t carry = 0;
     uint2* st = stage + tg.t0;
-    for (uint32_t c0 = 0; c0 < tg.nvec; c0 += CV) {
-        f32x4 a[VPT], b[VPT];
-#pragma unroll
-        for (int v = 0; v < VPT; ++v) {
-            const uint32_t vi = min(c0 + uint32_t(v * THREADS + tid), tg.nvec - 1u);
-            a[v] = load4<kNtSecondRead>(residue + tg.v0 + uint64_t(vi) * 4u);
-            b[v] = load4<kNtSecondRead>(dW + tg.v0 + uint64_t(vi) * 4u);
-        }
+    auto pass2 = [&](const f32x4 (&a)[VPT], const f32x4 (&b)[VPT], uint32_t c0) {
         uint32_t sel[VPT], wrank[VPT];
         float g[VPT][4];
 #pragma unroll
@@ -462,6 +462,33 @@ k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ t
             }
         }
         carry += total;
+    };
+
+    if constexpr (NCR > 0) {
+        // The whole bin in registers (the launch guarantees nvec <= NCR * CV);
+        // residue and dW are read once: non-temporal like the dense tile pass.
+        f32x4 ra[NCR][VPT], rb[NCR][VPT];
+#pragma unroll
+        for (int k = 0; k < NCR; ++k) load_chunk(uint32_t(k) * CV, ra[k], rb[k], std::integral_constant<bool, kNtLoadResidue>{});
+#pragma unroll
+        for (int k = 0; k < NCR; ++k)
+            if (uint32_t(k) * CV < tg.nvec) pass1(ra[k], rb[k], uint32_t(k) * CV);
+        reduce();
+#pragma unroll
+        for (int k = 0; k < NCR; ++k)
+            if (uint32_t(k) * CV < tg.nvec) pass2(ra[k], rb[k], uint32_t(k) * CV);   // workgroup-uniform
+    } else {
+        for (uint32_t c0 = 0; c0 < tg.nvec; c0 += CV) {
+            f32x4 a[VPT], b[VPT];
+            load_chunk(c0, a, b, std::integral_constant<bool, false>{});
+            pass1(a, b, c0);
+        }
+        reduce();
+        for (uint32_t c0 = 0; c0 < tg.nvec; c0 += CV) {
+            f32x4 a[VPT], b[VPT];
+            load_chunk(c0, a, b, std::integral_constant<bool, true>{});   // last use: non-temporal
+            pass2(a, b, c0);
+        }
     }
     if (tid == 0) {
         put_word(msg + sg.count_off + uint64_t(tg.first_bin) * sg.wb, sg.wb, carry);
