@@ -56,6 +56,12 @@ hipError_t launch_tile_pass(const adacomp_plan* plan, hipStream_t stream, float*
                            dim3(kVarThreads[2]), 0, stream, plan->d_segs, plan->dct.tile_seg,
                            plan->dct.vtiles[2], residue, dW, msg, stage, tile_cnt, tile_gsum,
                            bin_max_out);
+    else if (V == 2 && plan->L.ct.max_span_vecs[2] <= kLongRegChunks * 4 * CV)
+        // up to 4 chunks of 1024 x 2 float4 (every L_T up to 32768): 1024-thread workgroups
+        hipLaunchKernelGGL((k_tile_pass_long<1024, kVarVecs[2], kLongRegChunks>), dim3(n),
+                           dim3(1024), 0, stream, plan->d_segs, plan->dct.tile_seg,
+                           plan->dct.vtiles[2], residue, dW, msg, stage, tile_cnt, tile_gsum,
+                           bin_max_out);
     else if (V == 2)   // longer bins: one bin per workgroup, streamed twice in chunks
         hipLaunchKernelGGL((k_tile_pass_long<kVarThreads[2], kVarVecs[2], 0>), dim3(n),
                            dim3(kVarThreads[2]), 0, stream, plan->d_segs, plan->dct.tile_seg,
