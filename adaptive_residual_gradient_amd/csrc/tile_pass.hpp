@@ -89,7 +89,9 @@ __device__ __forceinline__ void load_tile(TileRegs<VPT>& t, const SegDev* __rest
 }
 
 // Everything a tile does after its inputs arrived.  lds: this tile's
-// [2*bpt_max+1] words (bin maxima, then bin boundaries).
+// 2 * bpt_max + 1 words (bin maxima, then bin boundaries), followed, when
+// the plan has hard local selection layers, by bpt_max words for each
+// bin's first maximum.
 template <int THREADS, int VPT>
 __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* lds,
                                              const SegDev* __restrict__ segs,
