@@ -70,8 +70,12 @@ def test_decode_parity(name, K):
     plan.close()
 
 
-@pytest.mark.parametrize("lt", [1, 3, 7, 50, 64, 500, 1021, 4093, 4094, 32768])
+@pytest.mark.parametrize("lt", [1, 3, 7, 50, 64, 500, 1021, 4093, 4094, 9000, 18432, 18433, 32768])
 def test_decode_edge_tables(lt):
+    """Every decode tile shape: LDS tiles (L_T <= 4093), long bins with at
+    least two bins per tile accumulated in LDS (4094 .. 18432) and one bin
+    per tile accumulated in place (18433 and up); ragged and one-element
+    layers; accumulate from zero and from a random start."""
     segs, off = [], 0
     for n in (1, 5, 63, 4097, 40003):
         segs.append((off, n, lt))
