@@ -169,14 +169,18 @@ int launch_status() {
 // takes 1.50 against 2.60 ms) and the tile's tables fit the 160 KB a
 // workgroup may hold (the kernel is allowed that much; if that fails, the
 // in-place kernel is used).
-bool long_decode_in_lds(const Layout& L, uint32_t K, uint32_t KG, uint32_t ps) {
+bool long_decode_in_lds(const Layout& L, uint32_t K, uint32_t KG, uint32_t ps, int opt) {
     constexpr uint32_t kLdsMax = 160u * 1024u;
     for (const SegDev& sg : L.segs)
         if (sg.dt.variant == 1u && sg.dt.bpt < 2u) return false;
     const uint32_t lds = adacomp::decode_lds_bytes(L.dt.max_span_vecs[1] * 4, K, KG, ps, 16);
     if (lds > kLdsMax) return false;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&adacomp::k_decode_apply<1024, true>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsMax)) ==
+    const void* fn = opt == adacomp::kOptSgd
+                         ? reinterpret_cast<const void*>(&adacomp::k_decode_apply<1024, true, adacomp::kOptSgd>)
+                     : opt == adacomp::kOptAdam
+                         ? reinterpret_cast<const void*>(&adacomp::k_decode_apply<1024, true, adacomp::kOptAdam>)
+                         : reinterpret_cast<const void*>(&adacomp::k_decode_apply<1024, true>);
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsMax)) ==
            hipSuccess;
 }
 
@@ -642,14 +646,24 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
                     hipLaunchKernelGGL((adacomp::k_decode_apply<256, true>), dim3(n), dim3(256), lds,
                                        stream, mp, K, KG, ps, plan->ddesc[0], DT, DC, L.nseg, dw, out,
                                        accumulate, acc_words, op);
-            } else if (!fused && long_decode_in_lds(L, K, KG, ps)) {
-                // long bins, the whole tile accumulated in LDS (one 1024-thread workgroup per CU)
+            } else if (long_decode_in_lds(L, K, KG, ps, opt)) {
+                // long bins, the whole tile accumulated in LDS (one 1024-thread workgroup per
+                // CU) and written once, or stepped by the optimizer
                 const uint32_t acc_words = L.dt.max_span_vecs[1] * 4;
                 const uint32_t lds = adacomp::decode_lds_bytes(acc_words, K, KG, ps, 16);
-                hipLaunchKernelGGL((adacomp::k_decode_apply<1024, true>), dim3(n), dim3(1024), lds,
-                                   stream, mp, K, KG, ps, plan->ddesc[1], DT, DC, L.nseg, dw, out,
-                                   accumulate, acc_words, op);
-            } else {        // long bins, accumulated in place (in out, or the scratch)
+                if (opt == adacomp::kOptSgd)
+                    hipLaunchKernelGGL((adacomp::k_decode_apply<1024, true, adacomp::kOptSgd>), dim3(n),
+                                       dim3(1024), lds, stream, mp, K, KG, ps, plan->ddesc[1], DT, DC,
+                                       L.nseg, dw, nullptr, 0, acc_words, op);
+                else if (opt == adacomp::kOptAdam)
+                    hipLaunchKernelGGL((adacomp::k_decode_apply<1024, true, adacomp::kOptAdam>), dim3(n),
+                                       dim3(1024), lds, stream, mp, K, KG, ps, plan->ddesc[1], DT, DC,
+                                       L.nseg, dw, nullptr, 0, acc_words, op);
+                else
+                    hipLaunchKernelGGL((adacomp::k_decode_apply<1024, true>), dim3(n), dim3(1024), lds,
+                                       stream, mp, K, KG, ps, plan->ddesc[1], DT, DC, L.nseg, dw, out,
+                                       accumulate, acc_words, op);
+            } else {   // long bins accumulated in place: in out, or in the scratch for an optimizer step
                 const uint32_t lds = adacomp::decode_lds_bytes(0, K, KG, ps, 16);
                 hipLaunchKernelGGL((adacomp::k_decode_apply<1024, false>), dim3(n), dim3(1024), lds,
                                    stream, mp, K, KG, ps, plan->ddesc[1], DT, DC, L.nseg, dw, sums,

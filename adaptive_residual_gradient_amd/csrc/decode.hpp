@@ -257,7 +257,10 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                DecodeWs ws, float* __restrict__ out, int accumulate, uint32_t acc_words,
                OptParams op) {
     constexpr bool FUSED = OPT != kOptNone;
-    static_assert(!FUSED || (LDS_ACC && THREADS == 256), "optimizer steps are fused into LDS tiles");
+    static_assert(!FUSED || LDS_ACC, "optimizer steps are fused into LDS tiles");
+    // 256-thread tiles request their weights and state when the tile starts
+    // (held in registers); larger tiles load them float4 by float4 at the end.
+    constexpr bool PRELOAD = FUSED && THREADS == 256;
     constexpr int NW = THREADS / 64;
     extern __shared__ uint64_t dyn64[];
     uint32_t* dyn = reinterpret_cast<uint32_t*>(dyn64);
@@ -285,9 +288,9 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
     uint32_t* wfk = wfk_all + wv * (KG + 1);
 
     for (uint32_t k = tid; k < K; k += THREADS) ks[k] = ws.dseg_s[uint64_t(k) * nseg + dd.si];
-    constexpr uint32_t NS = FUSED ? kOptSlots : 1;
+    constexpr uint32_t NS = PRELOAD ? kOptSlots : 1;
     f32x4 wv4[NS], mv4[NS], vv4[OPT == kOptAdam ? NS : 1];
-    if (FUSED) {   // weights and state of this thread's float4 slots, requested early
+    if (PRELOAD) {   // weights and state of this thread's float4 slots, requested early
 #pragma unroll
         for (uint32_t j = 0; j < NS; ++j) {
             const uint32_t vi = uint32_t(tid) + THREADS * j;
@@ -445,7 +448,7 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
             }
         }
     }
-    if (FUSED) {
+    if (PRELOAD) {
         __syncthreads();
 #pragma unroll
         for (uint32_t j = 0; j < NS; ++j) {
@@ -455,6 +458,15 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
             f32x4 wq = wv4[j], mq = mv4[j], vq = vv4[OPT == kOptAdam ? j : 0];
             opt_apply<OPT>(a, wq, mq, vq, op, v0 + uint64_t(vi) * 4u, int(vi * 4) - int(lead),
                            int(tlen));
+        }
+    } else if (FUSED) {
+        __syncthreads();
+        for (uint32_t vi = tid; vi < nvec; vi += THREADS) {
+            const uint64_t e0 = v0 + uint64_t(vi) * 4u;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(acc + vi * 4);
+            f32x4 wq = load4<true>(op.w + e0), mq = load4<true>(op.m + e0), vq = {0.f, 0.f, 0.f, 0.f};
+            if (OPT == kOptAdam) vq = load4<true>(op.v + e0);
+            opt_apply<OPT>(a, wq, mq, vq, op, e0, int(vi * 4) - int(lead), int(tlen));
         }
     }
 }
