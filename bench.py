@@ -425,6 +425,9 @@ def main():
     ap.add_argument("--small-table", action="store_true",
                     help="instead of the benchmark, time the compress of the 100 x 1000 layer "
                          "with each finish (default, three-kernel, single launch); one JSON line")
+    ap.add_argument("--other-workloads", action="store_true",
+                    help="instead of the benchmark, time the compress of the conv-stack, FC/LSTM "
+                         "and ResNet-50 tables (steps 6-10 from zero residue); one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device copy of 1 GiB (a known-size reference "
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -445,6 +448,15 @@ def main():
         dev = torch.device("cuda:0")
         torch.cuda.set_device(dev)
         print(json.dumps(measure_small_table(A, W, dev)), flush=True)
+        return
+    if args.other_workloads:
+        import torch
+
+        import adaptive_residual_gradient_amd as A
+        import workloads as W
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        print(json.dumps(measure_other_workloads(A, W, dev)), flush=True)
         return
 
     import numpy as np
