@@ -150,8 +150,8 @@ struct CallTimer {
 };
 
 // Encode workgroups (4 wavefronts each): about one wavefront per 2048
-// elements, at most one per wavefront slot of the chip.  The survivors are
-// shared out evenly among them on the device.
+// elements, at most kEncMaxBlocks.  The survivors are shared out evenly
+// among them on the device.
 uint32_t encode_blocks(const Layout& L) {
     const uint64_t b = (L.total_numel + 8191) / 8192;
     return static_cast<uint32_t>(std::min<uint64_t>(std::max<uint64_t>(b, 1), adacomp::kEncMaxBlocks));

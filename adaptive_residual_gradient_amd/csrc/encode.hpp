@@ -242,7 +242,11 @@ k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
 // kEncBatch rounds loaded before any of them is used.  Only wavefront-level
 // operations are used, so every wavefront ends on its own.
 constexpr int kEncBatch = 8;   // 4 and 6 measured within noise; 8 keeps the most loads in flight
-constexpr uint32_t kEncMaxBlocks = 2048;   // 8192 wavefronts: one per wavefront slot of the chip
+// 2048 wavefronts, 8 per CU.  Against 8192, this shortens the launch and the
+// finalize step every workgroup repeats (a 25 M-element, 0.36 M-survivor
+// table: finish 23 -> 15 us); finishes bound by their scattered residue
+// stores (1.07e9 elements, or 10% of elements sent) took the same time.
+constexpr uint32_t kEncMaxBlocks = 512;
 
 // Largest i in [0, n) with key(i) <= x, for key nondecreasing with
 // key(0) = 0 <= x; wavefront-uniform, and *kv = key(i).  Each round probes
