@@ -44,35 +44,47 @@ struct adacomp_plan {
 };
 
 namespace adacomp {
-template <int V>
-hipError_t launch_tile_pass(const adacomp_plan* plan, hipStream_t stream, float* residue,
-                            const float* dW, uint8_t* msg, uint2* stage, uint32_t* tile_cnt,
-                            double* tile_gsum, float* bin_max_out) {
+// NTS: non-temporal residue stores (tables past kCachedResidueMaxElems).
+template <int V, bool NTS>
+hipError_t launch_tile_pass_nts(const adacomp_plan* plan, hipStream_t stream, float* residue,
+                                const float* dW, uint8_t* msg, uint2* stage, uint32_t* tile_cnt,
+                                double* tile_gsum, float* bin_max_out) {
     const uint32_t n = static_cast<uint32_t>(plan->L.ct.by_variant[V].size());
     constexpr uint32_t CV = kVarThreads[2] * kVarVecs[2];   // float4 per chunk of shape 2
     if (V == 2 && plan->L.ct.max_span_vecs[2] <= kLongRegChunks * CV)
         // long bins of at most kLongRegChunks chunks: one bin per workgroup, held in registers
-        hipLaunchKernelGGL((k_tile_pass_long<kVarThreads[2], kVarVecs[2], kLongRegChunks>), dim3(n),
-                           dim3(kVarThreads[2]), 0, stream, plan->d_segs, plan->dct.tile_seg,
-                           plan->dct.vtiles[2], residue, dW, msg, stage, tile_cnt, tile_gsum,
-                           bin_max_out);
+        hipLaunchKernelGGL((k_tile_pass_long<kVarThreads[2], kVarVecs[2], kLongRegChunks, NTS>),
+                           dim3(n), dim3(kVarThreads[2]), 0, stream, plan->d_segs,
+                           plan->dct.tile_seg, plan->dct.vtiles[2], residue, dW, msg, stage,
+                           tile_cnt, tile_gsum, bin_max_out);
     else if (V == 2 && plan->L.ct.max_span_vecs[2] <= kLongRegChunks * 4 * CV)
         // up to 4 chunks of 1024 x 2 float4 (every L_T up to 32768): 1024-thread workgroups
-        hipLaunchKernelGGL((k_tile_pass_long<1024, kVarVecs[2], kLongRegChunks>), dim3(n),
+        hipLaunchKernelGGL((k_tile_pass_long<1024, kVarVecs[2], kLongRegChunks, NTS>), dim3(n),
                            dim3(1024), 0, stream, plan->d_segs, plan->dct.tile_seg,
                            plan->dct.vtiles[2], residue, dW, msg, stage, tile_cnt, tile_gsum,
                            bin_max_out);
     else if (V == 2)   // longer bins: one bin per workgroup, streamed twice in chunks
-        hipLaunchKernelGGL((k_tile_pass_long<kVarThreads[2], kVarVecs[2], 0>), dim3(n),
+        hipLaunchKernelGGL((k_tile_pass_long<kVarThreads[2], kVarVecs[2], 0, NTS>), dim3(n),
                            dim3(kVarThreads[2]), 0, stream, plan->d_segs, plan->dct.tile_seg,
                            plan->dct.vtiles[2], residue, dW, msg, stage, tile_cnt, tile_gsum,
                            bin_max_out);
     else
-        hipLaunchKernelGGL((k_tile_pass<kVarThreads[V], kVarVecs[V]>), dim3(n), dim3(kVarThreads[V]),
-                           plan->tile_lds_words[V] * 4, stream, plan->d_segs, plan->dct.tile_seg,
-                           plan->dct.vtiles[V], residue, dW, msg, stage, tile_cnt, tile_gsum,
-                           bin_max_out);
+        hipLaunchKernelGGL((k_tile_pass<kVarThreads[V], kVarVecs[V], NTS>), dim3(n),
+                           dim3(kVarThreads[V]), plan->tile_lds_words[V] * 4, stream,
+                           plan->d_segs, plan->dct.tile_seg, plan->dct.vtiles[V], residue, dW,
+                           msg, stage, tile_cnt, tile_gsum, bin_max_out);
     return hipGetLastError();
+}
+
+template <int V>
+hipError_t launch_tile_pass(const adacomp_plan* plan, hipStream_t stream, float* residue,
+                            const float* dW, uint8_t* msg, uint2* stage, uint32_t* tile_cnt,
+                            double* tile_gsum, float* bin_max_out) {
+    if (plan->L.total_numel > kCachedResidueMaxElems)
+        return launch_tile_pass_nts<V, true>(plan, stream, residue, dW, msg, stage, tile_cnt,
+                                             tile_gsum, bin_max_out);
+    return launch_tile_pass_nts<V, false>(plan, stream, residue, dW, msg, stage, tile_cnt,
+                                          tile_gsum, bin_max_out);
 }
 }  // namespace adacomp
 

@@ -12,11 +12,12 @@ namespace adacomp {
 
 constexpr uint32_t kSentinel = 0xFFFFFFFFu;
 
-// Non-temporal hints on the dense streams of the tile pass: residue and dW
-// are read once and the residue written once per call, so none of them
-// should displace other data from the caches (a streaming probe on this
-// chip: read-read-write 6.16 TB/s with the hints against 5.9 without).
-constexpr bool kNtLoadResidue = true, kNtLoadDw = true, kNtStoreResidue = true;
+// Non-temporal hints on the dense reads of the tile pass: residue and dW are
+// read once per call, so neither should displace other data from the caches
+// (a streaming probe on this chip: read-read-write 6.16 TB/s with the hints
+// against 5.9 without).  The residue store's hint is a template parameter of
+// the tile-pass kernels, chosen per plan (layout.hpp, kCachedResidueMaxElems).
+constexpr bool kNtLoadResidue = true, kNtLoadDw = true;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 

@@ -47,6 +47,16 @@ constexpr int kLongRegChunks = 4;
 constexpr uint32_t var_cap(int v) { return v == 2 ? kLongCap : kVarThreads[v] * kVarVecs[v] * 4; }
 constexpr uint32_t kMaxCap = 1024 * 9 * 4;   // 36864 elements: long-bin decode tiles
 constexpr uint32_t kChunkTiles = 1024;  // tiles per scan chunk (4 per thread of a 256-thread block)
+// Tables of at most this many elements write the residue in the tile pass with
+// ordinary (cached) stores, larger ones non-temporally.  The finish rewrites
+// the residue at every sent element; while the whole residue (here at most
+// 256 MB) can stay in the 256 MB Infinity Cache those partial-line stores hit
+// it.  Compress calls measured with each hint, 16.7 M-element layers at
+// L_T 50 / 500 (us): 16 M 72 / 65 cached against 81 / 72 non-temporal;
+// 32 M 120 / 105 against 140 / 122; 64 M 247 / 191 against 262 / 221;
+// 128 M 598 / 500 against 557 / 450 (there the cached stores evict data the
+// stream still needs).
+constexpr uint64_t kCachedResidueMaxElems = uint64_t(1) << 26;
 constexpr uint32_t kPrefWords = 8192;   // LDS words for per-message bin prefixes in decode
 constexpr uint64_t kAlign = 256;        // workspace sub-buffer alignment
 

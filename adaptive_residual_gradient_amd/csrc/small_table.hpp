@@ -284,19 +284,21 @@ __global__ void __launch_bounds__(256) k_compress_single(SmallArgs A) {
     __shared__ uint64_t lsz[4], lns[4];
     __shared__ uint32_t last;
 
+    // Small tables keep their residue stores cached (see kCachedResidueMaxElems).
+    static_assert(ADACOMP_SMALL_TABLE_MAX_SPAN <= kCachedResidueMaxElems, "small tables are cached");
     if (blockIdx.x < A.n0) {
         TileRegs<kVarVecs[0]> t;
         load_tile<256, kVarVecs[0]>(t, A.segs, A.tile_seg, A.vtiles0, blockIdx.x, A.residue, A.dW);
-        process_tile<256, kVarVecs[0]>(t, dyn, A.segs, A.tile_seg, A.residue, A.msg,
-                                       const_cast<uint2*>(A.stage), A.tile_cnt, A.tile_gsum,
-                                       A.bin_max_out, ch_tot);
+        process_tile<256, kVarVecs[0], false>(t, dyn, A.segs, A.tile_seg, A.residue, A.msg,
+                                              const_cast<uint2*>(A.stage), A.tile_cnt,
+                                              A.tile_gsum, A.bin_max_out, ch_tot);
     } else {
         TileRegs<kVarVecs[1]> t;
         load_tile<256, kVarVecs[1]>(t, A.segs, A.tile_seg, A.vtiles1, blockIdx.x - A.n0,
                                     A.residue, A.dW);
-        process_tile<256, kVarVecs[1]>(t, dyn, A.segs, A.tile_seg, A.residue, A.msg,
-                                       const_cast<uint2*>(A.stage), A.tile_cnt, A.tile_gsum,
-                                       A.bin_max_out, ch_tot);
+        process_tile<256, kVarVecs[1], false>(t, dyn, A.segs, A.tile_seg, A.residue, A.msg,
+                                              const_cast<uint2*>(A.stage), A.tile_cnt,
+                                              A.tile_gsum, A.bin_max_out, ch_tot);
     }
     // Publish: every wavefront releases its own stores at agent scope (a
     // workgroup barrier alone does not wait for them to leave the CU), the

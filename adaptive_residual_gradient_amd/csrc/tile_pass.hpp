@@ -92,7 +92,7 @@ __device__ __forceinline__ void load_tile(TileRegs<VPT>& t, const SegDev* __rest
 // 2 * bpt_max + 1 words (bin maxima, then bin boundaries), followed, when
 // the plan has hard local selection layers, by bpt_max words for each
 // bin's first maximum.
-template <int THREADS, int VPT>
+template <int THREADS, int VPT, bool NTS>
 __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* lds,
                                              const SegDev* __restrict__ segs,
                                              const uint32_t* __restrict__ tile_seg,
@@ -271,7 +271,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
         if (vm[v] == 15u) {
             f32x4 o;
             o.x = g[v][0]; o.y = g[v][1]; o.z = g[v][2]; o.w = g[v][3];
-            store4<kNtStoreResidue>(residue + e0, o);
+            store4<NTS>(residue + e0, o);
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
@@ -305,8 +305,8 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
     }
 }
 
-// One workgroup per tile.
-template <int THREADS, int VPT>
+// One workgroup per tile.  NTS: non-temporal residue stores.
+template <int THREADS, int VPT, bool NTS>
 __global__ void __launch_bounds__(THREADS)
 k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
             const uint32_t* __restrict__ vtiles, float* __restrict__ residue,
@@ -318,8 +318,8 @@ k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_s
     __shared__ uint32_t ch_tot[NCH];
     TileRegs<VPT> a;
     load_tile<THREADS, VPT>(a, segs, tile_seg, vtiles, blockIdx.x, residue, dW);
-    process_tile<THREADS, VPT>(a, dyn, segs, tile_seg, residue, msg, stage, tile_cnt, tile_gsum,
-                               bin_max_out, ch_tot);
+    process_tile<THREADS, VPT, NTS>(a, dyn, segs, tile_seg, residue, msg, stage, tile_cnt,
+                                    tile_gsum, bin_max_out, ch_tot);
 }
 
 // Long bins (L_T > 4093): one workgroup per bin, in chunks of THREADS x VPT
@@ -331,7 +331,7 @@ k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_s
 // second pass reads what the first one just brought on chip (non-temporal:
 // it is the last use), so HBM traffic stays near 12 B per element while bins
 // fit the caches, and only one chunk lives in registers.
-template <int THREADS, int VPT, int NCR>
+template <int THREADS, int VPT, int NCR, bool NTS>
 __global__ void __launch_bounds__(THREADS)
 k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
                  const uint32_t* __restrict__ vtiles, float* __restrict__ residue,
@@ -454,7 +454,7 @@ k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ t
             if (x0 >= 0 && x0 + 4 <= tlen) {
                 f32x4 o;
                 o.x = g[v][0]; o.y = g[v][1]; o.z = g[v][2]; o.w = g[v][3];
-                store4<kNtStoreResidue>(residue + e0, o);
+                store4<NTS>(residue + e0, o);
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
