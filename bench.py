@@ -241,7 +241,9 @@ def measure_other_workloads(A, W, dev):
     """The three other parity workloads at full size (context; the metric is
     the 1.07e9-element workload's): each runs its first 10 steps from zero
     residue on its own seeded gradients, all resident before timing; steps
-    6-10 are timed one call at a time with events (median)."""
+    6-10 are timed one call at a time with events (median).  Then the decode
+    of 16 learners' third-step messages, timed the same way after a 1 GiB
+    read each."""
     import torch
     out = {}
     for name in ("conv", "fc_lstm", "resnet50"):
@@ -262,14 +264,43 @@ def measure_other_workloads(A, W, dev):
                 times.append(a.elapsed_time(b))
         t = sorted(times)[len(times) // 2]
         total, surv, _ = A.message_header(plan, msg)
+        del dws
+        # Decode of K = 16 messages: learner k's third step from zero residue,
+        # each timed call after a 1 GiB read (median of 5).
+        msgs = []
+        for k in range(16):
+            rk = torch.zeros(n, dtype=torch.float32, device=dev)
+            for s in range(1, 4):
+                A.compress(plan, rk, W.make_dw(wl, k, s, dev), msg, ws)
+            tk, _, _ = A.message_header(plan, msg)
+            msgs.append(msg[:tk].clone())
+            del rk
+        dsum = torch.empty(n, dtype=torch.float32, device=dev)
+        dws = plan.decode_workspace(len(msgs), dev)
+        evict = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dt = []
+        for i in range(7):
+            evict.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            A.decode_accumulate(plan, msgs, dsum, False, dws)
+            b.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                dt.append(a.elapsed_time(b))
+        td = sorted(dt)[len(dt) // 2]
+        mbytes = sum(int(m.numel()) for m in msgs)
         out[wl.name] = {"elements": wl.numel, "layers": len(wl.segments),
                         "compress_launches": int(plan.info.compress_launches),
                         "compress_us": round(t * 1e3, 1),
                         "Gelem_per_s": round(wl.numel / (t * 1e-3) / 1e9, 1),
                         "GBps": round((12.0 * wl.numel + total) / (t * 1e-3) / 1e9, 1),
-                        "survivors_step10": int(surv)}
+                        "survivors_step10": int(surv),
+                        "decode_messages": len(msgs), "decode_message_bytes": mbytes,
+                        "decode_us": round(td * 1e3, 1),
+                        "decode_GBps": round((4.0 * wl.numel + mbytes) / (td * 1e-3) / 1e9, 1)}
         plan.close()
-        del dws, r, msg, ws
+        del r, msg, ws, msgs, dsum, dws, evict
     torch.cuda.empty_cache()
     return out
 
@@ -426,8 +457,9 @@ def main():
                     help="instead of the benchmark, time the compress of the 100 x 1000 layer "
                          "with each finish (default, three-kernel, single launch); one JSON line")
     ap.add_argument("--other-workloads", action="store_true",
-                    help="instead of the benchmark, time the compress of the conv-stack, FC/LSTM "
-                         "and ResNet-50 tables (steps 6-10 from zero residue); one JSON line")
+                    help="instead of the benchmark, time the compress (steps 6-10 from zero "
+                         "residue) and a K = 16 decode of the conv-stack, FC/LSTM and ResNet-50 "
+                         "tables; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device copy of 1 GiB (a known-size reference "
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
