@@ -219,3 +219,15 @@ def test_header_is_plain_c_and_host_calls_work(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout + out.stderr
     assert "OK host-only calls" in out.stdout
+
+
+def test_bench_refuses_several_gpus():
+    """The benchmark measures one GPU: asked for more it prints one JSON line
+    saying so and exits with status 2, before touching any device."""
+    import json
+    import sys
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
