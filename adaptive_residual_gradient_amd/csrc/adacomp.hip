@@ -632,8 +632,8 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
         tm.mark(ADACOMP_STAGE_DECODE_COUNT);
     }
     {
-        hipLaunchKernelGGL(adacomp::k_decode_base, dim3(1), dim3(256), 0, stream, mp, K,
-                           plan->d_segs, L.nseg, L.plan_hash, DC, dw);
+        hipLaunchKernelGGL(adacomp::k_decode_base, dim3(std::max<uint32_t>(K, 1u)), dim3(256), 0,
+                           stream, mp, K, plan->d_segs, L.nseg, L.plan_hash, DC, dw);
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.mark(ADACOMP_STAGE_DECODE_BASE);
     }

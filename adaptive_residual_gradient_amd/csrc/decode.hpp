@@ -107,50 +107,60 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
     if (threadIdx.x == 0) ws.dchunk_cnt[uint64_t(k) * DC + c] = base;
 }
 
-// One block: message validity, per-segment s and entry offsets, chunk bases.
+// One block per message (at least one block): the message's validity,
+// per-segment s and entry offsets, chunk bases.  Block 0 also counts the
+// foreign messages into the status word.
 __global__ void __launch_bounds__(256)
 k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, uint32_t nseg,
               uint32_t plan_hash, uint32_t DC, DecodeWs ws) {
-    __shared__ uint32_t valid[ADACOMP_MAX_MESSAGES];
-    __shared__ uint32_t bad;
-    if (threadIdx.x == 0) bad = 0;
-    __syncthreads();
-    for (uint32_t k = threadIdx.x; k < K; k += 256) {
-        const bool ok = header_matches(msgs.p[k], nseg, plan_hash);
-        valid[k] = ok ? 1u : 0u;
-        ws.dvalid[k] = ok ? 1u : 0u;
-        if (!ok) atomicAdd(&bad, 1u);
+    __shared__ uint32_t valid, bad;
+    const uint32_t k = blockIdx.x;
+    if (threadIdx.x == 0) {
+        bad = 0;
+        valid = 0;
+        if (k < K) {
+            valid = header_matches(msgs.p[k], nseg, plan_hash) ? 1u : 0u;
+            ws.dvalid[k] = valid;
+        }
     }
     __syncthreads();
-    for (uint64_t i = threadIdx.x; i < uint64_t(K) * nseg; i += 256) {
-        const uint32_t k = uint32_t(i / nseg), l = uint32_t(i % nseg);
-        float s = 0.0f;
-        uint64_t eoff = 0;
-        if (valid[k]) {
-            const uint8_t* d = msgs.p[k] + 32 + 16 * uint64_t(l);
-            s = *reinterpret_cast<const float*>(d);
-            eoff = *reinterpret_cast<const uint64_t*>(d + 8);
-        }
-        ws.dseg_s[i] = s;
-        ws.dseg_eoff[i] = eoff;
-        const SegDev sg = segs[l];
-        const uint64_t c0 = uint64_t(k) * DC + sg.dt.chunk_begin;
-        uint32_t run = 0;
-        // Chunk totals eight at a time, all requested before any is used.
-        for (uint32_t c = 0; c < sg.dt.nchunks; c += 8) {
-            uint32_t v[8];
+    if (k == 0) {
+        for (uint32_t j = threadIdx.x; j < K; j += 256)
+            if (!header_matches(msgs.p[j], nseg, plan_hash)) atomicAdd(&bad, 1u);
+    }
+    if (k < K) {
+        for (uint32_t l = threadIdx.x; l < nseg; l += 256) {
+            const uint64_t i = uint64_t(k) * nseg + l;
+            float s = 0.0f;
+            uint64_t eoff = 0;
+            if (valid) {
+                const uint8_t* d = msgs.p[k] + 32 + 16 * uint64_t(l);
+                s = *reinterpret_cast<const float*>(d);
+                eoff = *reinterpret_cast<const uint64_t*>(d + 8);
+            }
+            ws.dseg_s[i] = s;
+            ws.dseg_eoff[i] = eoff;
+            const SegDev sg = segs[l];
+            const uint64_t c0 = uint64_t(k) * DC + sg.dt.chunk_begin;
+            uint32_t run = 0;
+            // Chunk totals eight at a time, all requested before any is used.
+            for (uint32_t c = 0; c < sg.dt.nchunks; c += 8) {
+                uint32_t v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                v[u] = c + u < sg.dt.nchunks ? ws.dchunk_cnt[c0 + c + u] : 0u;
+                for (int u = 0; u < 8; ++u)
+                    v[u] = c + u < sg.dt.nchunks ? ws.dchunk_cnt[c0 + c + u] : 0u;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (c + u < sg.dt.nchunks) ws.dchunk_base[c0 + c + u] = run;
-                run += v[u];
+                for (int u = 0; u < 8; ++u) {
+                    if (c + u < sg.dt.nchunks) ws.dchunk_base[c0 + c + u] = run;
+                    run += v[u];
+                }
             }
         }
     }
-    __syncthreads();
-    if (threadIdx.x == 0) *ws.status = bad;
+    if (k == 0) {
+        __syncthreads();
+        if (threadIdx.x == 0) *ws.status = bad;
+    }
 }
 
 // Index word at byte address a (w = 8 or 16 bits), read as the aligned
