@@ -623,17 +623,23 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
         accumulate = 0;
     }
 
+    adacomp::MsgGeom geo{};
+    geo.nseg = L.nseg;
+    geo.plan_hash = L.plan_hash;
+    geo.entries_begin = L.entries_begin;
+    geo.capacity = L.capacity;
+
     CallTimer tm(timer, stream, call_stage);
     {
         hipLaunchKernelGGL(adacomp::k_decode_count, dim3(DC, K), dim3(256), 0, stream, mp,
                            plan->d_segs, plan->ddt.chunk_tile_begin, plan->ddt.chunk_seg, DT, DC,
-                           L.nseg, L.plan_hash, dw);
+                           geo, dw);
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.mark(ADACOMP_STAGE_DECODE_COUNT);
     }
     {
-        hipLaunchKernelGGL(adacomp::k_decode_base, dim3(std::max<uint32_t>(K, 1u)), dim3(256), 0,
-                           stream, mp, K, plan->d_segs, L.nseg, L.plan_hash, DC, dw);
+        hipLaunchKernelGGL(adacomp::k_decode_base, dim3(K), dim3(256), 0, stream, mp, K,
+                           plan->d_segs, geo, DC, dw);
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.mark(ADACOMP_STAGE_DECODE_BASE);
     }
@@ -643,21 +649,27 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
             if (n == 0) continue;
             const uint32_t ps = L.dt.max_bpt[v] + 1;
             const uint32_t KG = adacomp::decode_group(K, ps);
-            if (v == 0) {   // the tile fits in LDS
+            if (v == 0) {   // tiles of at most 4096 elements: bits per message, then ordered sums
                 const uint32_t acc_words = L.dt.max_span_vecs[0] * 4;
-                const uint32_t lds = adacomp::decode_lds_bytes(acc_words, K, KG, ps, 4);
-                if (opt == adacomp::kOptSgd)
-                    hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, adacomp::kOptSgd>), dim3(n),
-                                       dim3(256), lds, stream, mp, K, KG, ps, plan->ddesc[0], DT, DC,
-                                       L.nseg, dw, nullptr, 0, acc_words, op);
-                else if (opt == adacomp::kOptAdam)
-                    hipLaunchKernelGGL((adacomp::k_decode_apply<256, true, adacomp::kOptAdam>), dim3(n),
-                                       dim3(256), lds, stream, mp, K, KG, ps, plan->ddesc[0], DT, DC,
-                                       L.nseg, dw, nullptr, 0, acc_words, op);
-                else
-                    hipLaunchKernelGGL((adacomp::k_decode_apply<256, true>), dim3(n), dim3(256), lds,
-                                       stream, mp, K, KG, ps, plan->ddesc[0], DT, DC, L.nseg, dw, out,
-                                       accumulate, acc_words, op);
+                const uint32_t kg = adacomp::decode_tiles_group(K, ps);
+                const bool sep = kg < K || (accumulate != 0 && !fused);
+                const uint32_t lds = adacomp::decode_tiles_lds_bytes(acc_words, K, kg, ps, sep);
+                float* dst = fused ? nullptr : out;
+                const int acc = fused ? 0 : accumulate;
+#define ADACOMP_TILES(SEP, OPT)                                                                    \
+    hipLaunchKernelGGL((adacomp::k_decode_tiles<SEP, OPT>), dim3(n), dim3(256), lds, stream, mp, K, \
+                       kg, ps, plan->ddesc[0], DT, DC, L.nseg, dw, dst, acc, acc_words, op)
+                if (opt == adacomp::kOptSgd) {
+                    if (sep) ADACOMP_TILES(true, adacomp::kOptSgd);
+                    else ADACOMP_TILES(false, adacomp::kOptSgd);
+                } else if (opt == adacomp::kOptAdam) {
+                    if (sep) ADACOMP_TILES(true, adacomp::kOptAdam);
+                    else ADACOMP_TILES(false, adacomp::kOptAdam);
+                } else {
+                    if (sep) ADACOMP_TILES(true, adacomp::kOptNone);
+                    else ADACOMP_TILES(false, adacomp::kOptNone);
+                }
+#undef ADACOMP_TILES
             } else if (long_decode_in_lds(L, K, KG, ps, opt)) {
                 // long bins, the whole tile accumulated in LDS (one 1024-thread workgroup per
                 // CU) and written once, or stepped by the optimizer

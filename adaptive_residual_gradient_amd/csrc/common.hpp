@@ -35,6 +35,39 @@ __device__ __forceinline__ void store4(float* p, f32x4 v) {
     else *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// DPP lane moves (VALU, no LDS round trip).  Lanes without a source, and
+// lanes of rows masked off, receive `old`.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROWS, 0xf, false));
+}
+// lane l receives lane l+1 (wave_shl:1); lane 63 receives old
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t old, uint32_t v) { return dpp_u32<0x130>(old, v); }
+// lane l receives lane l-1 (wave_shr:1); lane 0 receives old
+__device__ __forceinline__ uint32_t from_prev_lane(uint32_t old, uint32_t v) { return dpp_u32<0x138>(old, v); }
+
+// Inclusive sum over the 64 lanes of a wavefront: row shifts 1, 2, 4, 8 scan
+// within rows of 16 lanes, the row broadcasts of lanes 15/47 and then 31
+// carry across rows.
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t v) {
+    v += dpp_u32<0x111>(0u, v);
+    v += dpp_u32<0x112>(0u, v);
+    v += dpp_u32<0x114>(0u, v);
+    v += dpp_u32<0x118>(0u, v);
+    v += dpp_u32<0x142, 0xa>(0u, v);
+    v += dpp_u32<0x143, 0xc>(0u, v);
+    return v;
+}
+// The same within each row of 16 lanes only.
+__device__ __forceinline__ uint32_t row_incl_add(uint32_t v) {
+    v += dpp_u32<0x111>(0u, v);
+    v += dpp_u32<0x112>(0u, v);
+    v += dpp_u32<0x114>(0u, v);
+    v += dpp_u32<0x118>(0u, v);
+    return v;
+}
+
 __device__ __forceinline__ uint64_t rup16(uint64_t x) { return (x + 15u) & ~uint64_t(15); }
 
 __device__ __forceinline__ void put_word(uint8_t* p, uint32_t wb, uint32_t v) {

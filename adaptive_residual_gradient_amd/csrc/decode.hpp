@@ -28,12 +28,29 @@ struct DecodeWs {
     uint32_t* dvalid;     // [K]
 };
 
-__device__ __forceinline__ bool header_matches(const uint8_t* m, uint32_t nseg, uint32_t plan_hash) {
+// What a message must satisfy before any byte past its header is read: the
+// plan's magic, version, layer count and table hash, and a total length
+// between the end of the count regions and the plan's capacity, a multiple
+// of 16.  Every count word then lies inside the message.
+struct MsgGeom {
+    uint32_t nseg;
+    uint32_t plan_hash;
+    uint64_t entries_begin;   // end of the count regions
+    uint64_t capacity;        // largest message of the plan
+};
+
+__device__ __forceinline__ bool header_matches(const uint8_t* m, const MsgGeom& g) {
+    const uint64_t total = *reinterpret_cast<const uint64_t*>(m + 16);
     return *reinterpret_cast<const uint32_t*>(m) == 0x43414441u &&
            *reinterpret_cast<const uint16_t*>(m + 4) == 1 &&
-           *reinterpret_cast<const uint32_t*>(m + 8) == nseg &&
-           *reinterpret_cast<const uint32_t*>(m + 12) == plan_hash;
+           *reinterpret_cast<const uint32_t*>(m + 8) == g.nseg &&
+           *reinterpret_cast<const uint32_t*>(m + 12) == g.plan_hash &&
+           total >= g.entries_begin && total <= g.capacity && (total & 15u) == 0u;
 }
+
+// A chunk total with this bit set: some tile of the chunk counts more
+// transmitted elements than it has elements (a corrupt message).
+constexpr uint32_t kChunkBad = 0x80000000u;
 
 // Sum of the count words in message bytes [a0, a1), read as the aligned
 // 16-byte blocks that cover them (count regions start 16-byte aligned and
@@ -71,15 +88,21 @@ __device__ __forceinline__ uint32_t sum_count_words(const uint8_t* m, uint64_t a
 __global__ void __launch_bounds__(256)
 k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
                const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ chunk_seg,
-               uint32_t DT, uint32_t DC, uint32_t nseg, uint32_t plan_hash, DecodeWs ws) {
+               uint32_t DT, uint32_t DC, MsgGeom geo, DecodeWs ws) {
     __shared__ uint32_t lw[4];
+    __shared__ uint32_t bad;
     const uint32_t c = blockIdx.x, k = blockIdx.y;
     const uint8_t* m = msgs.p[k];
+    if (threadIdx.x == 0) {
+        bad = 0;
+        if (c == 0 && k == 0) *ws.status = 0;   // k_decode_base counts the rejected messages
+    }
     // A message made for another table is never read past its header.
-    const bool ok = header_matches(m, nseg, plan_hash);
+    const bool ok = header_matches(m, geo);
     const SegDev sg = segs[chunk_seg[c]];
     const uint32_t tb = chunk_tile_begin[c], n = chunk_tile_begin[c + 1] - tb;
     uint32_t cnt[4];
+    bool over = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t t = uint32_t(i) * 256u + threadIdx.x;
@@ -89,9 +112,17 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
             const uint32_t nb = min(sg.dt.bpt, sg.nbins - first_bin);
             const uint64_t a0 = sg.count_off + uint64_t(first_bin) * sg.wb;
             s = sum_count_words(m, a0, a0 + uint64_t(nb) * sg.wb, sg.wb);
+            // A tile never sends more elements than it holds.
+            const uint64_t e0 = uint64_t(first_bin) * sg.lt;
+            const uint64_t elems = min(uint64_t(nb) * sg.lt, sg.numel - e0);
+            if (s > elems) {
+                over = true;
+                s = 0;
+            }
         }
         cnt[i] = s;
     }
+    if (over) atomicOr(&bad, 1u);
     uint32_t base = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -104,62 +135,69 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
         }
         base += total;
     }
-    if (threadIdx.x == 0) ws.dchunk_cnt[uint64_t(k) * DC + c] = base;
+    __syncthreads();
+    if (threadIdx.x == 0) ws.dchunk_cnt[uint64_t(k) * DC + c] = base | (bad ? kChunkBad : 0u);
 }
 
-// One block per message (at least one block): the message's validity,
-// per-segment s and entry offsets, chunk bases.  Block 0 also counts the
-// foreign messages into the status word.
+// One block per message: per-segment s and entry offsets, chunk bases, and
+// the message's validity.  A message is decoded only if its header matches
+// (header_matches) and, for every segment, its directory entry is
+// consistent with the count words: entry offset 16-byte aligned and at or
+// past the count regions, survivors at most the segment's elements and equal
+// to the sum of its count words, no tile counting more than it holds, and
+// the entry region (padded to 16 bytes) inside the message's total length.
+// Then every entry word a decode kernel reads lies inside the message.  A
+// rejected message contributes nothing and is counted in the status word
+// (reset by k_decode_count).
 __global__ void __launch_bounds__(256)
-k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, uint32_t nseg,
-              uint32_t plan_hash, uint32_t DC, DecodeWs ws) {
-    __shared__ uint32_t valid, bad;
+k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, MsgGeom geo,
+              uint32_t DC, DecodeWs ws) {
+    __shared__ uint32_t fail;
     const uint32_t k = blockIdx.x;
-    if (threadIdx.x == 0) {
-        bad = 0;
-        valid = 0;
-        if (k < K) {
-            valid = header_matches(msgs.p[k], nseg, plan_hash) ? 1u : 0u;
-            ws.dvalid[k] = valid;
-        }
-    }
+    const uint8_t* m = msgs.p[k];
+    if (threadIdx.x == 0) fail = header_matches(m, geo) ? 0u : 1u;
     __syncthreads();
-    if (k == 0) {
-        for (uint32_t j = threadIdx.x; j < K; j += 256)
-            if (!header_matches(msgs.p[j], nseg, plan_hash)) atomicAdd(&bad, 1u);
-    }
-    if (k < K) {
-        for (uint32_t l = threadIdx.x; l < nseg; l += 256) {
-            const uint64_t i = uint64_t(k) * nseg + l;
-            float s = 0.0f;
-            uint64_t eoff = 0;
-            if (valid) {
-                const uint8_t* d = msgs.p[k] + 32 + 16 * uint64_t(l);
-                s = *reinterpret_cast<const float*>(d);
-                eoff = *reinterpret_cast<const uint64_t*>(d + 8);
-            }
-            ws.dseg_s[i] = s;
-            ws.dseg_eoff[i] = eoff;
-            const SegDev sg = segs[l];
-            const uint64_t c0 = uint64_t(k) * DC + sg.dt.chunk_begin;
-            uint32_t run = 0;
-            // Chunk totals eight at a time, all requested before any is used.
-            for (uint32_t c = 0; c < sg.dt.nchunks; c += 8) {
-                uint32_t v[8];
+    const bool hdr_ok = fail == 0u;
+    const uint64_t total = hdr_ok ? *reinterpret_cast<const uint64_t*>(m + 16) : 0u;
+    bool bad = false;
+    for (uint32_t l = threadIdx.x; l < geo.nseg; l += 256) {
+        const uint64_t i = uint64_t(k) * geo.nseg + l;
+        const SegDev sg = segs[l];
+        float s = 0.0f;
+        uint64_t eoff = 0;
+        uint32_t nsurv = 0;
+        if (hdr_ok) {
+            const uint8_t* d = m + 32 + 16 * uint64_t(l);
+            s = *reinterpret_cast<const float*>(d);
+            nsurv = *reinterpret_cast<const uint32_t*>(d + 4);
+            eoff = *reinterpret_cast<const uint64_t*>(d + 8);
+            bad |= (eoff & 15u) != 0u || eoff < geo.entries_begin || uint64_t(nsurv) > sg.numel ||
+                   eoff > total || rup16(uint64_t(nsurv) * sg.wb) > total - eoff;
+        }
+        ws.dseg_s[i] = s;
+        ws.dseg_eoff[i] = eoff;
+        const uint64_t c0 = uint64_t(k) * DC + sg.dt.chunk_begin;
+        uint64_t run = 0;
+        // Chunk totals eight at a time, all requested before any is used.
+        for (uint32_t c = 0; c < sg.dt.nchunks; c += 8) {
+            uint32_t v[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    v[u] = c + u < sg.dt.nchunks ? ws.dchunk_cnt[c0 + c + u] : 0u;
+            for (int u = 0; u < 8; ++u)
+                v[u] = c + u < sg.dt.nchunks ? ws.dchunk_cnt[c0 + c + u] : 0u;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    if (c + u < sg.dt.nchunks) ws.dchunk_base[c0 + c + u] = run;
-                    run += v[u];
-                }
+            for (int u = 0; u < 8; ++u) {
+                if (c + u < sg.dt.nchunks) ws.dchunk_base[c0 + c + u] = uint32_t(run);
+                bad |= (v[u] & kChunkBad) != 0u;
+                run += v[u] & ~kChunkBad;
             }
         }
+        if (hdr_ok) bad |= run != nsurv;
     }
-    if (k == 0) {
-        __syncthreads();
-        if (threadIdx.x == 0) *ws.status = bad;
+    if (bad) atomicOr(&fail, 1u);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        ws.dvalid[k] = fail == 0u ? 1u : 0u;
+        if (fail) atomicAdd(ws.status, 1u);
     }
 }
 
@@ -477,6 +515,521 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
             f32x4 wq = load4<true>(op.w + e0), mq = load4<true>(op.m + e0), vq = {0.f, 0.f, 0.f, 0.f};
             if (OPT == kOptAdam) vq = load4<true>(op.v + e0);
             opt_apply<OPT>(a, wq, mq, vq, op, e0, int(vi * 4) - int(lead), int(tlen));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode of tiles of whole bins of at most kDecCap elements (L_T <= 4093),
+// 256 threads, without ordered LDS additions.
+//
+// Messages are taken in groups of at most kMaskMsgs.  For a group, every
+// entry sets, with an LDS atomic OR, two bits in the 32-bit word of its
+// element: bit kk (message kk of the group sends the element) and bit
+// 16 + kk (with a negative sign).  Bits of different messages never collide,
+// so the order of the atomics does not matter and every entry of the tile is
+// placed in parallel.  Then the thread owning an element (float4 slots tid,
+// tid + 256, ...) walks its hit bits in ascending message order and adds
+// +s or -s one float32 addition at a time: the same additions, in the same
+// order, as summing the messages one after the other.
+//
+// Entry words are read as the aligned 16-byte blocks covering each message's
+// run of entries for the tile (a message's entries for a tile are contiguous:
+// bin-major, ascending index), so the loads are coalesced and every lane
+// gets 8 (16-bit words) or 16 (8-bit words) consecutive entries.  The bin of
+// a block's first entry comes from a binary search of that message's count
+// prefix over the tile's bins; the following entries advance the bin
+// linearly.
+//
+// SEP = false (K <= kMaskMsgs, sum from +0): one LDS word per element holds
+// the group's bits and is then overwritten by the element's sum (an element
+// no message sends keeps 0, the bits of +0.0f).  SEP = true (more messages,
+// or out += sum): a second LDS array holds each element's running sum.
+// OPT != kOptNone: the sums are not written; the tile's weights and
+// optimizer state (requested when the tile starts) take one step.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kMaskMsgs = 16;
+constexpr int kBlkBatch = 2;   // 16-byte entry blocks per thread requested together
+
+// Dynamic LDS bytes of k_decode_tiles: acc_words mask words (and as many sum
+// words with SEP), per message its address, per group message its first
+// entry's address, entry count and s, and the group's bin prefixes.
+inline uint32_t decode_tiles_lds_bytes(uint32_t acc_words, uint32_t K, uint32_t KG,
+                                       uint32_t pstride, bool sep) {
+    const uint32_t accw = (acc_words + 3u) & ~3u;
+    return 4u * (accw * (sep ? 2u : 1u) + 2u * K + 2u * KG + 2u * KG + KG * pstride);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4* global_u32x4_ptr;
+
+// The entry words of one 16-byte block of a message's run for the tile that
+// lie in the block's word window [wlo, whi): v holds the block, i0 the index
+// (within the message's run for this tile) of the block's first word
+// (negative when the run starts inside the block), n the run's length, pk
+// the message's exclusive count prefix over the tile's bins (pk[nb] = n), wb
+// the word bytes (1 or 2).  The block is shifted down to the window's first
+// word in one step, then one word at a time.
+template <class PK>
+__device__ __forceinline__ void place_window(const u32x4& v, int i0, uint32_t wlo, uint32_t whi,
+                                             uint32_t n, const PK* pk, uint32_t nb, uint32_t lt,
+                                             uint32_t tlen, uint32_t lead, uint32_t wb, uint32_t hit,
+                                             uint32_t* mask) {
+    const uint32_t wbits = 8u * wb, top = wbits - 1u;
+    const uint32_t wmask = (1u << wbits) - 1u, imask = (1u << top) - 1u;
+    const int first = max(i0 + int(wlo), 0);
+    const int last = min(i0 + int(whi), int(n));
+    if (first >= last) return;
+    // bin of the first entry: largest b < nb with pk[b] <= first
+    uint32_t lo = 0, hi = nb;
+    while (hi - lo > 1u) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (uint32_t(pk[mid]) <= uint32_t(first)) lo = mid; else hi = mid;
+    }
+    uint32_t b = lo, pn = pk[b + 1];
+    uint64_t w0 = uint64_t(v.x) | (uint64_t(v.y) << 32), w1 = uint64_t(v.z) | (uint64_t(v.w) << 32);
+    const uint32_t sbits = uint32_t(first - i0) * wbits;   // 0 .. 120
+    if (sbits >= 64u) {
+        w0 = w1 >> (sbits - 64u);
+        w1 = 0;
+    } else if (sbits != 0u) {
+        w0 = (w0 >> sbits) | (w1 << (64u - sbits));
+        w1 >>= sbits;
+    }
+#pragma unroll 1
+    for (int i = first; i < last; ++i) {
+        const uint32_t word = uint32_t(w0) & wmask;
+        w0 = (w0 >> wbits) | (w1 << (64u - wbits));
+        w1 >>= wbits;
+        while (uint32_t(i) >= pn && b + 1u < nb) {
+            ++b;
+            pn = pk[b + 1];
+        }
+        const uint32_t idx = word & imask;
+        const uint32_t x = b * lt + idx;
+        if (idx < lt && x < tlen) atomicOr(&mask[x + lead], (word >> top) ? hit | (hit << 16) : hit);
+    }
+}
+
+// The same for a window of at most 4 words, unrolled, keeping each placed
+// entry's LDS slot (x + lead) in xs (kNoSlot where no entry was placed) for
+// the entry-owned sums.
+constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
+template <class PK>
+__device__ __forceinline__ void place_window4(const u32x4& v, int i0, uint32_t wlo, uint32_t whi,
+                                              uint32_t n, const PK* pk, uint32_t nb, uint32_t lt,
+                                              uint32_t tlen, uint32_t lead, uint32_t wb, uint32_t hit,
+                                              uint32_t* mask, uint32_t (&xs)[4]) {
+    const uint32_t wbits = 8u * wb, top = wbits - 1u;
+    const uint32_t wmask = (1u << wbits) - 1u, imask = (1u << top) - 1u;
+    const int first = max(i0 + int(wlo), 0);
+    const int last = min(i0 + int(whi), int(n));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xs[e] = kNoSlot;
+    if (first >= last) return;
+    uint32_t lo = 0, hi = nb;
+    while (hi - lo > 1u) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (uint32_t(pk[mid]) <= uint32_t(first)) lo = mid; else hi = mid;
+    }
+    uint32_t b = lo, pn = pk[b + 1];
+    uint64_t w0 = uint64_t(v.x) | (uint64_t(v.y) << 32), w1 = uint64_t(v.z) | (uint64_t(v.w) << 32);
+    const uint32_t sbits = uint32_t(first - i0) * wbits;   // 0 .. 120
+    if (sbits >= 64u) {
+        w0 = w1 >> (sbits - 64u);
+        w1 = 0;
+    } else if (sbits != 0u) {
+        w0 = (w0 >> sbits) | (w1 << (64u - sbits));
+        w1 >>= sbits;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = first + e;
+        const uint32_t word = uint32_t(w0 >> (uint32_t(e) * wbits)) & wmask;
+        if (i < last) {
+            while (uint32_t(i) >= pn && b + 1u < nb) {
+                ++b;
+                pn = pk[b + 1];
+            }
+            const uint32_t idx = word & imask;
+            const uint32_t x = b * lt + idx;
+            if (idx < lt && x < tlen) {
+                atomicOr(&mask[x + lead], (word >> top) ? hit | (hit << 16) : hit);
+                xs[e] = x + lead;
+            }
+        }
+    }
+}
+
+// Messages per group of k_decode_tiles: at most kMaskMsgs, and as many bin
+// prefixes as fit in kTilesPrefWords LDS words (at least one message).
+constexpr uint32_t kTilesPrefWords = 4096;
+inline uint32_t decode_tiles_group(uint32_t K, uint32_t pstride) {
+    uint32_t kg = kTilesPrefWords / pstride;
+    if (kg > kMaskMsgs) kg = kMaskMsgs;
+    if (kg > K) kg = K;
+    return kg < 1u ? 1u : kg;
+}
+
+template <bool SEP, int OPT>
+__global__ void __launch_bounds__(256)
+k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
+               const DecDesc* __restrict__ descs, uint32_t DT, uint32_t DC, uint32_t nseg,
+               DecodeWs ws, float* __restrict__ out, int accumulate, uint32_t acc_words,
+               OptParams op) {
+    constexpr int THREADS = 256, NW = THREADS / 64;
+    constexpr uint32_t NS = kDecCap / 4 / THREADS;   // float4 slots per thread
+    constexpr bool FUSED = OPT != kOptNone;
+    extern __shared__ f32x4 dyn4[];
+    const uint32_t accw = (acc_words + 3u) & ~3u;
+    uint32_t* mask = reinterpret_cast<uint32_t*>(dyn4);          // [accw]
+    float* sums = reinterpret_cast<float*>(mask + accw);         // [accw] with SEP
+    uint64_t* mptr = reinterpret_cast<uint64_t*>(mask + accw * (SEP ? 2u : 1u));   // [K]
+    uint64_t* abase = mptr + K;                                  // [KG]
+    uint32_t* nent = reinterpret_cast<uint32_t*>(abase + KG);    // [KG]
+    float* ks = reinterpret_cast<float*>(nent + KG);             // [KG]
+    uint32_t* pref = reinterpret_cast<uint32_t*>(ks + KG);       // [KG][pstride]
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const DecDesc dd = descs[blockIdx.x];
+    const uint64_t v0 = dd.t0 & ~uint64_t(3);
+    const uint32_t lead = uint32_t(dd.t0 - v0);
+    const uint32_t nvec = (lead + dd.tlen + 3u) >> 2;
+    const uint32_t nb = dd.nb, tlen = dd.tlen, wb = dd.wb, lt = dd.lt;
+    // Message addresses (0 for a rejected message; K <= THREADS): both words
+    // requested together, without a branch, in the descriptor's round trip.
+    if (tid < int(K)) {
+        const uint64_t p = reinterpret_cast<uint64_t>(msgs.p[tid]);
+        const uint32_t ok = ws.dvalid[tid];
+        mptr[tid] = p & (uint64_t(0) - uint64_t(ok != 0u));
+    }
+    // An always readable address for loads whose result is not used.
+    const uint64_t dummy = reinterpret_cast<uint64_t>(ws.dvalid);
+
+    // This thread's float4 slots: starting values (out for out += sum) or
+    // weights and optimizer state, requested now.
+    f32x4 init[SEP ? NS : 1], wq[FUSED ? NS : 1], mq[FUSED ? NS : 1], vq[OPT == kOptAdam ? NS : 1];
+#pragma unroll
+    for (uint32_t j = 0; j < NS; ++j) {
+        const uint32_t vi = uint32_t(tid) + THREADS * j;
+        const uint64_t e0 = v0 + uint64_t(vi) * 4u;
+        const int x0 = int(vi * 4) - int(lead);
+        if (SEP) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            if (accumulate && vi < nvec) {
+                if (x0 >= 0 && x0 + 4 <= int(tlen)) {
+                    a = load4<true>(out + e0);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (x0 + c >= 0 && x0 + c < int(tlen)) a[c] = out[e0 + c];
+                }
+            }
+            init[SEP ? j : 0] = a;
+        }
+        if (FUSED && vi < nvec) {
+            wq[FUSED ? j : 0] = load4<true>(op.w + e0);
+            mq[FUSED ? j : 0] = load4<true>(op.m + e0);
+            if (OPT == kOptAdam) vq[OPT == kOptAdam ? j : 0] = load4<true>(op.v + e0);
+        }
+        if (vi < accw / 4u) reinterpret_cast<u32x4*>(mask)[vi] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    f32x4 a4[SEP ? 1 : NS];   // without SEP: this thread's sums
+    bool owned = false;       // entry-owned sums (sparse tiles, without SEP)
+    uint32_t own_x[4] = {kNoSlot, kNoSlot, kNoSlot, kNoSlot}, own_hit = 0;
+    // Without SEP there is one group (K <= KG), so the loop below is straight-line code.
+    const uint32_t ngroups = SEP ? (K + KG - 1u) / KG : 1u;
+    for (uint32_t g = 0; g < ngroups; ++g) {
+        const uint32_t k0 = g * KG;
+        const uint32_t kn = min(KG, K - k0);
+        __syncthreads();   // addresses staged; the previous group is done with pref, ks and mask
+        // ---- where each message's entries start, and the count words of the tile's bins ----
+        // Threads 0..kn-1 request their message's entry offset, entry count and s first, so that
+        // these loads and the count words below are in flight together.
+        uint64_t a_off = 0, a_msg = 0;
+        uint32_t a_n = 0;
+        float a_s = 0.0f;
+        if (tid < int(kn)) {
+            const uint32_t k = k0 + uint32_t(tid);
+            a_msg = mptr[k];
+            if (a_msg != 0u) {
+                a_off = ws.dseg_eoff[uint64_t(k) * nseg + dd.si] +
+                        (uint64_t(ws.dchunk_base[uint64_t(k) * DC + dd.chunk]) +
+                         ws.doff[uint64_t(k) * DT + dd.tile]) * wb;
+                a_n = ws.dcnt[uint64_t(k) * DT + dd.tile];
+                a_s = ws.dseg_s[uint64_t(k) * nseg + dd.si];
+            }
+        }
+        // Count words into registers, one lane per bin, then per-message prefixes by DPP scans.
+        // Every load is issued without a branch (unused lanes read `dummy`), so that all of a
+        // wavefront's loads are in flight together.
+        auto count_word = [&](uint32_t kk, uint32_t b) -> uint32_t {
+            const bool use = kk < kn && b < nb;
+            const uint64_t mb = mptr[k0 + min(kk, kn - 1u)];
+            const bool live = use && mb != 0u;
+            const uint32_t w = word_at(live ? mb + dd.count_at + uint64_t(b) * wb : dummy, wb);
+            return live ? w : 0u;
+        };
+        auto put_prefix = [&](uint32_t kk, uint32_t b, uint32_t inc) {
+            if (kk < kn && b < nb) {
+                pref[kk * pstride + b + 1u] = inc;
+                if (b == 0u) pref[kk * pstride] = 0u;
+            }
+        };
+        if (nb <= 16u) {
+            // one message per row of 16 lanes: wavefront wv, row q holds message 4 wv + q
+            const uint32_t kk = 4u * uint32_t(wv) + (uint32_t(lane) >> 4), b = uint32_t(lane) & 15u;
+            const uint32_t w = count_word(kk, b);
+            put_prefix(kk, b, row_incl_add(w));
+        } else if (nb <= 128u) {
+            // wavefront wv: messages wv + 4 m (m < 4), bins lane and 64 + lane
+            uint32_t cw[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                cw[u] = count_word(uint32_t(wv) + NW * uint32_t(u >> 1), 64u * uint32_t(u & 1) + uint32_t(lane));
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t kk = uint32_t(wv) + NW * uint32_t(m);
+                const uint32_t lo = wave_incl_add(cw[2 * m]);
+                const uint32_t hi = wave_incl_add(cw[2 * m + 1]) + __builtin_amdgcn_readlane(lo, 63);
+                put_prefix(kk, uint32_t(lane), lo);
+                put_prefix(kk, 64u + uint32_t(lane), hi);
+            }
+        } else {
+            // long runs of short bins: per message, 8 rounds of 64 bins at a time
+            for (uint32_t kk = uint32_t(wv); kk < kn; kk += NW) {
+                uint32_t carry = 0;
+                for (uint32_t b0 = 0; b0 < nb; b0 += 512u) {
+                    uint32_t cw[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) cw[u] = count_word(kk, b0 + 64u * uint32_t(u) + uint32_t(lane));
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const uint32_t inc = wave_incl_add(cw[u]) + carry;
+                        put_prefix(kk, b0 + 64u * uint32_t(u) + uint32_t(lane), inc);
+                        carry = __builtin_amdgcn_readlane(inc, 63);
+                    }
+                }
+            }
+        }
+        if (tid < int(kn)) {
+            abase[tid] = a_msg != 0u ? a_msg + a_off : 0u;
+            nent[tid] = a_n;
+            ks[tid] = a_s;
+        }
+        __syncthreads();
+
+        // ---- entries: 16-byte blocks, spread over the workgroup ----
+        {
+            // lanes 0..kn-1 of every wavefront: message kk's run and its first block
+            uint64_t ab = 0;
+            uint32_t ne = 0, nblk = 0;
+            if (uint32_t(lane) < kn) {
+                ab = abase[lane];
+                ne = nent[lane];
+                if (ne != 0u) nblk = uint32_t(((ab + uint64_t(ne) * wb + 15u) >> 4) - (ab >> 4));
+            }
+            const uint32_t incl = wave_incl_add(nblk);
+            const uint32_t bs = incl - nblk;               // first block of message `lane`
+            const uint32_t NBT = __builtin_amdgcn_readlane(incl, 63);
+            // Each block is split into 2^sh windows of 16 >> sh bytes (at least one word),
+            // as many as keep the windows within one per thread: the entries of a sparse
+            // tile then spread over the whole workgroup, one or two per thread, while a
+            // dense tile keeps whole blocks per thread.
+            uint32_t sh = 0;
+            while (sh < 3u && (NBT << (sh + 1u)) <= THREADS && (16u >> (sh + 1u)) >= wb) ++sh;
+            const uint32_t NU = NBT << sh, wbytes = 16u >> sh;
+            // Sparse tiles (one window of at most 4 words per thread) keep the slots of their
+            // entries for entry-owned sums; others sum per element afterwards.
+            owned = !SEP && NU <= THREADS && wbytes <= 4u * wb;
+            if (owned) {
+                const uint32_t u = min(uint32_t(tid), NU - 1u);
+                const uint32_t q = u >> sh;
+                uint32_t kk = 0;
+#pragma unroll
+                for (uint32_t step = kMaskMsgs / 2u; step >= 1u; step >>= 1) {
+                    const uint32_t c = kk + step;
+                    const uint32_t bc = __shfl(bs, int(min(c, kMaskMsgs - 1u)));
+                    if (c < kn && bc <= q) kk = c;
+                }
+                const uint64_t a = (uint64_t(__shfl(uint32_t(ab >> 32), int(kk))) << 32) |
+                                   __shfl(uint32_t(ab), int(kk));
+                const uint32_t nbk = __shfl(nblk, int(kk));
+                const uint32_t rel = min(q - __shfl(bs, int(kk)), nbk - 1u);
+                const uint64_t blk = nbk != 0u ? (a & ~uint64_t(15)) + 16u * uint64_t(rel)
+                                               : dummy & ~uint64_t(15);
+                const u32x4 v = *(global_u32x4_ptr)blk;
+                const uint32_t nq = __shfl(ne, int(kk));
+                const int iq = int(int64_t(blk) - int64_t(a));
+                const uint32_t sq = (u & ((1u << sh) - 1u)) * wbytes;
+                own_hit = 1u << kk;
+                if (uint32_t(tid) < NU) {
+                    const uint32_t wsh = wb == 1u ? 0u : 1u;
+                    place_window4(v, iq >> wsh, sq >> wsh, (sq + wbytes) >> wsh, nq, pref + kk * pstride, nb,
+                                  lt, tlen, lead, wb, own_hit, mask, own_x);
+                }
+            }
+            for (uint32_t u0 = owned ? NU : 0u; u0 < NU; u0 += THREADS * kBlkBatch) {   // workgroup-uniform
+                u32x4 v[kBlkBatch];
+                uint32_t kq[kBlkBatch], nq[kBlkBatch], sq[kBlkBatch];
+                int iq[kBlkBatch];
+#pragma unroll
+                for (int r = 0; r < kBlkBatch; ++r) {
+                    if (u0 + THREADS * uint32_t(r) >= NU) break;   // workgroup-uniform
+                    const uint32_t u = min(u0 + THREADS * uint32_t(r) + uint32_t(tid), NU - 1u);
+                    const uint32_t q = u >> sh;
+                    // The last message whose first block is at or before q (empty messages
+                    // share their successor's start, so the one found holds block q): fixed
+                    // steps 8, 4, 2, 1 with every lane active.  A lane shuffle reads 0 from
+                    // an inactive lane, so it must not sit in a loop whose trip count differs
+                    // between lanes.
+                    uint32_t kk = 0;
+#pragma unroll
+                    for (uint32_t step = kMaskMsgs / 2u; step >= 1u; step >>= 1) {
+                        const uint32_t c = kk + step;
+                        const uint32_t bc = __shfl(bs, int(min(c, kMaskMsgs - 1u)));
+                        if (c < kn && bc <= q) kk = c;
+                    }
+                    const uint64_t a = (uint64_t(__shfl(uint32_t(ab >> 32), int(kk))) << 32) |
+                                       __shfl(uint32_t(ab), int(kk));
+                    // kept inside message kk's blocks whatever q (a message without blocks is
+                    // never found; if it were, the always readable dummy word is read instead)
+                    const uint32_t nbk = __shfl(nblk, int(kk));
+                    const uint32_t rel = min(q - __shfl(bs, int(kk)), nbk - 1u);
+                    const uint64_t blk = nbk != 0u ? (a & ~uint64_t(15)) + 16u * uint64_t(rel)
+                                                   : dummy & ~uint64_t(15);
+                    v[r] = *(global_u32x4_ptr)blk;
+                    kq[r] = kk;
+                    nq[r] = __shfl(ne, int(kk));
+                    iq[r] = int(int64_t(blk) - int64_t(a));
+                    sq[r] = (u & ((1u << sh) - 1u)) * wbytes;   // the window's first byte
+                }
+#pragma unroll
+                for (int r = 0; r < kBlkBatch; ++r) {
+                    if (u0 + THREADS * uint32_t(r) >= NU) break;   // workgroup-uniform
+                    if (u0 + THREADS * uint32_t(r) + uint32_t(tid) >= NU) continue;
+                    const uint32_t kk = kq[r];
+                    const uint32_t wsh = wb == 1u ? 0u : 1u;
+                    place_window(v[r], iq[r] >> wsh, sq[r] >> wsh, (sq[r] + wbytes) >> wsh, nq[r],
+                                 pref + kk * pstride, nb, lt, tlen, lead, wb, 1u << kk, mask);
+                }
+            }
+        }
+        __syncthreads();   // every bit of the group is set
+
+        // ---- sums: each thread its own elements, hits in message order ----
+        if (!SEP && owned) {
+            // Entry-owned: the entry of an element's lowest-numbered message adds all of the
+            // element's hits in message order and writes the float over the bits, once every
+            // entry has read its element's bits.  An element no message sends keeps 0, +0.0f.
+            float r[4];
+            uint32_t mine = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r[e] = 0.0f;
+                if (own_x[e] != kNoSlot) {
+                    const uint32_t m = mask[own_x[e]];
+                    if (((m & 0xFFFFu) & (own_hit - 1u)) == 0u) {
+                        mine |= 1u << e;
+                        uint32_t h = m & 0xFFFFu;
+                        float acc = 0.0f;
+                        while (h != 0u) {
+                            const uint32_t kk = __builtin_ctz(h);
+                            h &= h - 1u;
+                            const float s = ks[kk];
+                            acc = acc + (((m >> (16u + kk)) & 1u) ? -s : s);
+                        }
+                        r[e] = acc;
+                    }
+                }
+            }
+            __syncthreads();   // every entry has read its element's bits
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if ((mine >> e) & 1u) mask[own_x[e]] = __float_as_uint(r[e]);
+            __syncthreads();
+#pragma unroll
+            for (uint32_t j = 0; j < NS; ++j) {
+                const uint32_t vi = uint32_t(tid) + THREADS * j;
+                a4[j] = vi < nvec ? reinterpret_cast<const f32x4*>(mask)[vi] : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        } else if (!SEP) {
+            // One group: the sums stay in registers.  An element's first hit is looked up
+            // for the four elements of a slot together (four independent LDS reads); only
+            // elements with more hits loop over the rest.
+#pragma unroll
+            for (uint32_t j = 0; j < NS; ++j) {
+                const uint32_t vi = uint32_t(tid) + THREADS * j;
+                u32x4 m4 = {0u, 0u, 0u, 0u};
+                if (vi < nvec) m4 = reinterpret_cast<const u32x4*>(mask)[vi];
+                float s1[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) s1[c] = ks[__builtin_ctz((m4[c] & 0xFFFFu) | 0x10000u) & 15u];
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t m = m4[c];
+                    uint32_t h = m & 0xFFFFu;
+                    const uint32_t k1 = __builtin_ctz(h | 0x10000u);
+                    float acc = h != 0u ? (((m >> (16u + k1)) & 1u) ? -s1[c] : s1[c]) : 0.0f;
+                    h &= h - 1u;
+                    while (h != 0u) {
+                        const uint32_t kk = __builtin_ctz(h);
+                        h &= h - 1u;
+                        const float s = ks[kk];
+                        acc = acc + (((m >> (16u + kk)) & 1u) ? -s : s);
+                    }
+                    a[c] = acc;
+                }
+                a4[j] = a;
+            }
+        } else {
+#pragma unroll
+            for (uint32_t j = 0; j < NS; ++j) {
+                const uint32_t vi = uint32_t(tid) + THREADS * j;
+                if (vi >= nvec) continue;
+                const u32x4 m4 = reinterpret_cast<const u32x4*>(mask)[vi];
+                if (g == 0) reinterpret_cast<f32x4*>(sums)[vi] = init[SEP ? j : 0];
+                uint32_t nz = (m4.x != 0u ? 1u : 0u) | (m4.y != 0u ? 2u : 0u) |
+                              (m4.z != 0u ? 4u : 0u) | (m4.w != 0u ? 8u : 0u);
+                while (nz != 0u) {
+                    const uint32_t c = __builtin_ctz(nz);
+                    nz &= nz - 1u;
+                    const uint32_t m = c == 0u ? m4.x : c == 1u ? m4.y : c == 2u ? m4.z : m4.w;
+                    const uint32_t at = vi * 4u + c;
+                    float acc = sums[at];
+                    uint32_t h = m & 0xFFFFu;
+                    while (h != 0u) {
+                        const uint32_t kk = __builtin_ctz(h);
+                        h &= h - 1u;
+                        const float s = ks[kk];
+                        acc = acc + (((m >> (16u + kk)) & 1u) ? -s : s);
+                    }
+                    sums[at] = acc;
+                    mask[at] = 0u;
+                }
+            }
+        }
+    }
+
+    // ---- the tile's sums: written once, or one optimizer step ----
+#pragma unroll
+    for (uint32_t j = 0; j < NS; ++j) {
+        const uint32_t vi = uint32_t(tid) + THREADS * j;
+        if (vi >= nvec) continue;
+        const uint64_t e0 = v0 + uint64_t(vi) * 4u;
+        const int x0 = int(vi * 4) - int(lead);
+        const f32x4 a = SEP ? reinterpret_cast<const f32x4*>(sums)[vi] : a4[SEP ? 0 : j];
+        if (FUSED) {
+            f32x4 w4 = wq[FUSED ? j : 0], m4 = mq[FUSED ? j : 0], q4 = vq[OPT == kOptAdam ? j : 0];
+            opt_apply<OPT>(a, w4, m4, q4, op, e0, x0, int(tlen));
+        } else if (x0 >= 0 && x0 + 4 <= int(tlen)) {
+            store4<true>(out + e0, a);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (x0 + c >= 0 && x0 + c < int(tlen)) out[e0 + c] = a[c];
         }
     }
 }

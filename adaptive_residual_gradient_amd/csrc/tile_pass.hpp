@@ -15,18 +15,6 @@ namespace adacomp {
 // ---------------------------------------------------------------------------
 constexpr uint32_t kNoKey = 0xFFFFFFFEu;   // never a bin index nor kSentinel
 
-// DPP lane moves (VALU, no LDS round trip).  Lanes without a source, and
-// lanes of rows masked off, receive `old`.
-template <int CTRL, int ROWS = 0xf>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
-    return static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROWS, 0xf, false));
-}
-// lane l receives lane l+1 (wave_shl:1); lane 63 receives old
-__device__ __forceinline__ uint32_t from_next_lane(uint32_t old, uint32_t v) { return dpp_u32<0x130>(old, v); }
-// lane l receives lane l-1 (wave_shr:1); lane 0 receives old
-__device__ __forceinline__ uint32_t from_prev_lane(uint32_t old, uint32_t v) { return dpp_u32<0x138>(old, v); }
-
 // Segmented inclusive max-scan across a wavefront: segments are runs of equal
 // key, keys ascending along the lanes.  Each lane gets the max of val over
 // lanes [start of its run, lane].  Row shifts 1, 2, 4, 8 scan within rows of
