@@ -47,7 +47,7 @@ namespace adacomp {
 // NTS: non-temporal residue stores (tables past kCachedResidueMaxElems).
 template <int V, bool NTS>
 hipError_t launch_tile_pass_nts(const adacomp_plan* plan, hipStream_t stream, float* residue,
-                                const float* dW, uint8_t* msg, uint2* stage, uint32_t* tile_cnt,
+                                const float* dW, uint8_t* msg, uint32_t* stage, uint32_t* tile_cnt,
                                 double* tile_gsum, float* bin_max_out) {
     const uint32_t n = static_cast<uint32_t>(plan->L.ct.by_variant[V].size());
     constexpr uint32_t CV = kVarThreads[2] * kVarVecs[2];   // float4 per chunk of shape 2
@@ -78,7 +78,7 @@ hipError_t launch_tile_pass_nts(const adacomp_plan* plan, hipStream_t stream, fl
 
 template <int V>
 hipError_t launch_tile_pass(const adacomp_plan* plan, hipStream_t stream, float* residue,
-                            const float* dW, uint8_t* msg, uint2* stage, uint32_t* tile_cnt,
+                            const float* dW, uint8_t* msg, uint32_t* stage, uint32_t* tile_cnt,
                             double* tile_gsum, float* bin_max_out) {
     if (plan->L.total_numel > kCachedResidueMaxElems)
         return launch_tile_pass_nts<V, true>(plan, stream, residue, dW, msg, stage, tile_cnt,
@@ -415,7 +415,7 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     hipStream_t stream = static_cast<hipStream_t>(stream_);
 
     uint8_t* w8 = static_cast<uint8_t*>(ws);
-    uint2* stage = reinterpret_cast<uint2*>(w8 + L.ws_stage);
+    uint32_t* stage = reinterpret_cast<uint32_t*>(w8 + L.ws_stage);
     uint32_t* tile_cnt = reinterpret_cast<uint32_t*>(w8 + L.ws_tile_cnt);
     double* tile_gsum = reinterpret_cast<double*>(w8 + L.ws_tile_gsum);
     uint32_t* tile_off = reinterpret_cast<uint32_t*>(w8 + L.ws_tile_off);

@@ -241,7 +241,9 @@ k_finalize(const SegDev* __restrict__ segs, uint32_t nseg, uint32_t plan_hash,
 // survivors, and the lanes take them 64 at a time, with the staged pairs of
 // kEncBatch rounds loaded before any of them is used.  Only wavefront-level
 // operations are used, so every wavefront ends on its own.
-constexpr int kEncBatch = 8;   // 4 and 6 measured within noise; 8 keeps the most loads in flight
+// Survivor rounds per batch; the next batch's staged keys are in flight while
+// this batch's G values are read, so two batches' tables live in registers.
+constexpr int kEncBatch = 4;
 // 2048 wavefronts, 8 per CU.  Against 8192, this shortens the launch and the
 // finalize step every workgroup repeats (a 25 M-element, 0.36 M-survivor
 // table: finish 23 -> 15 us); finishes bound by their scattered residue
@@ -273,7 +275,7 @@ __device__ __forceinline__ uint32_t wave_last_le(uint32_t n, uint64_t x, Key key
 // Wavefront w of W: its share of the survivors (wavefront-uniform arguments).
 __device__ __forceinline__ void encode_wave(uint32_t w, uint32_t W, const SegDev* __restrict__ segs,
                                             uint32_t nseg, const uint32_t* __restrict__ tile_seg,
-                                            const uint2* __restrict__ stage,
+                                            const uint32_t* __restrict__ stage,
                                             const uint32_t* __restrict__ tile_cnt,
                                             const uint32_t* __restrict__ tile_off,
                                             const uint32_t* __restrict__ chunk_base,
@@ -337,11 +339,13 @@ __device__ __forceinline__ void encode_wave(uint32_t w, uint32_t W, const SegDev
             ltwb = (q.lt << 2) | q.wb;
             mag = q.magic;
         }
-        for (uint32_t base = 0; base < take; base += 64u * kEncBatch) {   // wavefront-uniform
-            uint32_t own[kEncBatch], k[kEncBatch];
+        // Survivors base + 64u + lane (u < kEncBatch), clamped to the last one: owning lane,
+        // rank in the owner's tile, the tile's first element and the staged key.
+        struct Batch {
+            uint32_t own[kEncBatch], k[kEncBatch], key[kEncBatch];
             uint64_t tt[kEncBatch];
-            uint2 p[kEncBatch];
-            // Owners and staged pairs first; lanes past the end reload the last survivor.
+        };
+        auto issue = [&](uint32_t base, Batch& b) {
 #pragma unroll
             for (int u = 0; u < kEncBatch; ++u) {
                 const uint32_t e = min(base + 64u * u + lane, take - 1u);
@@ -349,30 +353,45 @@ __device__ __forceinline__ void encode_wave(uint32_t w, uint32_t W, const SegDev
 #pragma unroll
                 for (uint32_t bit = 32; bit >= 1; bit >>= 1)
                     if (__shfl(incl, int(L + bit - 1u)) <= e) L += bit;
-                own[u] = L;
-                k[u] = e - __shfl(excl, int(L));
-                tt[u] = (uint64_t(__shfl(uint32_t(t0 >> 32), int(L))) << 32) |
-                        __shfl(uint32_t(t0), int(L));
-                p[u] = stage[tt[u] + (L == 0 ? r0 : 0u) + k[u]];
+                b.own[u] = L;
+                b.k[u] = e - __shfl(excl, int(L));
+                b.tt[u] = (uint64_t(__shfl(uint32_t(t0 >> 32), int(L))) << 32) |
+                          __shfl(uint32_t(t0), int(L));
+                b.key[u] = stage[b.tt[u] + (L == 0 ? r0 : 0u) + b.k[u]];
             }
+        };
+        if (take != 0) {   // wavefront-uniform; the window advances below either way
+            // Two round trips per batch (the staged keys, then G at those elements): the next
+            // batch's keys are requested (always, clamped) while this batch's G is in flight.
+            Batch cur;
+            issue(0, cur);
+            for (uint32_t base = 0; base < take; base += 64u * kEncBatch) {   // wavefront-uniform
+                // G of every survivor of the batch (the tile pass left residue = G there).
+                float gq[kEncBatch];
 #pragma unroll
-            for (int u = 0; u < kEncBatch; ++u) {
-                const uint32_t L = own[u];
-                const uint64_t ea = (uint64_t(__shfl(uint32_t(eat >> 32), int(L))) << 32) |
-                                    __shfl(uint32_t(eat), int(L));
-                const uint32_t lw = __shfl(ltwb, int(L)), mg = __shfl(mag, int(L));
-                const float sv = __shfl(s, int(L));
-                if (base + 64u * u + lane < take) {
-                    const uint32_t lt = lw >> 2, wb = lw & 3u;
-                    const uint32_t x = p[u].x & 0x7FFFFFFFu;
-                    const uint32_t neg = p[u].x >> 31;
-                    const uint32_t bin = div_bin(x, lt, mg);
-                    const uint32_t topbit = wb == 1u ? 7u : 15u;
-                    put_word(msg + ea + uint64_t(k[u]) * wb, wb, (neg << topbit) | (x - bin * lt));
-                    const float gv = __uint_as_float(p[u].y);
-                    // residue <- G - G_q with G_q = sign(G) * s
-                    residue[tt[u] + x] = neg ? gv + sv : gv - sv;
+                for (int u = 0; u < kEncBatch; ++u) gq[u] = residue[cur.tt[u] + (cur.key[u] & 0x7FFFFFFFu)];
+                Batch nxt;
+                issue(base + 64u * kEncBatch, nxt);
+#pragma unroll
+                for (int u = 0; u < kEncBatch; ++u) {
+                    const uint32_t L = cur.own[u];
+                    const uint64_t ea = (uint64_t(__shfl(uint32_t(eat >> 32), int(L))) << 32) |
+                                        __shfl(uint32_t(eat), int(L));
+                    const uint32_t lw = __shfl(ltwb, int(L)), mg = __shfl(mag, int(L));
+                    const float sv = __shfl(s, int(L));
+                    if (base + 64u * u + lane < take) {
+                        const uint32_t lt = lw >> 2, wb = lw & 3u;
+                        const uint32_t x = cur.key[u] & 0x7FFFFFFFu;
+                        const uint32_t neg = cur.key[u] >> 31;
+                        const uint32_t bin = div_bin(x, lt, mg);
+                        const uint32_t topbit = wb == 1u ? 7u : 15u;
+                        put_word(msg + ea + uint64_t(cur.k[u]) * wb, wb, (neg << topbit) | (x - bin * lt));
+                        const float gv = gq[u];
+                        // residue <- G - G_q with G_q = sign(G) * s
+                        residue[cur.tt[u] + x] = neg ? gv + sv : gv - sv;
+                    }
                 }
+                cur = nxt;
             }
         }
         remaining -= take;
@@ -383,7 +402,7 @@ __device__ __forceinline__ void encode_wave(uint32_t w, uint32_t W, const SegDev
 
 __global__ void __launch_bounds__(256)
 k_encode(const SegDev* __restrict__ segs, uint32_t nseg, const uint32_t* __restrict__ tile_seg,
-         const uint2* __restrict__ stage, const uint32_t* __restrict__ tile_cnt,
+         const uint32_t* __restrict__ stage, const uint32_t* __restrict__ tile_cnt,
          const uint32_t* __restrict__ tile_off, const uint32_t* __restrict__ chunk_base,
          const float* __restrict__ seg_s, const uint64_t* __restrict__ seg_eoff,
          const uint64_t* __restrict__ seg_sbase, uint8_t* __restrict__ msg,
@@ -403,7 +422,7 @@ k_encode(const SegDev* __restrict__ segs, uint32_t nseg, const uint32_t* __restr
 struct ChunkFinishArgs {
     const SegDev* segs;
     const uint32_t* tile_seg;
-    const uint2* stage;
+    const uint32_t* stage;
     const uint32_t* tile_cnt;
     const uint32_t* tile_off;
     const uint32_t* chunk_cnt;

@@ -336,7 +336,7 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
         return at;
     };
     L.ws_sync = take(8);
-    L.ws_stage = take(8 * L.span);     // (key, G) pair per possible survivor
+    L.ws_stage = take(4 * L.span);     // sign | in-tile offset of each survivor, at its tile's offset
     L.ws_tile_cnt = take(4 * tiles);
     L.ws_tile_gsum = take(8 * tiles);
     L.ws_tile_off = take(4 * tiles);

@@ -45,7 +45,7 @@ struct SmallArgs {
     float* residue;
     const float* dW;
     uint8_t* msg;
-    const uint2* stage;
+    const uint32_t* stage;
     uint32_t* tile_cnt;
     double* tile_gsum;
     float* bin_max_out;             // single launch only
@@ -99,15 +99,15 @@ __device__ __forceinline__ SmallLds small_lds(uint32_t* base, uint32_t T, uint32
 
 constexpr int kSmallBatch = 8;   // survivors per lane with their loads in flight together
 
-// kSmallBatch x 64 survivors of one wavefront: their tiles and staged pairs.
+// kSmallBatch x 64 survivors of one wavefront: their tiles and staged keys.
 struct EncBatch {
-    uint2 p[kSmallBatch];
+    uint32_t key[kSmallBatch];
     uint32_t tile[kSmallBatch], e[kSmallBatch];
 };
 
 // Survivors base + 64u + lane (u < kSmallBatch) below e1, clamped to e1 - 1:
 // find each one's tile in the LDS prefix and issue the load of its staged
-// pair (used by enc_store; needs only tpre and tt0).
+// key (used by enc_store; needs only tpre and tt0).
 __device__ __forceinline__ void enc_load(const SmallArgs& A, const SmallLds& L, uint32_t base,
                                          uint32_t e1, EncBatch& b) {
     const uint32_t lane = threadIdx.x & 63u, T = A.ntiles;
@@ -130,7 +130,7 @@ __device__ __forceinline__ void enc_load(const SmallArgs& A, const SmallLds& L, 
     }
 #pragma unroll
     for (int u = 0; u < kSmallBatch; ++u)
-        b.p[u] = A.stage[L.tt0[b.tile[u]] + (b.e[u] - L.tpre[b.tile[u]])];
+        b.key[u] = A.stage[L.tt0[b.tile[u]] + (b.e[u] - L.tpre[b.tile[u]])];
 }
 
 // Entry words and residue fix-up of a loaded batch (needs the finalized
@@ -138,17 +138,22 @@ __device__ __forceinline__ void enc_load(const SmallArgs& A, const SmallLds& L, 
 __device__ __forceinline__ void enc_store(const SmallArgs& A, const SmallLds& L, uint32_t base,
                                           uint32_t e1, const EncBatch& b) {
     const uint32_t lane = threadIdx.x & 63u;
+    // G of every survivor of the batch (the tile pass left residue = G there).
+    float gq[kSmallBatch];
+#pragma unroll
+    for (int u = 0; u < kSmallBatch; ++u)
+        gq[u] = A.residue[uint64_t(L.tt0[b.tile[u]]) + (b.key[u] & 0x7FFFFFFFu)];
 #pragma unroll
     for (int u = 0; u < kSmallBatch; ++u) {
         if (base + 64u * u + lane < e1) {
             const uint32_t t = b.tile[u], si = L.tsi[t];
             const uint32_t lt = L.sltwb[si] >> 2, wb = L.sltwb[si] & 3u;
-            const uint32_t x = b.p[u].x & 0x7FFFFFFFu, neg = b.p[u].x >> 31;
+            const uint32_t x = b.key[u] & 0x7FFFFFFFu, neg = b.key[u] >> 31;
             const uint32_t bin = div_bin(x, lt, L.smag[si]);
             const uint32_t topbit = wb == 1u ? 7u : 15u;
             put_word(A.msg + L.seoff[si] + uint64_t(b.e[u] - uint32_t(L.ssbase[si])) * wb, wb,
                      (neg << topbit) | (x - bin * lt));
-            const float gv = __uint_as_float(b.p[u].y), sv = L.ss[si];
+            const float gv = gq[u], sv = L.ss[si];
             // residue <- G - G_q with G_q = sign(G) * s
             A.residue[uint64_t(L.tt0[t]) + x] = neg ? gv + sv : gv - sv;
         }
@@ -159,7 +164,7 @@ __device__ __forceinline__ void enc_store(const SmallArgs& A, const SmallLds& L,
 // tables, survivor offsets per tile, s, entry offsets and survivors per
 // segment (write_msg: also the directory, header and padding), then the
 // entry words and residue fix-ups of wavefront w of W's share of the
-// survivors, [S*w/W, S*(w+1)/W).  The first batch of staged pairs is loaded
+// survivors, [S*w/W, S*(w+1)/W).  The first batch of staged keys is loaded
 // before the finalize step, so the two memory round trips overlap.
 __device__ __forceinline__ void small_finish(const SmallArgs& A, uint32_t* dyn, uint32_t* lw,
                                              uint64_t* lsz, uint64_t* lns, uint32_t* nlong,
@@ -290,14 +295,14 @@ __global__ void __launch_bounds__(256) k_compress_single(SmallArgs A) {
         TileRegs<kVarVecs[0]> t;
         load_tile<256, kVarVecs[0]>(t, A.segs, A.tile_seg, A.vtiles0, blockIdx.x, A.residue, A.dW);
         process_tile<256, kVarVecs[0], false>(t, dyn, A.segs, A.tile_seg, A.residue, A.msg,
-                                              const_cast<uint2*>(A.stage), A.tile_cnt,
+                                              const_cast<uint32_t*>(A.stage), A.tile_cnt,
                                               A.tile_gsum, A.bin_max_out, ch_tot);
     } else {
         TileRegs<kVarVecs[1]> t;
         load_tile<256, kVarVecs[1]>(t, A.segs, A.tile_seg, A.vtiles1, blockIdx.x - A.n0,
                                     A.residue, A.dW);
         process_tile<256, kVarVecs[1], false>(t, dyn, A.segs, A.tile_seg, A.residue, A.msg,
-                                              const_cast<uint2*>(A.stage), A.tile_cnt,
+                                              const_cast<uint32_t*>(A.stage), A.tile_cnt,
                                               A.tile_gsum, A.bin_max_out, ch_tot);
     }
     // Publish: every wavefront releases its own stores at agent scope (a

@@ -85,7 +85,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
                                              const SegDev* __restrict__ segs,
                                              const uint32_t* __restrict__ tile_seg,
                                              float* __restrict__ residue, uint8_t* __restrict__ msg,
-                                             uint2* __restrict__ stage,
+                                             uint32_t* __restrict__ stage,
                                              uint32_t* __restrict__ tile_cnt,
                                              double* __restrict__ tile_gsum,
                                              float* __restrict__ bin_max_out,
@@ -235,7 +235,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
     }
 
     // ---- survivors to staging, bin boundaries, residue <- G ----
-    uint2* st = stage + tg.t0;
+    uint32_t* st = stage + tg.t0;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int vi = v * THREADS + tid;
@@ -249,8 +249,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
                 const uint32_t b = bn[v][c];
                 if ((fb[v] >> c) & 1u) sbound[b] = r;
                 if (sel[v] & (1u << c)) {
-                    const uint32_t neg = g[v][c] < 0.0f ? 0x80000000u : 0u;
-                    st[r] = make_uint2(neg | uint32_t(x), __float_as_uint(g[v][c]));
+                    st[r] = (g[v][c] < 0.0f ? 0x80000000u : 0u) | uint32_t(x);
                     ++r;
                 }
             }
@@ -298,7 +297,7 @@ template <int THREADS, int VPT, bool NTS>
 __global__ void __launch_bounds__(THREADS)
 k_tile_pass(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
             const uint32_t* __restrict__ vtiles, float* __restrict__ residue,
-            const float* __restrict__ dW, uint8_t* __restrict__ msg, uint2* __restrict__ stage,
+            const float* __restrict__ dW, uint8_t* __restrict__ msg, uint32_t* __restrict__ stage,
             uint32_t* __restrict__ tile_cnt, double* __restrict__ tile_gsum,
             float* __restrict__ bin_max_out) {
     constexpr int NCH = (THREADS / 64) * VPT;
@@ -323,7 +322,7 @@ template <int THREADS, int VPT, int NCR, bool NTS>
 __global__ void __launch_bounds__(THREADS)
 k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ tile_seg,
                  const uint32_t* __restrict__ vtiles, float* __restrict__ residue,
-                 const float* __restrict__ dW, uint8_t* __restrict__ msg, uint2* __restrict__ stage,
+                 const float* __restrict__ dW, uint8_t* __restrict__ msg, uint32_t* __restrict__ stage,
                  uint32_t* __restrict__ tile_cnt, double* __restrict__ tile_gsum,
                  float* __restrict__ bin_max_out) {
     constexpr int NW = THREADS / 64;
@@ -387,7 +386,7 @@ k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ t
 
     // ---- pass 2 over one chunk: selection, compaction to staging, residue <- G ----
     uint32_t carry = 0;
-    uint2* st = stage + tg.t0;
+    uint32_t* st = stage + tg.t0;
     auto pass2 = [&](const f32x4 (&a)[VPT], const f32x4 (&b)[VPT], uint32_t c0) {
         uint32_t sel[VPT], wrank[VPT];
         float g[VPT][4];
@@ -433,8 +432,7 @@ k_tile_pass_long(const SegDev* __restrict__ segs, const uint32_t* __restrict__ t
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 if (sel[v] & (1u << c)) {
-                    const uint32_t neg = g[v][c] < 0.0f ? 0x80000000u : 0u;
-                    st[r] = make_uint2(neg | uint32_t(x0 + c), __float_as_uint(g[v][c]));
+                    st[r] = (g[v][c] < 0.0f ? 0x80000000u : 0u) | uint32_t(x0 + c);
                     ++r;
                 }
             }

@@ -101,7 +101,7 @@ static std::string check(const std::vector<adacomp_segment>& segs, int expect_st
     uint64_t at = L.entries_begin;
     for (const SegDev& d : L.segs) at = round_up(at + d.numel * d.wb, 16);
     if (at != L.capacity) return "FAIL capacity";
-    if (L.ws_tile_cnt - L.ws_stage < 8 * L.span) return "FAIL stage size";
+    if (L.ws_tile_cnt - L.ws_stage < 4 * L.span) return "FAIL stage size";   // one 32-bit key per element
     // LDS per workgroup stays within 64 KiB.
     for (int v = 0; v < kVariants; ++v)
         if (!L.ct.by_variant[v].empty() && (2 * L.ct.max_bpt[v] + 1) * 4 > 65536) return "FAIL tile LDS";
