@@ -1,7 +1,7 @@
 """GPU parity of adacomp_decode_accumulate against the CPU oracle: bit-exact,
 messages summed in order, for K = 1..16 messages, both accumulate modes,
-edge-case tables, the full-size 1.07-billion-element workload (sampled
-segments), and messages whose header does not match the plan."""
+edge-case tables, and messages whose header does not match the plan (the
+full-size 1.07-billion-element workload: tests/test_gpu_large_full.py)."""
 import sys
 
 import numpy as np
@@ -130,36 +130,6 @@ def test_decode_skips_foreign_messages():
     plan2.close()
 
 
-def test_decode_large_workload_sampled():
-    """K = 16 learner messages of the 1.07-billion-element workload summed on
-    the GPU at full size; three sampled segments checked bit for bit."""
-    wl = W.workload("large")
-    plan = A.Plan(wl.segments)
-    K = 16
-    say("  building 16 learner messages at full size")
-    msgs = learner_messages(wl, plan, K, steps=2)
-    ws = plan.decode_workspace(K, DEV)
-    out = torch.empty(W.alloc_len(wl), dtype=torch.float32, device=DEV)
-    say("  decode K=16 full size")
-    A.decode_accumulate(plan, msgs, out, False, ws)
-    torch.cuda.synchronize()
-    host_msgs = []
-    for m in msgs:
-        total, _, _ = A.message_header(plan, m)
-        host_msgs.append(host(m[:total]))
-    for i in (0, 31, 63):
-        o, c, lt = wl.segments[i]
-        sub = [(0, c, lt)]
-        want = np.zeros(c, np.float32)
-        oracle.decode_accumulate(sub, [mp.single_segment_message(hm, wl.segments, i)
-                                       for hm in host_msgs], want, False)
-        np.testing.assert_array_equal(bits(host(out[o:o + c])), bits(want))
-        say(f"    segment {i} ok")
-    plan.close()
-    del msgs, out, ws
-    torch.cuda.empty_cache()
-
-
 @pytest.mark.parametrize("K,lt", [(70, 50), (256, 500), (20, 1)])
 def test_decode_many_messages(K, lt):
     """Message groups: more messages than one group holds (64 at most, fewer
@@ -267,41 +237,6 @@ def test_decode_sgd_edge_tables(lt):
     say(f"  decode+SGD L_T={lt}")
     _sgd_check(plan, segs, msgs, host_msgs, w, m, 0.05, 0.5, 1e-3, 1.0 / 3.0)
     plan.close()
-
-
-def test_decode_sgd_large_workload_sampled():
-    """K = 16 on the 1.07-billion-element workload in one call; three layers
-    checked bit for bit against the oracle on their own."""
-    wl = W.workload("large")
-    plan = A.Plan(wl.segments)
-    K = 16
-    say("  building 16 learner messages at full size")
-    msgs = learner_messages(wl, plan, K, steps=2)
-    n = W.alloc_len(wl)
-    w = torch.empty(n, dtype=torch.float32, device=DEV)
-    w.normal_(0.0, 0.05, generator=torch.Generator(device=DEV).manual_seed(5))
-    m = torch.zeros(n, dtype=torch.float32, device=DEV)
-    w0 = {i: host(w[o:o + c]) for i, (o, c, _) in enumerate(wl.segments) if i in (0, 31, 63)}
-    ws = plan.decode_sgd_workspace(K, DEV)
-    say("  decode+SGD K=16 full size")
-    A.decode_sgd(plan, msgs, w, m, 0.01, 0.9, ws, scale=1.0 / K)
-    torch.cuda.synchronize()
-    host_msgs = []
-    for mm in msgs:
-        total, _, _ = A.message_header(plan, mm)
-        host_msgs.append(host(mm[:total]))
-    for i in (0, 31, 63):
-        o, c, lt = wl.segments[i]
-        sub = [(0, c, lt)]
-        w_ref, m_ref = w0[i].copy(), np.zeros(c, np.float32)
-        oracle.decode_sgd(sub, [mp.single_segment_message(hm, wl.segments, i) for hm in host_msgs],
-                          w_ref, m_ref, 0.01, 0.9, 0.0, 1.0 / K)
-        np.testing.assert_array_equal(bits(host(w[o:o + c])), bits(w_ref))
-        np.testing.assert_array_equal(bits(host(m[o:o + c])), bits(m_ref))
-        say(f"    segment {i} ok")
-    plan.close()
-    del msgs, w, m, ws
-    torch.cuda.empty_cache()
 
 
 def test_decode_sgd_argument_errors():
