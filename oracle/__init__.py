@@ -26,6 +26,10 @@ import numpy as np
 _HERE = pathlib.Path(__file__).resolve().parent
 _SRC = _HERE / "adacomp_oracle.c"
 _LIB_PATH = _HERE / "libadacomp_oracle.so"
+# A test may point the wrapper at another build of an oracle source (the
+# mutation test loads deliberately broken copies this way); such a library is
+# loaded as it is and never rebuilt here.
+_LIB_OVERRIDE = os.environ.get("ADACOMP_ORACLE_LIB")
 
 # Plain C, IEEE single and double arithmetic, no contraction into fused
 # multiply-adds, no fast-math, no flush-to-zero.
@@ -52,9 +56,15 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not _LIB_PATH.exists():
-            build()
-        lib = ctypes.CDLL(str(_LIB_PATH))
+        if _LIB_OVERRIDE:
+            path = pathlib.Path(_LIB_OVERRIDE)
+            if not path.exists():
+                raise OracleError(f"ADACOMP_ORACLE_LIB names a missing file: {path}")
+        else:
+            path = _LIB_PATH
+            if not path.exists():
+                build()
+        lib = ctypes.CDLL(str(path))
         P = ctypes.POINTER
         lib.oracle_plan_hash.argtypes = [P(_Seg), ctypes.c_uint32]
         lib.oracle_plan_hash.restype = ctypes.c_uint32

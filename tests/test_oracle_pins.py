@@ -314,6 +314,86 @@ def test_codec_round_trip():
         assert np.all(err <= np.spacing(np.abs(r)) / 2)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_capacity_is_the_all_sent_message(seed):
+    """P8: the message capacity is the length of the message in which every
+    element is transmitted (dW = 0 and equal magnitudes in each bin, so every
+    |H| ties with its bin maximum), as the byte-level brute force lays it
+    out; any other message is no longer.  Catches: a capacity that drops the
+    16-byte padding, the count regions or the 16-bit word width."""
+    rng = np.random.default_rng(300 + seed)
+    segs, span = random_table(rng, max_seg=4, max_n=300)
+    # 16-bit ragged, 8-bit ragged, and two whose entry regions end exactly
+    # on a 16-byte boundary
+    segs += [(span, 97, 64), (span + 100, 130, 63), (span + 232, 96, 64), (span + 328, 48, 8)]
+    span += 376
+    r = np.zeros(span, np.float32)
+    for (o, n, lt) in segs:
+        for b in range(0, n, lt):
+            k = min(lt, n - b)
+            r[o + b:o + b + k] = rng.choice([-1.0, 1.0], k) * np.float32(rng.uniform(0.5, 2.0))
+    d = np.zeros(span, np.float32)
+    _, _, want, _ = bf.compress(segs, r, d)
+    got_r, _, msg = run_oracle(segs, r, d)
+    assert mp.parse(msg, segs).total_survivors == sum(n for (_, n, _) in segs)
+    assert msg.tobytes() == want
+    assert oracle.message_capacity(segs) == len(want)
+    d2 = rng.standard_normal(span).astype(np.float32)
+    msg2, _ = oracle.compress(segs, got_r, d2)
+    assert len(msg2) <= len(want)
+
+
+def test_h_is_rounded_after_g():
+    """P1: H is G + dW with G already rounded to float32, two roundings, not
+    residue + 2*dW rounded once.  In units u = 2^-24 (the float32 spacing
+    just below 1): residue 1 - 4u and dW 1.5u give G = fl(1 - 2.5u) = 1 - 2u
+    (tie to the even significand), then H = fl(1 - 0.5u) = 1 (tie to even),
+    while 1 - 4u + 3u = 1 - u is a float.  Beside an element with G = 1 (the
+    bin maximum), the element is sent only under two roundings.  Catches: H
+    formed in one step or in higher precision."""
+    u = 2.0 ** -24
+    r = np.array([1.0, 1.0 - 4 * u], np.float32)
+    d = np.array([0.0, 1.5 * u], np.float32)
+    assert float(r[1]) == 1.0 - 4 * u and float(d[1]) == 1.5 * u
+    segs = [(0, 2, 2)]
+    _, _, msg = run_oracle(segs, r, d)
+    m = mp.parse(msg, segs)
+    np.testing.assert_array_equal(mp.sent_mask(m, segs, 2), [True, True])
+
+
+def test_decode_rejects_foreign_and_inconsistent_messages():
+    """P8: a message is summed only under the table it was made for: a plan
+    hash of another table with the same segment count, a survivor count that
+    disagrees with the count words, or a bad magic is refused, not summed.
+    Catches: a decoder that trusts the header or the directory."""
+    segs = [(0, 40, 7), (40, 30, 64)]
+    rng = np.random.default_rng(81)
+    r = np.zeros(72, np.float32)
+    msg, _ = oracle.compress(segs, r, rng.standard_normal(72).astype(np.float32))
+    out = np.zeros(72, np.float32)
+    oracle.decode_accumulate(segs, [msg], out, False)
+    other = [(0, 40, 7), (40, 30, 65)]
+    with pytest.raises(oracle.OracleError):
+        oracle.decode_accumulate(other, [msg], out, False)
+    bad = msg.copy()
+    bad[12] ^= 1                       # plan hash
+    with pytest.raises(oracle.OracleError):
+        oracle.decode_accumulate(segs, [bad], out, False)
+    bad = msg.copy()
+    bad[0] ^= 1                        # magic
+    with pytest.raises(oracle.OracleError):
+        oracle.decode_accumulate(segs, [bad], out, False)
+    for seg in range(2):               # directory survivor count, each segment
+        bad = msg.copy()
+        at = 32 + 16 * seg + 4
+        n = int(np.frombuffer(bad[at:at + 4].tobytes(), np.uint32)[0])
+        bad[at:at + 4] = np.frombuffer(np.uint32(n + 1).tobytes(), np.uint8)
+        with pytest.raises(oracle.OracleError):
+            oracle.decode_accumulate(segs, [bad], out, False)
+        with pytest.raises(oracle.OracleError):
+            oracle.decode_sgd(segs, [bad], out.copy(), out.copy(), 0.1, 0.9)
+
+
 def test_decode_sums_messages_in_order():
     """Decode of K messages = for k in order, out[j] = fl32(out[j] + q_k[j]) at
     transmitted j only; accumulate = 1 starts from out (-0 stays -0 where no
