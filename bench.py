@@ -112,6 +112,8 @@ def cpu_baseline(wl, dws_host_fn, max_steps: int, seconds: float = 15.0):
         "value": round(best, 4),
         "unit": "Gelem/s",
         "cores": cores,
+        "threads": threads,
+        "host_cores": os.cpu_count(),
         "kind": "oracle",
         "single_thread_value": round(v1, 4),
         "threaded_value": round(vn, 4),

@@ -190,7 +190,10 @@ def geometry_tables():
 
 def test_tile_geometry_on_cpu(tmp_path):
     exe = tmp_path / "geometry_check"
-    subprocess.run(["g++", "-O2", "-std=c++17", "-o", str(exe),
+    # built with the address and undefined-behaviour sanitizers: any access
+    # of the layout code outside its vectors, or an overflow, ends the run
+    subprocess.run(["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-o", str(exe),
                     str(ROOT / "tests" / "cpu" / "geometry_check.cpp")], check=True)
     tables = geometry_tables()
     lines = []
@@ -200,6 +203,7 @@ def test_tile_geometry_on_cpu(tmp_path):
     inp = tmp_path / "tables.txt"
     inp.write_text("\n".join(lines) + "\n")
     r = subprocess.run([str(exe), str(inp)], capture_output=True, text=True)
+    assert "Sanitizer" not in r.stderr and "runtime error" not in r.stderr, r.stderr[-4000:]
     out = r.stdout.strip().splitlines()
     assert len(out) == len(tables), r.stderr
     fails = [(i, l) for i, l in enumerate(out) if not l.startswith("OK")]
