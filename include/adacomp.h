@@ -182,9 +182,19 @@ int adacomp_compress(const adacomp_plan* plan, float* residue, const float* dW,
  *               segment starts from +0; accumulate = 1: starts from out.
  *               An element no message transmits gets no addition.
  *   ws          ws_bytes >= fixed + K * per_message (see plan info).
- * A message whose header does not match the plan (magic, version, nseg,
- * plan_hash) contributes nothing; the number of such messages is written as
- * a uint32 at byte 0 of ws. */
+ * Each msgs[k] must point to at least the header's total_bytes readable
+ * bytes (at least 32).  A message is checked on the device before any entry
+ * word is read, and is refused -- it contributes nothing, the other messages
+ * are summed as if it were absent -- when its header does not match the plan
+ * (magic, version, nseg, plan_hash; total_bytes a multiple of 16 between the
+ * start of the entry regions and info.message_capacity), or when a segment's
+ * directory entry disagrees with the count words (entry offset not 16-byte
+ * aligned or before the entry regions; survivors more than the segment's
+ * elements or unequal to the sum of its count words; a tile counting more
+ * survivors than it has elements; the padded entry region past total_bytes).
+ * Entry words whose in-bin index lies outside the bin are ignored.  The
+ * number of refused messages is written as a uint32 at byte 0 of ws; the
+ * call itself still returns ADACOMP_OK. */
 int adacomp_decode_accumulate(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
                               float* out, uint64_t n_elems, int accumulate, void* ws,
                               uint64_t ws_bytes, void* stream);
@@ -211,7 +221,8 @@ typedef struct adacomp_sgd {
  *   ws          ws_bytes >= adacomp_decode_sgd_workspace_bytes(plan, K); plans
  *               with bins longer than 4093 elements need a dense scratch of
  *               4 * span bytes in it.
- * Foreign messages are skipped and counted as in adacomp_decode_accumulate. */
+ * Messages are checked, refused and counted at byte 0 of ws as in
+ * adacomp_decode_accumulate. */
 int adacomp_decode_sgd(const adacomp_plan* plan, const void* const* msgs, uint32_t K,
                        float* weights, float* momentum, uint64_t n_elems, const adacomp_sgd* sgd,
                        void* ws, uint64_t ws_bytes, void* stream);

@@ -130,6 +130,81 @@ def test_decode_skips_foreign_messages():
     plan2.close()
 
 
+def _put(buf, at, dtype, value):
+    n = np.dtype(dtype).itemsize
+    buf[at:at + n] = np.frombuffer(np.array(value, dtype).tobytes(), np.uint8)
+
+
+def _get(buf, at, dtype):
+    return np.frombuffer(buf[at:at + np.dtype(dtype).itemsize].tobytes(), dtype)[0]
+
+
+def test_decode_rejects_inconsistent_messages():
+    """Messages whose header matches the plan but whose body is inconsistent,
+    every offset still inside the buffer, are refused one by one: the others
+    are summed as the oracle sums them alone, and the refused ones are
+    counted in the status word, for the plain sum, the accumulate mode and
+    the fused SGD step.  Corruptions: a directory survivor count one too
+    high; one count word one too high; an entry offset off its 16-byte
+    alignment; a total length past the plan's capacity."""
+    segs = [(0, 6000, 50), (6000, 9000, 500)]
+    wl_n = 15000
+    plan = A.Plan(segs)
+    ws_c = plan.compress_workspace(DEV)
+    rng = np.random.default_rng(77)
+    good = []
+    for k in range(6):
+        r = torch.zeros(wl_n, dtype=torch.float32, device=DEV)
+        d = torch.from_numpy((rng.standard_normal(wl_n) * 1e-3).astype(np.float32)).to(DEV)
+        msg = plan.message_buffer(DEV)
+        A.compress(plan, r, d, msg, ws_c)
+        good.append(host(msg).copy())
+    info = plan.info
+    cap = int(info.message_capacity)
+    bad = [m.copy() for m in good]
+    _put(bad[1], 32 + 16 + 4, np.uint32, _get(bad[1], 32 + 16 + 4, np.uint32) + 1)
+    cnt0 = ((32 + 16 * 2) + 15) // 16 * 16          # first count word of segment 0 (8-bit)
+    bad[2][cnt0] += 1
+    _put(bad[3], 32 + 8, np.uint64, _get(bad[3], 32 + 8, np.uint64) + 8)
+    _put(bad[4], 16, np.uint64, cap + 16)
+    dev = [torch.from_numpy(m).to(DEV) for m in bad]
+    keep = [bad[0][:int(_get(bad[0], 16, np.uint64))], bad[5][:int(_get(bad[5], 16, np.uint64))]]
+    for m in bad[1:3]:          # the oracle refuses the two count mismatches as well
+        with pytest.raises(oracle.OracleError):
+            oracle.decode_accumulate(segs, [m], np.zeros(wl_n, np.float32), False)
+
+    ws = plan.decode_workspace(6, DEV)
+    out = torch.full((wl_n,), 3.0, dtype=torch.float32, device=DEV)
+    A.decode_accumulate(plan, dev, out, False, ws)
+    torch.cuda.synchronize()
+    assert int(host(ws[:4]).view(np.uint32)[0]) == 4
+    want = np.zeros(wl_n, np.float32)
+    oracle.decode_accumulate(segs, keep, want, False)
+    np.testing.assert_array_equal(bits(host(out)), bits(want))
+
+    start = (rng.standard_normal(wl_n) * 1e-2).astype(np.float32)
+    out = torch.from_numpy(start.copy()).to(DEV)
+    A.decode_accumulate(plan, dev, out, True, ws)
+    torch.cuda.synchronize()
+    assert int(host(ws[:4]).view(np.uint32)[0]) == 4
+    want = start.copy()
+    oracle.decode_accumulate(segs, keep, want, True)
+    np.testing.assert_array_equal(bits(host(out)), bits(want))
+
+    w0 = (rng.standard_normal(wl_n) * 0.05).astype(np.float32)
+    m0 = (rng.standard_normal(wl_n) * 1e-3).astype(np.float32)
+    w, m = torch.from_numpy(w0.copy()).to(DEV), torch.from_numpy(m0.copy()).to(DEV)
+    ws2 = plan.decode_sgd_workspace(6, DEV)
+    A.decode_sgd(plan, dev, w, m, 0.01, 0.9, ws2, weight_decay=1e-4, scale=0.5)
+    torch.cuda.synchronize()
+    assert int(host(ws2[:4]).view(np.uint32)[0]) == 4
+    w_ref, m_ref = w0.copy(), m0.copy()
+    oracle.decode_sgd(segs, keep, w_ref, m_ref, 0.01, 0.9, weight_decay=1e-4, scale=0.5)
+    np.testing.assert_array_equal(bits(host(w)), bits(w_ref))
+    np.testing.assert_array_equal(bits(host(m)), bits(m_ref))
+    plan.close()
+
+
 @pytest.mark.parametrize("K,lt", [(70, 50), (256, 500), (20, 1)])
 def test_decode_many_messages(K, lt):
     """Message groups: more messages than one group holds (64 at most, fewer
