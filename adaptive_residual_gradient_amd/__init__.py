@@ -31,6 +31,7 @@ PLAN_SEPARATE_FINISH = 1   # plan flag: finish with three kernels whatever the t
 PLAN_SINGLE_LAUNCH = 2     # plan flag: a small table in one launch (slower; for comparison)
 SMALL_TABLE_MAX_SPAN = 1 << 21     # tables up to this span and this many segments
 SMALL_TABLE_MAX_SEGMENTS = 256     # finish in one launch after the tile pass
+NOALLOC_SCRATCH_BYTES = 128 << 20  # largest compress workspace compress_noalloc takes
 CHUNK_FINISH_MAX_TILES = 1 << 20   # larger tables of <= 256 segments and this many tiles: two
 
 
@@ -90,6 +91,7 @@ SIGNATURES = {
     "adacomp_plan_destroy": ([_P], _INT),
     "adacomp_plan_get_info": ([_P, ctypes.POINTER(PlanInfo)], _INT),
     "adacomp_compress": ([_P, _P, _P, _U64, _P, _U64, _P, _U64, _P, _P], _INT),
+    "adacomp_compress_noalloc": ([_P, _P, _P, _U64, _P, _U64, _P, _P], _INT),
     "adacomp_decode_accumulate": ([_P, ctypes.POINTER(_P), _U32, _P, _U64, _INT, _P, _U64, _P], _INT),
     "adacomp_compress_timed": ([_P, _P, _P, _U64, _P, _U64, _P, _U64, _P, _P, _P], _INT),
     "adacomp_decode_accumulate_timed": ([_P, ctypes.POINTER(_P), _U32, _P, _U64, _INT, _P, _U64,
@@ -274,6 +276,20 @@ def compress(plan: Plan, residue, dW, msg, ws, bin_max_out=None, stream=None,
         _u8_ptr(msg, "msg"), msg.numel(), _u8_ptr(ws, "ws"), ws.numel(), bm,
         _stream_handle(stream), timer.handle if timer is not None else None)
     _check("adacomp_compress", st)
+
+
+def compress_noalloc(plan: Plan, residue, dW, msg, bin_max_out=None, stream=None) -> None:
+    """One AdaComp step as compress(), its workspace the library's own
+    per-GPU scratch: the call allocates no device memory.  Calls that may
+    overlap on one GPU race on that scratch."""
+    bm = _f32_ptr(bin_max_out, "bin_max_out") if bin_max_out is not None else None
+    if bin_max_out is not None and bin_max_out.numel() < plan.info.total_bins:
+        raise ValueError("bin_max_out shorter than the plan's total_bins")
+    n = min(residue.numel(), dW.numel())
+    st = lib().adacomp_compress_noalloc(
+        plan.handle, _f32_ptr(residue, "residue"), _f32_ptr(dW, "dW"), n,
+        _u8_ptr(msg, "msg"), msg.numel(), bm, _stream_handle(stream))
+    _check("adacomp_compress_noalloc", st)
 
 
 def decode_accumulate(plan: Plan, msgs: List, out, accumulate: bool, ws, stream=None,

@@ -7,6 +7,7 @@
 // Application claim (Table 2).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -235,6 +236,7 @@ const char* adacomp_status_str(int status) {
         case ADACOMP_ERR_CAPACITY: return "buffer smaller than the plan requires";
         case ADACOMP_ERR_HIP: return "HIP runtime error";
         case ADACOMP_ERR_TOO_LARGE: return "segment table too large";
+        case ADACOMP_ERR_SCRATCH_LIMIT: return "plan workspace larger than the no-alloc scratch";
         default: return "unknown status";
     }
 }
@@ -403,11 +405,13 @@ int adacomp_compress_timed(const adacomp_plan* plan, float* residue, const float
     if (n_elems < L.span || msg_bytes < L.capacity || ws_bytes < L.ws_compress)
         return ADACOMP_ERR_CAPACITY;
     {
-        std::vector<Range> r = {range_of(residue, 4 * L.span), range_of(dW, 4 * L.span),
-                                range_of(msg, L.capacity), range_of(ws, L.ws_compress)};
-        if (bin_max_out) r.push_back(range_of(bin_max_out, 4 * L.total_bins));
-        for (size_t i = 0; i < r.size(); ++i)
-            for (size_t j = i + 1; j < r.size(); ++j)
+        // a fixed array: this check allocates nothing (adacomp_compress_noalloc)
+        const Range r[5] = {range_of(residue, 4 * L.span), range_of(dW, 4 * L.span),
+                            range_of(msg, L.capacity), range_of(ws, L.ws_compress),
+                            range_of(bin_max_out, bin_max_out ? 4 * L.total_bins : 0)};
+        const int nr = bin_max_out ? 5 : 4;
+        for (int i = 0; i < nr; ++i)
+            for (int j = i + 1; j < nr; ++j)
                 if (overlaps(r[i], r[j])) return ADACOMP_ERR_INVALID_ARGUMENT;
     }
     int st = check_device(plan);
@@ -538,6 +542,50 @@ int adacomp_compress(const adacomp_plan* plan, float* residue, const float* dW, 
                      float* bin_max_out, void* stream) {
     return adacomp_compress_timed(plan, residue, dW, n_elems, msg, msg_bytes, ws, ws_bytes,
                                   bin_max_out, stream, nullptr);
+}
+
+}  // extern "C"
+
+// Workspace of adacomp_compress_noalloc: a file-scope device array, one copy
+// per GPU.  Host code never uses its name as an address (on the host it is
+// only a stand-in); the device address comes from hipGetSymbolAddress, once
+// per device, and is kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[ADACOMP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> scratch_ptr[kScratchDevices];
+
+// The current device's copy of `scratch`, looked up on the first call on
+// that device (with it current) and kept for the process.
+int scratch_for_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return ADACOMP_ERR_HIP;
+    if (dev < 0 || dev >= kScratchDevices) return ADACOMP_ERR_INVALID_ARGUMENT;
+    void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return ADACOMP_ERR_HIP;
+        scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return ADACOMP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int adacomp_compress_noalloc(const adacomp_plan* plan, float* residue, const float* dW,
+                             uint64_t n_elems, void* msg, uint64_t msg_bytes, float* bin_max_out,
+                             void* stream) {
+    if (plan == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
+    if (plan->L.ws_compress > ADACOMP_NOALLOC_SCRATCH_BYTES) return ADACOMP_ERR_SCRATCH_LIMIT;
+    int st = check_device(plan);
+    if (st != ADACOMP_OK) return st;
+    void* ws = nullptr;
+    if ((st = scratch_for_current_device(&ws)) != ADACOMP_OK) return st;
+    return adacomp_compress_timed(plan, residue, dW, n_elems, msg, msg_bytes, ws,
+                                  ADACOMP_NOALLOC_SCRATCH_BYTES, bin_max_out, stream, nullptr);
 }
 
 }  // extern "C"

@@ -67,6 +67,7 @@ extern "C" {
 #define ADACOMP_ERR_CAPACITY (-5)         /* a buffer is smaller than the plan requires */
 #define ADACOMP_ERR_HIP (-6)              /* a HIP runtime call or kernel launch failed */
 #define ADACOMP_ERR_TOO_LARGE (-7)        /* numel >= 2^32 in one segment, or the table exceeds launch limits */
+#define ADACOMP_ERR_SCRATCH_LIMIT (-8)    /* adacomp_compress_noalloc: the plan's workspace exceeds its scratch */
 
 #define ADACOMP_MAX_BIN_LEN 32768u
 
@@ -173,6 +174,26 @@ int adacomp_plan_get_info(const adacomp_plan* plan, adacomp_plan_info* info);
 int adacomp_compress(const adacomp_plan* plan, float* residue, const float* dW,
                      uint64_t n_elems, void* msg, uint64_t msg_bytes, void* ws,
                      uint64_t ws_bytes, float* bin_max_out, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): one
+ * compression step exactly as adacomp_compress, with the workspace taken
+ * from a scratch array the library holds on each GPU it runs on, from the
+ * first call on that GPU until the process ends.  The call allocates nothing
+ * (no hipMalloc, hipFree or other allocating routine).
+ *   Arguments as for adacomp_compress, without ws and ws_bytes; the current
+ *   device must be the plan's.
+ *   The plan's info.compress_workspace_bytes must be at most
+ *   ADACOMP_NOALLOC_SCRATCH_BYTES (128 MiB: tables of up to about 33 million
+ *   elements); larger plans return ADACOMP_ERR_SCRATCH_LIMIT before any work.
+ *   Every call on one GPU shares that GPU's scratch and it keeps the last
+ *   call's contents (compress needs no initial contents): calls that may
+ *   overlap on one GPU -- on different streams, or from different threads
+ *   without ordering -- race and must not be issued. */
+#define ADACOMP_NOALLOC_SCRATCH_BYTES (128ull << 20)
+int adacomp_compress_noalloc(const adacomp_plan* plan, float* residue, const float* dW,
+                             uint64_t n_elems, void* msg, uint64_t msg_bytes, float* bin_max_out,
+                             void* stream);
 
 /* Sum K messages made by adacomp_compress with this same segment table into
  * out, in message order: for k = 0..K-1 and every element j message k
