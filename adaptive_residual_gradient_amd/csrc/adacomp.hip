@@ -198,7 +198,7 @@ bool long_decode_in_lds(const Layout& L, uint32_t K, uint32_t KG, uint32_t ps, i
 }
 
 struct DecodeLayout {
-    uint64_t status, dcnt, doff, dchunk_cnt, dchunk_base, dseg_s, dseg_eoff, dvalid, total;
+    uint64_t status, dcnt, doff, dchunk_cnt, dchunk_base, dseg_s, dseg_eoff, dvalid, drec, total;
 };
 
 DecodeLayout decode_layout(const Layout& L, uint32_t K) {
@@ -218,6 +218,7 @@ DecodeLayout decode_layout(const Layout& L, uint32_t K) {
     d.dseg_s = take(4 * K * S);
     d.dseg_eoff = take(8 * K * S);
     d.dvalid = take(4 * uint64_t(K));
+    d.drec = take(8 * K * uint64_t(L.dt.by_variant[0].size()));
     d.total = w;
     return d;
 }
@@ -644,6 +645,9 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
     for (uint32_t k = 0; k < K; ++k) {
         if (msgs[k] == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
         if (!aligned16(msgs[k])) return ADACOMP_ERR_MISALIGNED;
+        // entry records hold 48-bit addresses
+        if (reinterpret_cast<uintptr_t>(msgs[k]) + L.capacity >= (uint64_t(1) << 48))
+            return ADACOMP_ERR_INVALID_ARGUMENT;
         const Range rm = range_of(msgs[k], 32 + 16 * uint64_t(L.nseg));
         if (overlaps(rm, rw)) return ADACOMP_ERR_INVALID_ARGUMENT;
         for (const Range& r : dense)
@@ -664,6 +668,7 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
     dw.dseg_s = reinterpret_cast<float*>(w8 + D.dseg_s);
     dw.dseg_eoff = reinterpret_cast<uint64_t*>(w8 + D.dseg_eoff);
     dw.dvalid = reinterpret_cast<uint32_t*>(w8 + D.dvalid);
+    dw.drec = reinterpret_cast<uint64_t*>(w8 + D.drec);
     const uint32_t DT = static_cast<uint32_t>(L.dt.ntiles), DC = static_cast<uint32_t>(L.dt.nchunks);
     float* sums = out;   // where long-bin tiles accumulate
     if (fused) {
@@ -677,6 +682,11 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
     geo.entries_begin = L.entries_begin;
     geo.capacity = L.capacity;
 
+    // The plain sum of at most 16 messages from +0 over LDS tiles takes the two-round-trip
+    // kernel; everything else (more messages, out += sum, an optimizer step) k_decode_tiles.
+    const uint32_t ps0 = L.dt.max_bpt[0] + 1;
+    const bool plain_sum = !L.dt.by_variant[0].empty() && !fused && accumulate == 0 &&
+                           adacomp::decode_tiles_group(K, ps0) == K;
     CallTimer tm(timer, stream, call_stage);
     {
         hipLaunchKernelGGL(adacomp::k_decode_count, dim3(DC, K), dim3(256), 0, stream, mp,
@@ -689,6 +699,12 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
         hipLaunchKernelGGL(adacomp::k_decode_base, dim3(K), dim3(256), 0, stream, mp, K,
                            plan->d_segs, geo, DC, dw);
         if ((st = launch_status()) != ADACOMP_OK) return st;
+        if (plain_sum) {   // the LDS tiles' entry records for k_decode_tiles_sum
+            const uint32_t P = static_cast<uint32_t>(L.dt.by_variant[0].size());
+            hipLaunchKernelGGL(adacomp::k_decode_records, dim3((P + 255) / 256), dim3(256), 0, stream,
+                               mp, K, plan->ddesc[0], P, DT, DC, L.nseg, dw);
+            if ((st = launch_status()) != ADACOMP_OK) return st;
+        }
         tm.mark(ADACOMP_STAGE_DECODE_BASE);
     }
     {
@@ -707,15 +723,18 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
 #define ADACOMP_TILES(SEP, OPT)                                                                    \
     hipLaunchKernelGGL((adacomp::k_decode_tiles<SEP, OPT>), dim3(n), dim3(256), lds, stream, mp, K, \
                        kg, ps, plan->ddesc[0], DT, DC, L.nseg, dw, dst, acc, acc_words, op)
-                if (opt == adacomp::kOptSgd) {
+                if (plain_sum) {
+                    hipLaunchKernelGGL(adacomp::k_decode_tiles_sum, dim3(n), dim3(256),
+                                       adacomp::decode_sum_lds_bytes(acc_words, K, ps), stream, mp, K,
+                                       ps, plan->ddesc[0], L.nseg, dw, out, acc_words);
+                } else if (opt == adacomp::kOptSgd) {
                     if (sep) ADACOMP_TILES(true, adacomp::kOptSgd);
                     else ADACOMP_TILES(false, adacomp::kOptSgd);
                 } else if (opt == adacomp::kOptAdam) {
                     if (sep) ADACOMP_TILES(true, adacomp::kOptAdam);
                     else ADACOMP_TILES(false, adacomp::kOptAdam);
-                } else {
-                    if (sep) ADACOMP_TILES(true, adacomp::kOptNone);
-                    else ADACOMP_TILES(false, adacomp::kOptNone);
+                } else {   // out += sum, or more messages than one group (sep)
+                    ADACOMP_TILES(true, adacomp::kOptNone);
                 }
 #undef ADACOMP_TILES
             } else if (long_decode_in_lds(L, K, KG, ps, opt)) {

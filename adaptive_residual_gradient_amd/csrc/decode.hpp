@@ -26,7 +26,14 @@ struct DecodeWs {
     float* dseg_s;        // [K*nseg]
     uint64_t* dseg_eoff;  // [K*nseg]
     uint32_t* dvalid;     // [K]
+    uint64_t* drec;       // [K*P]: entry records of the LDS decode tiles (k_decode_records)
 };
+
+// An entry record: the byte address of a decode tile's first entry word in a
+// message (device addresses fit 48 bits) and the number of the tile's
+// entries in that message (at most a tile's 4096 elements) in the top 16
+// bits; 0 for a tile without entries and for a refused message.
+constexpr uint64_t kRecAddrMask = (uint64_t(1) << 48) - 1u;
 
 // What a message must satisfy before any byte past its header is read: the
 // plan's magic, version, layer count and table hash, and a total length
@@ -201,12 +208,50 @@ k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, MsgGeom
     }
 }
 
+// Per (message, LDS decode tile in launch order): the tile's entry record,
+// so that k_decode_tiles requests its entry words in the same round trip as
+// its count words.  Thread p takes launch position p; the message loop is
+// unrolled by four so that each round's loads are in flight together.
+__global__ void __launch_bounds__(256)
+k_decode_records(MsgPtrs msgs, uint32_t K, const DecDesc* __restrict__ descs, uint32_t P,
+                 uint32_t DT, uint32_t DC, uint32_t nseg, DecodeWs ws) {
+    const uint32_t p = blockIdx.x * 256u + threadIdx.x;
+    if (p >= P) return;
+    const DecDesc dd = descs[p];
+    for (uint32_t k0 = 0; k0 < K; k0 += 4) {
+        uint32_t n[4], cb[4], off[4], ok[4];
+        uint64_t eoff[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t k = min(k0 + uint32_t(u), K - 1u);
+            ok[u] = ws.dvalid[k];
+            n[u] = ws.dcnt[uint64_t(k) * DT + dd.tile];
+            off[u] = ws.doff[uint64_t(k) * DT + dd.tile];
+            cb[u] = ws.dchunk_base[uint64_t(k) * DC + dd.chunk];
+            eoff[u] = ws.dseg_eoff[uint64_t(k) * nseg + dd.si];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t k = k0 + uint32_t(u);
+            if (k >= K) break;
+            uint64_t r = 0;
+            if (ok[u] != 0u && n[u] != 0u) {
+                const uint64_t a = reinterpret_cast<uint64_t>(msgs.p[k]) + eoff[u] +
+                                   (uint64_t(cb[u]) + off[u]) * dd.wb;
+                r = (a & kRecAddrMask) | (uint64_t(n[u]) << 48);
+            }
+            ws.drec[uint64_t(k) * P + p] = r;
+        }
+    }
+}
+
 // Index word at byte address a (w = 8 or 16 bits), read as the aligned
 // 16-bit word that contains it; messages are 16-byte aligned and padded to a
 // multiple of 16 bytes, so the read stays inside the message.
 // The address is formed from integers kept in LDS, so it is cast to a
 // global-address-space pointer (a global load, not a flat one).
 typedef const __attribute__((address_space(1))) uint16_t* global_u16_ptr;
+typedef const __attribute__((address_space(1))) uint32_t* global_u32_ptr;
 
 // Entry rounds whose loads are issued together (1: 1.59 ms for the K = 16
 // decode of the 1.07e9-element workload, 2: 1.50 ms, 4: 1.50 ms).
@@ -548,17 +593,8 @@ k_decode_apply(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
 // OPT != kOptNone: the sums are not written; the tile's weights and
 // optimizer state (requested when the tile starts) take one step.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kMaskMsgs = 16;
 constexpr int kBlkBatch = 2;   // 16-byte entry blocks per thread requested together
 
-// Dynamic LDS bytes of k_decode_tiles: acc_words mask words (and as many sum
-// words with SEP), per message its address, per group message its first
-// entry's address, entry count and s, and the group's bin prefixes.
-inline uint32_t decode_tiles_lds_bytes(uint32_t acc_words, uint32_t K, uint32_t KG,
-                                       uint32_t pstride, bool sep) {
-    const uint32_t accw = (acc_words + 3u) & ~3u;
-    return 4u * (accw * (sep ? 2u : 1u) + 2u * K + 2u * KG + 2u * KG + KG * pstride);
-}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) u32x4* global_u32x4_ptr;
@@ -661,15 +697,6 @@ __device__ __forceinline__ void place_window4(const u32x4& v, int i0, uint32_t w
     }
 }
 
-// Messages per group of k_decode_tiles: at most kMaskMsgs, and as many bin
-// prefixes as fit in kTilesPrefWords LDS words (at least one message).
-constexpr uint32_t kTilesPrefWords = 4096;
-inline uint32_t decode_tiles_group(uint32_t K, uint32_t pstride) {
-    uint32_t kg = kTilesPrefWords / pstride;
-    if (kg > kMaskMsgs) kg = kMaskMsgs;
-    if (kg > K) kg = K;
-    return kg < 1u ? 1u : kg;
-}
 
 template <bool SEP, int OPT>
 __global__ void __launch_bounds__(256)
@@ -1032,6 +1059,361 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                 if (x0 + c >= 0 && x0 + c < int(tlen)) out[e0 + c] = a[c];
         }
     }
+}
+
+// The plain sum of at most kMaskMsgs messages from +0 (the decode of one
+// data-parallel step), one LDS tile per workgroup: the same bits-then-ordered-
+// sums scheme as k_decode_tiles with one group of messages, its message
+// records (k_decode_records) staged at the start, and the tile's first entry
+// blocks copied straight into LDS (global_load_lds) together with the count
+// words, so that the tile needs two round trips to memory before its sums.
+__global__ void __launch_bounds__(256)
+k_decode_tiles_sum(MsgPtrs msgs, uint32_t K, uint32_t pstride, const DecDesc* __restrict__ descs,
+                   uint32_t nseg, DecodeWs ws, float* __restrict__ out, uint32_t acc_words) {
+    constexpr int THREADS = 256, NW = THREADS / 64;
+    constexpr uint32_t NS = kDecCap / 4 / THREADS;   // float4 slots per thread
+    extern __shared__ f32x4 dyn4[];
+    const uint32_t accw = (acc_words + 3u) & ~3u;
+    uint32_t* mask = reinterpret_cast<uint32_t*>(dyn4);                   // [accw]
+    u32x4* blkbuf = reinterpret_cast<u32x4*>(mask + accw);                // [kPreBlocks]
+    uint32_t* blkmeta = reinterpret_cast<uint32_t*>(blkbuf + kPreBlocks); // [kPreBlocks]
+    uint64_t* gl_mp = reinterpret_cast<uint64_t*>(blkmeta + kPreBlocks);  // [K]
+    uint64_t* gl_rc = gl_mp + K;                                          // [K]
+    float* ks = reinterpret_cast<float*>(gl_rc + K);                      // [K]
+    uint32_t* pref = reinterpret_cast<uint32_t*>(ks + K);                 // [K][pstride]
+    const uint32_t k0 = 0, kn = K;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // First round trip: the tile's descriptor (read first, with scalar loads) and, staged
+    // in LDS by wavefront 0 (lane l: message l; lanes past K repeat message K - 1), the
+    // messages' addresses and this tile's entry records.
+    const DecDesc dd = descs[blockIdx.x];
+    if (wv == 0) {
+        const uint32_t l = min(uint32_t(lane), K - 1u);
+        const uint64_t mp = reinterpret_cast<uint64_t>(msgs.p[l]);
+        const uint64_t rc = ws.drec[uint64_t(l) * gridDim.x + blockIdx.x];
+        gl_mp[l] = mp;
+        gl_rc[l] = rc;
+    }
+    // lane l's 64-bit value, in every lane (l the same in every lane)
+    auto lane64 = [](uint64_t x, uint32_t l) -> uint64_t {
+        return (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(x >> 32)), int(l)))) << 32) |
+               uint32_t(__builtin_amdgcn_readlane(int(uint32_t(x)), int(l)));
+    };
+    // lane l's 64-bit value (l per lane; every lane active)
+    auto shfl64 = [](uint64_t x, uint32_t l) -> uint64_t {
+        return (uint64_t(__shfl(uint32_t(x >> 32), int(l))) << 32) | __shfl(uint32_t(x), int(l));
+    };
+    const uint64_t v0 = dd.t0 & ~uint64_t(3);
+    const uint32_t lead = uint32_t(dd.t0 - v0);
+    const uint32_t nvec = (lead + dd.tlen + 3u) >> 2;
+    const uint32_t nb = dd.nb, tlen = dd.tlen, wb = dd.wb, lt = dd.lt;
+    // An always readable address for loads whose result is not used.
+    const uint64_t dummy = reinterpret_cast<uint64_t>(ws.dvalid);
+#pragma unroll
+    for (uint32_t j = 0; j < NS; ++j) {
+        const uint32_t vi = uint32_t(tid) + THREADS * j;
+        if (vi < accw / 4u) reinterpret_cast<u32x4*>(mask)[vi] = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();   // records staged
+    // lanes 0..K-1 of every wavefront: message lane's address and entry record
+    const uint64_t gmp = gl_mp[min(uint32_t(lane), kn - 1u)], grc = gl_rc[min(uint32_t(lane), kn - 1u)];
+
+    // ---- second round trip: the entry words and the count words of the tile's messages ----
+    // Lanes 0..kn-1 of every wavefront: message lane's run of entries for this tile.
+    struct Runs {
+        uint64_t ab;        // address of the run's first word
+        uint32_t ne, nblk;  // its words, and the 16-byte blocks they touch
+        uint32_t bs, NBT;   // the run's first block in the tile, and the tile's blocks
+    };
+    auto runs = [&]() -> Runs {
+        Runs q{0u, 0u, 0u, 0u, 0u};
+        if (uint32_t(lane) < kn) {
+            q.ne = uint32_t(grc >> 48);
+            q.ab = grc & kRecAddrMask;
+            if (q.ne != 0u) q.nblk = uint32_t(((q.ab + uint64_t(q.ne) * wb + 15u) >> 4) - (q.ab >> 4));
+        }
+        const uint32_t incl = wave_incl_add(q.nblk);
+        q.bs = incl - q.nblk;
+        q.NBT = __builtin_amdgcn_readlane(incl, 63);
+        return q;
+    };
+
+    const Runs R0 = runs();
+    const uint32_t NBT = R0.NBT;
+    // Each block is split into 2^sh windows of 16 >> sh bytes (at least one word),
+    // as many as keep the windows within one per thread: the entries of a sparse
+    // tile then spread over the whole workgroup, one or two per thread, while a
+    // dense tile keeps whole blocks per thread.
+    uint32_t sh = 0;
+    while (sh < 3u && (NBT << (sh + 1u)) <= THREADS && (16u >> (sh + 1u)) >= wb) ++sh;
+    const uint32_t NU = NBT << sh, wbytes = 16u >> sh;
+    // Sparse tiles (one window of at most 4 words per thread) keep the slots of their
+    // entries for entry-owned sums; others sum per element afterwards.
+    const bool owned = NU <= THREADS && wbytes <= 4u * wb;
+
+    // Block q of the tile (q < NBT): its message kk -- the last message whose first block
+    // is at or before q (empty messages share their successor's start, so the one found
+    // holds block q) -- by fixed steps 8, 4, 2, 1 with every lane active (a lane shuffle
+    // reads 0 from an inactive lane, so it must not sit in a loop whose trip count differs
+    // between lanes); its address, kept inside that message's blocks whatever q (a message
+    // without blocks is never found; if it were, the always readable dummy word is read
+    // instead); and meta = kk | run length << 4 | (byte index in the run of the block's
+    // first byte + 16) << 17.
+    struct BlkAt {
+        uint64_t addr;
+        uint32_t meta;
+    };
+    auto block_at = [&](const Runs& R, uint32_t q) -> BlkAt {
+        uint32_t kk = 0;
+#pragma unroll
+        for (uint32_t step = kMaskMsgs / 2u; step >= 1u; step >>= 1) {
+            const uint32_t c = kk + step;
+            const uint32_t bc = __shfl(R.bs, int(min(c, kMaskMsgs - 1u)));
+            if (c < kn && bc <= q) kk = c;
+        }
+        const uint64_t a = (uint64_t(__shfl(uint32_t(R.ab >> 32), int(kk))) << 32) |
+                           __shfl(uint32_t(R.ab), int(kk));
+        const uint32_t nbk = __shfl(R.nblk, int(kk));
+        const uint32_t rel = min(q - __shfl(R.bs, int(kk)), nbk - 1u);
+        BlkAt b;
+        b.addr = nbk != 0u ? (a & ~uint64_t(15)) + 16u * uint64_t(rel) : dummy & ~uint64_t(15);
+        b.meta = kk | (__shfl(R.ne, int(kk)) << 4) | (uint32_t(int(int64_t(b.addr) - int64_t(a)) + 16) << 17);
+        return b;
+    };
+    // Count words into registers, one lane per bin, then per-message prefixes by DPP
+    // scans.  Every load is issued without a branch (unused lanes, and messages without
+    // entries in this tile, read `dummy`), so that all of a wavefront's loads are in
+    // flight together; a load (the aligned 32 bits holding the word: count regions are
+    // 16-byte aligned and padded, so they lie inside the message) and the word's value
+    // are separate steps, so that no use of a loaded value sits between the loads.
+    auto put_prefix = [&](uint32_t kk, uint32_t b, uint32_t inc) {
+        if (kk < kn && b < nb) {
+            pref[kk * pstride + b + 1u] = inc;
+            if (b == 0u) pref[kk * pstride] = 0u;
+        }
+    };
+    // Address of the tile's first count word in message kk, or 0 when the message
+    // has no entries in this tile (kk the same in every lane of the wavefront).
+    auto first_count = [&](uint32_t kk) -> uint64_t {
+        const uint32_t kc = min(kk, kn - 1u);
+        const uint64_t rc = lane64(grc, kc), mk = lane64(gmp, kc);
+        return kk < kn && (rc >> 48) != 0u ? mk + dd.count_at : 0u;
+    };
+    auto count_load = [&](uint64_t first, uint32_t b) -> uint32_t {
+        const uint64_t a = first != 0u && b < nb ? first + uint64_t(b) * wb : dummy;
+        return *(global_u32_ptr)(a & ~uint64_t(3));
+    };
+    auto count_value = [&](uint64_t first, uint32_t b, uint32_t raw) -> uint32_t {
+        // messages are 16-byte aligned: the word's place in the 32 bits is that of count_at + b wb
+        const uint32_t sh8 = 8u * uint32_t((dd.count_at + uint64_t(b) * wb) & 3u);
+        const uint32_t w = (raw >> sh8) & (wb == 1u ? 0xFFu : 0xFFFFu);
+        return first != 0u && b < nb ? w : 0u;
+    };
+    // Bins of up to 16: one message per row of 16 lanes (wavefront wv, row q holds
+    // message 4 wv + q).  Up to 128: wavefront wv holds messages wv + 4 m (m < 4), bins
+    // lane and 64 + lane.  The count words of those are requested before the entry blocks
+    // below; longer runs of short bins come after, 256 bins of a message at a time.
+    const uint32_t kk16 = 4u * uint32_t(wv) + (uint32_t(lane) >> 4), b16 = uint32_t(lane) & 15u;
+    uint64_t f16 = 0;
+    uint64_t f128[4] = {0, 0, 0, 0};
+    uint32_t cw[8];
+    if (nb <= 16u) {
+        const uint32_t kc = min(kk16, kn - 1u);
+        const uint64_t rc = shfl64(grc, kc), mk = shfl64(gmp, kc);
+        f16 = kk16 < kn && (rc >> 48) != 0u ? mk + dd.count_at : 0u;
+        cw[0] = count_load(f16, b16);
+    } else if (nb <= 128u) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) f128[m] = first_count(uint32_t(wv) + NW * uint32_t(m));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cw[u] = count_load(f128[u >> 1], 64u * uint32_t(u & 1) + uint32_t(lane));
+    }
+    // The tile's first kPreBlocks blocks are copied straight into LDS (no registers held
+    // while they are in flight), one per lane of wavefronts 0 and 1, requested while the count
+    // words are in flight, so that both arrive in one round trip.
+    if (NBT != 0u && uint32_t(wv) < kPreBlocks / 64u) {   // wavefront-uniform
+        const BlkAt b = block_at(R0, min(uint32_t(tid), NBT - 1u));
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)b.addr,
+                                         (__attribute__((address_space(3))) void*)(blkbuf + 64u * uint32_t(wv)),
+                                         16, 0, 0);
+        if (uint32_t(tid) < NBT) blkmeta[tid] = b.meta;
+    }
+    float a_s = 0.0f;
+    if (tid < int(kn)) a_s = ws.dseg_s[uint64_t(k0 + uint32_t(tid)) * nseg + dd.si];
+
+    if (nb <= 16u) {
+        put_prefix(kk16, b16, row_incl_add(count_value(f16, b16, cw[0])));
+    } else if (nb <= 128u) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t kk = uint32_t(wv) + NW * uint32_t(m);
+            const uint32_t lo = wave_incl_add(count_value(f128[m], uint32_t(lane), cw[2 * m]));
+            const uint32_t hi = wave_incl_add(count_value(f128[m], 64u + uint32_t(lane), cw[2 * m + 1])) +
+                                __builtin_amdgcn_readlane(lo, 63);
+            put_prefix(kk, uint32_t(lane), lo);
+            put_prefix(kk, 64u + uint32_t(lane), hi);
+        }
+    } else {
+        for (uint32_t kk = uint32_t(wv); kk < kn; kk += NW) {
+            const uint64_t f = first_count(kk);
+            uint32_t carry = 0;
+            for (uint32_t b0 = 0; b0 < nb; b0 += 256u) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) cw[u] = count_load(f, b0 + 64u * uint32_t(u) + uint32_t(lane));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t b = b0 + 64u * uint32_t(u) + uint32_t(lane);
+                    const uint32_t inc = wave_incl_add(count_value(f, b, cw[u])) + carry;
+                    put_prefix(kk, b, inc);
+                    carry = __builtin_amdgcn_readlane(inc, 63);
+                }
+            }
+        }
+    }
+    if (tid < int(kn)) ks[tid] = a_s;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the blocks copied into LDS
+    __syncthreads();   // the tile's blocks, bin prefixes and s are in LDS
+
+    // ---- the entries' bits: unit u is window u & (2^sh - 1) of block u >> sh ----
+    uint32_t own_x[4] = {kNoSlot, kNoSlot, kNoSlot, kNoSlot}, own_hit = 0;
+    const uint32_t wsh = wb == 1u ? 0u : 1u;
+    if (owned) {   // one window per thread; owned implies NBT <= kPreBlocks, all copied
+        const uint32_t q = min(uint32_t(tid), NU - 1u) >> sh;
+        if (uint32_t(tid) < NU) {
+            const uint32_t m = blkmeta[q];
+            const uint32_t kk = m & 15u, sq = (uint32_t(tid) & ((1u << sh) - 1u)) * wbytes;
+            own_hit = 1u << kk;
+            place_window4(blkbuf[q], (int(m >> 17) - 16) >> wsh, sq >> wsh, (sq + wbytes) >> wsh,
+                          (m >> 4) & 0x1FFFu, pref + kk * pstride, nb, lt, tlen, lead, wb, own_hit,
+                          mask, own_x);
+        }
+    } else {
+        const Runs R = runs();
+        for (uint32_t u0 = 0; u0 < NU; u0 += THREADS * kBlkBatch) {   // workgroup-uniform
+            u32x4 v[kBlkBatch] = {};
+            uint32_t mt[kBlkBatch] = {};
+#pragma unroll
+            for (int r = 0; r < kBlkBatch; ++r) {
+                if (u0 + THREADS * uint32_t(r) >= NU) break;   // workgroup-uniform
+                const uint32_t q = min(u0 + THREADS * uint32_t(r) + uint32_t(tid), NU - 1u) >> sh;
+                const BlkAt b = block_at(R, q);
+                if (q < kPreBlocks) {
+                    v[r] = blkbuf[q];
+                    mt[r] = blkmeta[q];
+                } else {
+                    v[r] = *(global_u32x4_ptr)b.addr;
+                    mt[r] = b.meta;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < kBlkBatch; ++r) {
+                if (u0 + THREADS * uint32_t(r) >= NU) break;   // workgroup-uniform
+                const uint32_t u = u0 + THREADS * uint32_t(r) + uint32_t(tid);
+                if (u >= NU) continue;
+                const uint32_t m = mt[r], kk = m & 15u, sq = (u & ((1u << sh) - 1u)) * wbytes;
+                place_window(v[r], (int(m >> 17) - 16) >> wsh, sq >> wsh, (sq + wbytes) >> wsh,
+                             (m >> 4) & 0x1FFFu, pref + kk * pstride, nb, lt, tlen, lead, wb, 1u << kk, mask);
+            }
+            // every lane's blocks are taken in here, also where a lane placed nothing, so that
+            // no load is still counted as in flight after the loop (later writes to those
+            // registers would wait for it)
+#pragma unroll
+            for (int r = 0; r < kBlkBatch; ++r) asm volatile("" ::"v"(v[r]));
+        }
+    }
+    __syncthreads();   // every bit is set
+
+    f32x4 a4[NS];   // this thread's sums
+    // ---- sums: each thread its own elements, hits in message order ----
+    if (owned) {
+        // Entry-owned: the entry of an element's lowest-numbered message adds all of the
+        // element's hits in message order and writes the float over the bits, once every
+        // entry has read its element's bits.  An element no message sends keeps 0, +0.0f.
+        float r[4];
+        uint32_t mine = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r[e] = 0.0f;
+            if (own_x[e] != kNoSlot) {
+                const uint32_t m = mask[own_x[e]];
+                if (((m & 0xFFFFu) & (own_hit - 1u)) == 0u) {
+                    mine |= 1u << e;
+                    uint32_t h = m & 0xFFFFu;
+                    float acc = 0.0f;
+                    while (h != 0u) {
+                        const uint32_t kk = __builtin_ctz(h);
+                        h &= h - 1u;
+                        const float s = ks[kk];
+                        acc = acc + (((m >> (16u + kk)) & 1u) ? -s : s);
+                    }
+                    r[e] = acc;
+                }
+            }
+        }
+        __syncthreads();   // every entry has read its element's bits
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if ((mine >> e) & 1u) mask[own_x[e]] = __float_as_uint(r[e]);
+        __syncthreads();
+#pragma unroll
+        for (uint32_t j = 0; j < NS; ++j) {
+            const uint32_t vi = uint32_t(tid) + THREADS * j;
+            a4[j] = vi < nvec ? reinterpret_cast<const f32x4*>(mask)[vi] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    } else {
+        // The sums stay in registers.  An element's first hit is looked up
+        // for the four elements of a slot together (four independent LDS reads); only
+        // elements with more hits loop over the rest.
+#pragma unroll
+        for (uint32_t j = 0; j < NS; ++j) {
+            const uint32_t vi = uint32_t(tid) + THREADS * j;
+            u32x4 m4 = {0u, 0u, 0u, 0u};
+            if (vi < nvec) m4 = reinterpret_cast<const u32x4*>(mask)[vi];
+            float s1[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s1[c] = ks[__builtin_ctz((m4[c] & 0xFFFFu) | 0x10000u) & 15u];
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t m = m4[c];
+                uint32_t h = m & 0xFFFFu;
+                const uint32_t k1 = __builtin_ctz(h | 0x10000u);
+                float acc = h != 0u ? (((m >> (16u + k1)) & 1u) ? -s1[c] : s1[c]) : 0.0f;
+                h &= h - 1u;
+                while (h != 0u) {
+                    const uint32_t kk = __builtin_ctz(h);
+                    h &= h - 1u;
+                    const float s = ks[kk];
+                    acc = acc + (((m >> (16u + kk)) & 1u) ? -s : s);
+                }
+                a[c] = acc;
+            }
+            a4[j] = a;
+        }
+    }
+
+    // ---- the tile's sums, written once ----
+    // Whole float4 first, then the tile's ragged ends; the sums stay live until the last
+    // store, so that no register a store reads is reused for arithmetic (which would wait
+    // for that store to complete).
+#pragma unroll
+    for (uint32_t j = 0; j < NS; ++j) {
+        const uint32_t vi = uint32_t(tid) + THREADS * j;
+        const int x0 = int(vi * 4) - int(lead);
+        if (vi < nvec && x0 >= 0 && x0 + 4 <= int(tlen)) store4<true>(out + v0 + uint64_t(vi) * 4u, a4[j]);
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < NS; ++j) {
+        const uint32_t vi = uint32_t(tid) + THREADS * j;
+        const int x0 = int(vi * 4) - int(lead);
+        if (vi < nvec && !(x0 >= 0 && x0 + 4 <= int(tlen))) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (x0 + c >= 0 && x0 + c < int(tlen)) out[v0 + uint64_t(vi) * 4u + c] = a4[j][c];
+        }
+    }
+    asm volatile("" ::"v"(a4[0]), "v"(a4[1]), "v"(a4[2]), "v"(a4[3]));
 }
 
 // The optimizer step for long-bin decode tiles, whose sums were accumulated

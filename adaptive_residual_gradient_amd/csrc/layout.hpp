@@ -175,6 +175,40 @@ inline uint32_t decode_group(uint32_t K, uint32_t pstride) {
     return kg < 1u ? 1u : kg;
 }
 
+// The LDS decode tiles (k_decode_tiles) hold one 32-bit word per element for
+// a group of up to kMaskMsgs messages: a hit bit and a sign bit per message.
+constexpr uint32_t kMaskMsgs = 16;
+// Entry blocks (16 bytes) per message group that k_decode_tiles copies
+// straight into LDS together with the count words.
+constexpr uint32_t kPreBlocks = 128;
+
+// Dynamic LDS bytes of k_decode_tiles: acc_words mask words (and as many sum
+// words with SEP), per message its address, per group message its first
+// entry's address, entry count and s, and the group's bin prefixes.
+inline uint32_t decode_tiles_lds_bytes(uint32_t acc_words, uint32_t K, uint32_t KG,
+                                       uint32_t pstride, bool sep) {
+    const uint32_t accw = (acc_words + 3u) & ~3u;
+    return 4u * (accw * (sep ? 2u : 1u) + 2u * K + 2u * KG + 2u * KG + KG * pstride);
+}
+
+// Dynamic LDS bytes of k_decode_tiles_sum (K <= kMaskMsgs messages): the mask
+// words, kPreBlocks entry blocks and a word of placement data each, per
+// message its address, entry record and s, and the bin prefixes.
+inline uint32_t decode_sum_lds_bytes(uint32_t acc_words, uint32_t K, uint32_t pstride) {
+    const uint32_t accw = (acc_words + 3u) & ~3u;
+    return 4u * (accw + 5u * kPreBlocks + 5u * K + K * pstride);
+}
+
+// Messages per group of k_decode_tiles: at most kMaskMsgs, and as many bin
+// prefixes as fit in kTilesPrefWords LDS words (at least one message).
+constexpr uint32_t kTilesPrefWords = 4096;
+inline uint32_t decode_tiles_group(uint32_t K, uint32_t pstride) {
+    uint32_t kg = kTilesPrefWords / pstride;
+    if (kg > kMaskMsgs) kg = kMaskMsgs;
+    if (kg > K) kg = K;
+    return kg < 1u ? 1u : kg;
+}
+
 struct Layout {
     uint32_t nseg = 0;
     uint32_t plan_hash = 0;
@@ -352,9 +386,10 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
     // Decode workspace for K messages: a status block, then arrays indexed by
     // message: decode-tile counts and offsets [K*DT], chunk counts and bases
     // [K*DC], per-segment s and entry offsets [K*nseg], per-message validity
-    // [K].  Each array is kAlign-aligned, so fixed covers the padding of all.
-    L.dws_fixed = 9 * kAlign;
-    L.dws_per_msg = round_up(8 * L.dt.ntiles + 8 * L.dt.nchunks + 12 * uint64_t(nseg) + 4, 16);
+    // [K], and an 8-byte entry record per LDS decode tile [K*P], P <= DT.
+    // Each array is kAlign-aligned, so fixed covers the padding of all.
+    L.dws_fixed = 10 * kAlign;
+    L.dws_per_msg = round_up(16 * L.dt.ntiles + 8 * L.dt.nchunks + 12 * uint64_t(nseg) + 4, 16);
     return ADACOMP_OK;
 }
 

@@ -113,6 +113,15 @@ static std::string check(const std::vector<adacomp_segment>& segs, int expect_st
         const uint32_t acc = v == 0 ? L.dt.max_span_vecs[0] * 4 : 0;
         if (decode_lds_bytes(acc, ADACOMP_MAX_MESSAGES, kg, ps, kDecThreads[v] / 64) > 65536)
             return "FAIL decode LDS";
+        if (v == 0) {
+            const uint32_t tg = decode_tiles_group(ADACOMP_MAX_MESSAGES, ps);
+            if (decode_tiles_lds_bytes(acc, ADACOMP_MAX_MESSAGES, tg, ps, true) > 65536)
+                return "FAIL decode tiles LDS";
+            // the plain sum of up to kMaskMsgs messages, where they fit one group
+            if (decode_tiles_group(kMaskMsgs, ps) == kMaskMsgs &&
+                decode_sum_lds_bytes(acc, kMaskMsgs, ps) > 65536)
+                return "FAIL decode sum LDS";
+        }
     }
     return "OK tiles=" + std::to_string(L.ct.ntiles) + " dtiles=" + std::to_string(L.dt.ntiles);
 }
