@@ -29,6 +29,7 @@ MAX_BIN_LEN = 32768
 SEG_LS = 1   # segment flag: hard local selection (see include/adacomp.h)
 PLAN_SEPARATE_FINISH = 1   # plan flag: finish with three kernels whatever the table
 PLAN_SINGLE_LAUNCH = 2     # plan flag: a small table in one launch (slower; for comparison)
+PLAN_DECODE_RECORDS = 4    # plan flag: plain sums always take the entry-record decode
 SMALL_TABLE_MAX_SPAN = 1 << 21     # tables up to this span and this many segments
 SMALL_TABLE_MAX_SEGMENTS = 256     # finish in one launch after the tile pass
 NOALLOC_SCRATCH_BYTES = 128 << 20  # largest compress workspace compress_noalloc takes

@@ -42,7 +42,14 @@ struct adacomp_plan {
     uint32_t small_lds_bytes = 0;   // k_finish_small's dynamic LDS
     uint32_t single_lds_bytes = 0;  // k_compress_single's: tile or finish tables, the larger
     uint32_t chunk_lds_bytes = 0;   // k_finish_chunks' dynamic LDS
+    // Plain sums of up to 16 messages take k_decode_tiles_sum: plans with at least
+    // kSumKernelMinTiles LDS decode tiles, all of 16-bit words, or made with
+    // ADACOMP_PLAN_DECODE_RECORDS.  Measured on MI355X
+    // (K = 16, step-10 messages): 1.07e9 elements at L_T 500, 1.30 -> 1.15 ms; at L_T 50
+    // (8-bit words, dense tiles) 2.12 -> 2.32 ms; 25e6 elements at L_T 500, 51.6 -> 57.6 us.
+    bool sum_kernel = false;
 };
+constexpr uint64_t kSumKernelMinTiles = 65536;
 
 namespace adacomp {
 // NTS: non-temporal residue stores (tables past kCachedResidueMaxElems).
@@ -263,8 +270,9 @@ int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t 
                            adacomp_plan** out) {
     if (out == nullptr) return ADACOMP_ERR_INVALID_ARGUMENT;
     *out = nullptr;
-    if (plan_flags != 0u && plan_flags != ADACOMP_PLAN_SEPARATE_FINISH &&
-        plan_flags != ADACOMP_PLAN_SINGLE_LAUNCH)
+    const uint32_t finish_flags = plan_flags & ~ADACOMP_PLAN_DECODE_RECORDS;
+    if (finish_flags != 0u && finish_flags != ADACOMP_PLAN_SEPARATE_FINISH &&
+        finish_flags != ADACOMP_PLAN_SINGLE_LAUNCH)
         return ADACOMP_ERR_INVALID_ARGUMENT;
     adacomp_plan* p = nullptr;
     try {
@@ -320,7 +328,7 @@ int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t 
             const std::vector<adacomp::DecDesc> d = adacomp::decode_descs(L, v);
             o_desc[v] = put(d.data(), sizeof(adacomp::DecDesc) * d.size());
         }
-        p->finish = adacomp::choose_finish(L, plan_flags);
+        p->finish = adacomp::choose_finish(L, finish_flags);
         uint64_t o_t0 = 0;
         if (adacomp::uses_small_tables(p->finish)) {
             std::vector<uint32_t> t0(L.ct.ntiles);
@@ -367,6 +375,11 @@ int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t 
             p->small_lds_bytes);
         p->chunk_lds_bytes = static_cast<uint32_t>(
             adacomp::round_up(adacomp::chunk_finish_lds_bytes(L.ct.nchunks, L.nseg), 8));
+        p->sum_kernel = L.dt.by_variant[0].size() >= kSumKernelMinTiles;
+        for (const SegDev& sg : L.segs)
+            if (sg.dt.variant == 0u && sg.wb != 2u) p->sum_kernel = false;
+        if (plan_flags & ADACOMP_PLAN_DECODE_RECORDS) p->sum_kernel = true;
+        if (L.dt.by_variant[0].empty()) p->sum_kernel = false;
         *out = p;
         return ADACOMP_OK;
     } catch (...) {
@@ -682,10 +695,11 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
     geo.entries_begin = L.entries_begin;
     geo.capacity = L.capacity;
 
-    // The plain sum of at most 16 messages from +0 over LDS tiles takes the two-round-trip
-    // kernel; everything else (more messages, out += sum, an optimizer step) k_decode_tiles.
+    // The plain sum of at most 16 messages from +0 over many LDS tiles of 16-bit words
+    // (sparse messages) takes the two-round-trip kernel; everything else (more messages,
+    // out += sum, an optimizer step, 8-bit words, smaller tables) k_decode_tiles.
     const uint32_t ps0 = L.dt.max_bpt[0] + 1;
-    const bool plain_sum = !L.dt.by_variant[0].empty() && !fused && accumulate == 0 &&
+    const bool plain_sum = plan->sum_kernel && !fused && accumulate == 0 &&
                            adacomp::decode_tiles_group(K, ps0) == K;
     CallTimer tm(timer, stream, call_stage);
     {
@@ -733,8 +747,9 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
                 } else if (opt == adacomp::kOptAdam) {
                     if (sep) ADACOMP_TILES(true, adacomp::kOptAdam);
                     else ADACOMP_TILES(false, adacomp::kOptAdam);
-                } else {   // out += sum, or more messages than one group (sep)
-                    ADACOMP_TILES(true, adacomp::kOptNone);
+                } else {
+                    if (sep) ADACOMP_TILES(true, adacomp::kOptNone);
+                    else ADACOMP_TILES(false, adacomp::kOptNone);
                 }
 #undef ADACOMP_TILES
             } else if (long_decode_in_lds(L, K, KG, ps, opt)) {

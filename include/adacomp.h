@@ -145,11 +145,19 @@ int adacomp_plan_create(const adacomp_segment* segs, uint32_t nseg, adacomp_plan
  *   alone.  Correct, but slower on MI355X than the default (the release of
  *   every tile and one CU's scattered stores cost more than the launches it
  *   saves); built for comparison.  Other tables ignore it.
- * The two flags are exclusive. */
+ * The two flags are exclusive.
+ * DECODE_RECORDS: plain sums (adacomp_decode_accumulate with accumulate = 0)
+ *   of at most 16 messages over bins of at most 4093 elements always take the
+ *   entry-record decode (a per-tile record pass, then tiles that read their
+ *   count and entry words in one round trip).  By default only tables of at
+ *   least 65536 such tiles, all of 16-bit words, take it; smaller tables and
+ *   8-bit words measured faster without it.  Combines with either flag above. */
 #define ADACOMP_PLAN_SEPARATE_FINISH 1u
 #define ADACOMP_PLAN_SINGLE_LAUNCH 2u
-/* adacomp_plan_create with plan flags (0, or one of the above; any other
- * value is ADACOMP_ERR_INVALID_ARGUMENT). */
+#define ADACOMP_PLAN_DECODE_RECORDS 4u
+/* adacomp_plan_create with plan flags (0, or an OR of the above with at most
+ * one of SEPARATE_FINISH and SINGLE_LAUNCH; any other value is
+ * ADACOMP_ERR_INVALID_ARGUMENT). */
 int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t plan_flags,
                            adacomp_plan** plan);
 int adacomp_plan_destroy(adacomp_plan* plan);

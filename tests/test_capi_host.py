@@ -137,7 +137,8 @@ def test_plan_flags_rejected_before_any_device_call():
     L = A.lib()
     arr, n = A._segments([(0, 1000, 50)])
     h = ctypes.c_void_p()
-    for flags in (3, 4, 0x80000000):
+    # both finish flags together, with or without the decode flag; unknown bits
+    for flags in (3, 7, 8, 12, 0x80000000):
         assert L.adacomp_plan_create_ex(arr, n, flags, ctypes.byref(h)) == -1
         assert h.value is None
 

@@ -46,11 +46,17 @@ def host(t):
     return t.cpu().numpy()
 
 
+# flags: the default kernel choice, and plain sums forced onto the entry-record
+# kernel (taken by default only by tables of at least 65536 tiles)
+FLAGS = [0, A.PLAN_DECODE_RECORDS]
+
+
+@pytest.mark.parametrize("flags", FLAGS)
 @pytest.mark.parametrize("name,K", [("fc", 1), ("fc", 3), ("conv", 4), ("resnet50", 16),
                                     ("fc_lstm", 2)])
-def test_decode_parity(name, K):
+def test_decode_parity(name, K, flags):
     wl = W.workload(name)
-    plan = A.Plan(wl.segments)
+    plan = A.Plan(wl.segments, plan_flags=flags)
     n = W.alloc_len(wl)
     msgs = learner_messages(wl, plan, K)
     host_msgs = [host(m) for m in msgs]
@@ -70,8 +76,9 @@ def test_decode_parity(name, K):
     plan.close()
 
 
+@pytest.mark.parametrize("flags", FLAGS)
 @pytest.mark.parametrize("lt", [1, 3, 7, 50, 64, 500, 1021, 4093, 4094, 9000, 18432, 18433, 32768])
-def test_decode_edge_tables(lt):
+def test_decode_edge_tables(lt, flags):
     """Every decode tile shape: LDS tiles (L_T <= 4093), long bins with at
     least two bins per tile accumulated in LDS (4094 .. 18432) and one bin
     per tile accumulated in place (18433 and up); ragged and one-element
@@ -81,7 +88,7 @@ def test_decode_edge_tables(lt):
         segs.append((off, n, lt))
         off += (n + 3) // 4 * 4 + 4
     span = off
-    plan = A.Plan(segs)
+    plan = A.Plan(segs, plan_flags=flags)
     rng = np.random.default_rng(lt)
     cws = plan.compress_workspace(DEV)
     msgs = []
@@ -107,12 +114,13 @@ def test_decode_edge_tables(lt):
     plan.close()
 
 
-def test_decode_skips_foreign_messages():
+@pytest.mark.parametrize("flags", FLAGS)
+def test_decode_skips_foreign_messages(flags):
     """A message made for another segment table contributes nothing and is
     counted in the status word."""
     segs = [(0, 5000, 50)]
     other = [(0, 5000, 500)]
-    plan, plan2 = A.Plan(segs), A.Plan(other)
+    plan, plan2 = A.Plan(segs, plan_flags=flags), A.Plan(other)
     r = torch.zeros(5000, dtype=torch.float32, device=DEV)
     d = torch.from_numpy((np.random.default_rng(0).standard_normal(5000) * 1e-3)
                          .astype(np.float32)).to(DEV)
@@ -139,7 +147,8 @@ def _get(buf, at, dtype):
     return np.frombuffer(buf[at:at + np.dtype(dtype).itemsize].tobytes(), dtype)[0]
 
 
-def test_decode_rejects_inconsistent_messages():
+@pytest.mark.parametrize("flags", FLAGS)
+def test_decode_rejects_inconsistent_messages(flags):
     """Messages whose header matches the plan but whose body is inconsistent,
     every offset still inside the buffer, are refused one by one: the others
     are summed as the oracle sums them alone, and the refused ones are
@@ -149,7 +158,7 @@ def test_decode_rejects_inconsistent_messages():
     alignment; a total length past the plan's capacity."""
     segs = [(0, 6000, 50), (6000, 9000, 500)]
     wl_n = 15000
-    plan = A.Plan(segs)
+    plan = A.Plan(segs, plan_flags=flags)
     ws_c = plan.compress_workspace(DEV)
     rng = np.random.default_rng(77)
     good = []

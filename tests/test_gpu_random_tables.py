@@ -12,8 +12,9 @@ whichever the table takes; three-kernel; single launch where it applies):
 their messages, residues and bin maxima must be equal byte for byte, and
 the default's first two must match the oracle (tests/parity.py).  Then the
 case's four messages, with a foreign one among them, are decoded
-(accumulate into a random start), decoded with an SGD step and with an Adam
-step, each against the oracle bit for bit."""
+(accumulate into a random start; summed from +0 by the default decode and by
+the entry-record decode the three-kernel plan's flag selects), decoded with
+an SGD step and with an Adam step, each against the oracle bit for bit."""
 import sys
 
 import numpy as np
@@ -77,7 +78,7 @@ def test_random_table(seed):
     segs, span = random_table(rng)
     kind = ["normal", "ties", "wide"][seed % 3]
     scale = float(10.0 ** rng.uniform(-6, 0))
-    plans = [A.Plan(segs), A.Plan(segs, plan_flags=A.PLAN_SEPARATE_FINISH),
+    plans = [A.Plan(segs), A.Plan(segs, plan_flags=A.PLAN_SEPARATE_FINISH | A.PLAN_DECODE_RECORDS),
              A.Plan(segs, plan_flags=A.PLAN_SINGLE_LAUNCH)]
     info = plans[0].info
     say(f"  seed {seed}: {len(segs)} layers, span {span}, {info.ntiles} tiles, {kind}, "
@@ -120,6 +121,13 @@ def test_random_table(seed):
     want = start.copy()
     oracle.decode_accumulate(segs, msgs, want, True)
     assert np.array_equal(bits(out.cpu().numpy()), bits(want)), "decode_accumulate"
+    # the plain sum, also on the entry-record decode (the second plan carries that flag)
+    for pl in (plans[0], plans[1]):
+        out = torch.from_numpy(start.copy()).to(DEV)
+        A.decode_accumulate(pl, dev_msgs, out, False, pl.decode_workspace(K, DEV))
+        want = start.copy()
+        oracle.decode_accumulate(segs, msgs, want, False)
+        assert np.array_equal(bits(out.cpu().numpy()), bits(want)), "decode (sum)"
 
     ws = plan.decode_sgd_workspace(K, DEV)
     w0 = random_values(rng, span, "normal", 1.0)
