@@ -1087,11 +1087,12 @@ k_decode_tiles_sum(MsgPtrs msgs, uint32_t K, uint32_t pstride, const DecDesc* __
     // First round trip: the tile's descriptor (read first, with scalar loads) and, staged
     // in LDS by wavefront 0 (lane l: message l; lanes past K repeat message K - 1), the
     // messages' addresses and this tile's entry records.
-    const DecDesc dd = descs[blockIdx.x];
+    const uint32_t pos = xcd_grouped(blockIdx.x, gridDim.x);   // this tile's launch position
+    const DecDesc dd = descs[pos];
     if (wv == 0) {
         const uint32_t l = min(uint32_t(lane), K - 1u);
         const uint64_t mp = reinterpret_cast<uint64_t>(msgs.p[l]);
-        const uint64_t rc = ws.drec[uint64_t(l) * gridDim.x + blockIdx.x];
+        const uint64_t rc = ws.drec[uint64_t(l) * gridDim.x + pos];
         gl_mp[l] = mp;
         gl_rc[l] = rc;
     }

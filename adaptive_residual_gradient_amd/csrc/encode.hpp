@@ -327,7 +327,7 @@ __device__ __forceinline__ void encode_wave(uint32_t w, uint32_t W, const SegDev
         // its first word taken here, s, L_T | word bytes, magic.
         uint64_t t0 = 0, eat = 0;
         float s = 0.0f;
-        uint32_t ltwb = 0, mag = 0;
+        uint32_t ltwb = 0, mag = 0, gofs = kSentinel;
         if (cnt != 0 && excl < take) {
             const SegDev q = segs[si];
             const TileGeom tg = tile_geom(q, q.ct, tl);
@@ -338,12 +338,18 @@ __device__ __forceinline__ void encode_wave(uint32_t w, uint32_t W, const SegDev
             s = seg_s[si];
             ltwb = (q.lt << 2) | q.wb;
             mag = q.magic;
+            // k_tile_pass stages each survivor's G after the tile's keys when both fit
+            const uint32_t full = cnt + skip;
+            if (q.ct.variant != 2u && 2u * full <= tg.tlen) gofs = full;
         }
         // Survivors base + 64u + lane (u < kEncBatch), clamped to the last one: owning lane,
-        // rank in the owner's tile, the tile's first element and the staged key.
+        // rank in the owner's tile, the tile's first element, the staged key and, where it
+        // was staged, G (staged[u]).
         struct Batch {
             uint32_t own[kEncBatch], k[kEncBatch], key[kEncBatch];
             uint64_t tt[kEncBatch];
+            float g[kEncBatch];
+            bool staged[kEncBatch];
         };
         auto issue = [&](uint32_t base, Batch& b) {
 #pragma unroll
@@ -357,19 +363,24 @@ __device__ __forceinline__ void encode_wave(uint32_t w, uint32_t W, const SegDev
                 b.k[u] = e - __shfl(excl, int(L));
                 b.tt[u] = (uint64_t(__shfl(uint32_t(t0 >> 32), int(L))) << 32) |
                           __shfl(uint32_t(t0), int(L));
-                b.key[u] = stage[b.tt[u] + (L == 0 ? r0 : 0u) + b.k[u]];
+                const uint32_t rk = (L == 0 ? r0 : 0u) + b.k[u], go = __shfl(gofs, int(L));
+                b.key[u] = stage[b.tt[u] + rk];
+                b.staged[u] = go != kSentinel;
+                b.g[u] = b.staged[u] ? __uint_as_float(stage[b.tt[u] + go + rk]) : 0.0f;
             }
         };
         if (take != 0) {   // wavefront-uniform; the window advances below either way
-            // Two round trips per batch (the staged keys, then G at those elements): the next
-            // batch's keys are requested (always, clamped) while this batch's G is in flight.
+            // One round trip per batch where G was staged with the keys, else two (the keys,
+            // then G at those elements): the next batch's keys are requested (always,
+            // clamped) while this batch's G is in flight.
             Batch cur;
             issue(0, cur);
             for (uint32_t base = 0; base < take; base += 64u * kEncBatch) {   // wavefront-uniform
                 // G of every survivor of the batch (the tile pass left residue = G there).
                 float gq[kEncBatch];
 #pragma unroll
-                for (int u = 0; u < kEncBatch; ++u) gq[u] = residue[cur.tt[u] + (cur.key[u] & 0x7FFFFFFFu)];
+                for (int u = 0; u < kEncBatch; ++u)
+                    gq[u] = cur.staged[u] ? cur.g[u] : residue[cur.tt[u] + (cur.key[u] & 0x7FFFFFFFu)];
                 Batch nxt;
                 issue(base + 64u * kEncBatch, nxt);
 #pragma unroll

@@ -178,9 +178,28 @@ inline uint32_t decode_group(uint32_t K, uint32_t pstride) {
 // The LDS decode tiles (k_decode_tiles) hold one 32-bit word per element for
 // a group of up to kMaskMsgs messages: a hit bit and a sign bit per message.
 constexpr uint32_t kMaskMsgs = 16;
-// Entry blocks (16 bytes) per message group that k_decode_tiles copies
-// straight into LDS together with the count words.
+// Entry blocks (16 bytes) per tile that k_decode_tiles_sum copies straight
+// into LDS together with the count words.
 constexpr uint32_t kPreBlocks = 128;
+
+// Launch position of workgroup b of n, in runs of kXcdGroup consecutive
+// positions per XCD.  The dispatcher hands workgroups to the 8 XCDs in turn
+// (workgroup b to XCD b % 8), and each XCD has its own L2.  Neighbouring
+// decode tiles share the cache lines of their per-message count words,
+// entry words and entry records, so with consecutive positions on different
+// XCDs each such line is fetched into several L2s.  Workgroup b takes
+// position 8G*floor(b/8G) + G*(b % 8) + floor(b/8) % G (G = kXcdGroup), and
+// the last n mod 8G workgroups keep their own positions: a bijection of
+// [0, n).  Runs of 8 made the plain K = 16 decode of 1.07e9 elements
+// (k_decode_tiles_sum) 1.096 -> 1.073 ms; in k_decode_tiles they made the
+// fused SGD and Adam steps slower (2.79 -> 2.91 ms, 4.28 -> 4.36 ms), and
+// one contiguous run per XCD slowed every decode (SGD 3.21 ms).
+constexpr uint32_t kXcdGroup = 8;
+ADACOMP_HD constexpr uint32_t xcd_grouped(uint32_t b, uint32_t n) {
+    return b >= n / (8u * kXcdGroup) * (8u * kXcdGroup)
+               ? b
+               : (b & ~(8u * kXcdGroup - 1u)) | ((b & 7u) * kXcdGroup) | ((b >> 3) & (kXcdGroup - 1u));
+}
 
 // Dynamic LDS bytes of k_decode_tiles: acc_words mask words (and as many sum
 // words with SEP), per message its address, per group message its first
@@ -370,7 +389,7 @@ inline int build_layout(const adacomp_segment* segs, uint32_t nseg, Layout& L) {
         return at;
     };
     L.ws_sync = take(8);
-    L.ws_stage = take(4 * L.span);     // sign | in-tile offset of each survivor, at its tile's offset
+    L.ws_stage = take(4 * L.span);     // per tile at its offset: survivor keys (sign | offset), then G where it fits
     L.ws_tile_cnt = take(4 * tiles);
     L.ws_tile_gsum = take(8 * tiles);
     L.ws_tile_off = take(4 * tiles);

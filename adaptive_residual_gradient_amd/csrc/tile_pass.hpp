@@ -235,7 +235,10 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
     }
 
     // ---- survivors to staging, bin boundaries, residue <- G ----
+    // Survivor r's key at st[r]; when the tile's region holds both, its G at
+    // st[total + r] as well, so that the finish can read it with the key.
     uint32_t* st = stage + tg.t0;
+    const bool pair = 2u * total <= tg.tlen;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const int vi = v * THREADS + tid;
@@ -250,6 +253,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<VPT>& in, uint32_t* 
                 if ((fb[v] >> c) & 1u) sbound[b] = r;
                 if (sel[v] & (1u << c)) {
                     st[r] = (g[v][c] < 0.0f ? 0x80000000u : 0u) | uint32_t(x);
+                    if (pair) st[total + r] = __float_as_uint(g[v][c]);
                     ++r;
                 }
             }

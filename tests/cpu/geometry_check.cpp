@@ -123,6 +123,21 @@ static std::string check(const std::vector<adacomp_segment>& segs, int expect_st
                 return "FAIL decode sum LDS";
         }
     }
+    // The decode launch order (runs of kXcdGroup positions per XCD) is a
+    // bijection of the launch positions, for this table's LDS decode tiles
+    // and for every n up to 300.
+    {
+        std::vector<uint64_t> ns = {L.dt.by_variant[0].size()};
+        for (uint64_t n = 1; n <= 300; ++n) ns.push_back(n);
+        for (uint64_t n : ns) {
+            std::vector<char> seen(n, 0);
+            for (uint64_t b = 0; b < n; ++b) {
+                const uint32_t p = xcd_grouped(uint32_t(b), uint32_t(n));
+                if (p >= n || seen[p]) return "FAIL xcd order n=" + std::to_string(n);
+                seen[p] = 1;
+            }
+        }
+    }
     return "OK tiles=" + std::to_string(L.ct.ntiles) + " dtiles=" + std::to_string(L.dt.ntiles);
 }
 
