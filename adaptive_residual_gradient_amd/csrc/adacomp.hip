@@ -48,7 +48,14 @@ struct adacomp_plan {
     // (K = 16, step-10 messages): 1.07e9 elements at L_T 500, 1.30 -> 1.15 ms; at L_T 50
     // (8-bit words, dense tiles) 2.12 -> 2.32 ms; 25e6 elements at L_T 500, 51.6 -> 57.6 us.
     bool sum_kernel = false;
+    // k_decode_count requests a decode tile's count blocks together on tables of at least
+    // kSumKernelMinTiles decode tiles where some tile's count words span more than
+    // kCountBatchMinBytes (dense short bins).  Measured on MI355X (K = 16, step-10 messages):
+    // 1.07e9 elements at L_T 50, decode 2.114 -> 2.055 ms; the conv-stack and ResNet-50 tables
+    // (fewer tiles) 36.3 -> 38.0 us and 107.3 -> 109.1 us, so they keep one block at a time.
+    bool count_batched = false;
 };
+constexpr uint32_t kCountBatchMinBytes = 48;
 constexpr uint64_t kSumKernelMinTiles = 65536;
 
 namespace adacomp {
@@ -380,6 +387,9 @@ int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t 
             if (sg.dt.variant == 0u && sg.wb != 2u) p->sum_kernel = false;
         if (plan_flags & ADACOMP_PLAN_DECODE_RECORDS) p->sum_kernel = true;
         if (L.dt.by_variant[0].empty()) p->sum_kernel = false;
+        for (const SegDev& sg : L.segs)
+            if (uint64_t(sg.dt.bpt) * sg.wb > kCountBatchMinBytes && L.dt.ntiles >= kSumKernelMinTiles)
+                p->count_batched = true;
         *out = p;
         return ADACOMP_OK;
     } catch (...) {
@@ -703,9 +713,14 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
                            adacomp::decode_tiles_group(K, ps0) == K;
     CallTimer tm(timer, stream, call_stage);
     {
-        hipLaunchKernelGGL(adacomp::k_decode_count, dim3(DC, K), dim3(256), 0, stream, mp,
-                           plan->d_segs, plan->ddt.chunk_tile_begin, plan->ddt.chunk_seg, DT, DC,
-                           geo, dw);
+        if (plan->count_batched)
+            hipLaunchKernelGGL(adacomp::k_decode_count<8>, dim3(DC, K), dim3(256), 0, stream, mp,
+                               plan->d_segs, plan->ddt.chunk_tile_begin, plan->ddt.chunk_seg, DT, DC,
+                               geo, dw);
+        else
+            hipLaunchKernelGGL(adacomp::k_decode_count<0>, dim3(DC, K), dim3(256), 0, stream, mp,
+                               plan->d_segs, plan->ddt.chunk_tile_begin, plan->ddt.chunk_seg, DT, DC,
+                               geo, dw);
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.mark(ADACOMP_STAGE_DECODE_COUNT);
     }

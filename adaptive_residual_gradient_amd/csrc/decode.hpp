@@ -87,11 +87,49 @@ __device__ __forceinline__ uint32_t sum_count_words(const uint8_t* m, uint64_t a
     return s;
 }
 
+// The same with the tile's blocks requested together when they are at most
+// NB (one memory round trip instead of one per block; the addresses are
+// clamped to the tile's last block, so every load stays inside the message).
+template <int NB>
+__device__ __forceinline__ uint32_t sum_count_words_batched(const uint8_t* m, uint64_t a0, uint64_t a1,
+                                                            uint32_t wb) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(1))) u32x4* gu4;
+    const uint64_t d0 = a0 & ~uint64_t(15);
+    const uint32_t nblk = uint32_t((a1 - d0 + 15u) >> 4);
+    if (nblk > uint32_t(NB)) return sum_count_words(m, a0, a1, wb);
+    u32x4 v[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) v[i] = *(gu4)(m + d0 + 16u * min(uint32_t(i), nblk - 1u));
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint64_t dj = d0 + 16u * uint32_t(i) + 4u * uint32_t(j);
+            uint32_t x = uint32_t(i) < nblk ? w4[j] : 0u;
+            if (dj + 4 <= a0 || dj >= a1) {
+                x = 0;   // no byte of [a0, a1)
+            } else {
+                if (dj < a0) x &= ~0u << (8u * uint32_t(a0 - dj));          // bytes before a0
+                if (dj + 4 > a1) x &= ~0u >> (8u * uint32_t(dj + 4 - a1));  // bytes from a1 on
+            }
+            s += wb == 1u ? (x & 0xFFu) + ((x >> 8) & 0xFFu) + ((x >> 16) & 0xFFu) + (x >> 24)
+                          : (x & 0xFFFFu) + (x >> 16);
+        }
+    }
+    return s;
+}
+
 // Per (chunk of decode tiles, message): survivors of each decode tile from
 // the count words, offsets within the chunk, chunk totals.  Thread t takes
 // tiles t, t + 256, t + 512, t + 768, so the lanes of a wavefront read
 // neighbouring tiles' count words together; one block scan per round of
-// 256 tiles gives the offsets in tile order.
+// 256 tiles gives the offsets in tile order.  NB > 0: a tile's count blocks
+// are requested together when they are at most NB (tables whose decode
+// tiles hold many count words: dense short bins); NB = 0: one at a time.
+template <int NB>
 __global__ void __launch_bounds__(256)
 k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
                const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ chunk_seg,
@@ -118,7 +156,8 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
             const uint32_t first_bin = (tb + t - sg.dt.tile_begin) * sg.dt.bpt;
             const uint32_t nb = min(sg.dt.bpt, sg.nbins - first_bin);
             const uint64_t a0 = sg.count_off + uint64_t(first_bin) * sg.wb;
-            s = sum_count_words(m, a0, a0 + uint64_t(nb) * sg.wb, sg.wb);
+            s = NB > 0 ? sum_count_words_batched<(NB > 0 ? NB : 1)>(m, a0, a0 + uint64_t(nb) * sg.wb, sg.wb)
+                       : sum_count_words(m, a0, a0 + uint64_t(nb) * sg.wb, sg.wb);
             // A tile never sends more elements than it holds.
             const uint64_t e0 = uint64_t(first_bin) * sg.lt;
             const uint64_t elems = min(uint64_t(nb) * sg.lt, sg.numel - e0);

@@ -77,6 +77,50 @@ def test_decode_parity(name, K, flags):
 
 
 @pytest.mark.parametrize("flags", FLAGS)
+def test_decode_dense_many_tiles(flags):
+    """One layer of 2^28 elements at L_T = 50: 66281 decode tiles of 81 bins
+    with 8-bit words, past the tile count from which the decode count reads a
+    tile's count blocks together; three learners' second-step messages, both
+    accumulate modes, compared in full with the oracle."""
+    n = 1 << 28
+    segs = [(0, n, 50)]
+    plan = A.Plan(segs, plan_flags=flags)
+    msg_ws = plan.compress_workspace(DEV)
+    d = torch.empty(n, dtype=torch.float32, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(50)
+    msgs = []
+    for k in range(3):
+        r = torch.zeros(n, dtype=torch.float32, device=DEV)
+        msg = plan.message_buffer(DEV)
+        for _ in range(2):
+            d.normal_(0.0, 1e-3, generator=gen)
+            A.compress(plan, r, d, msg, msg_ws)
+        total, surv, _ = A.message_header(plan, msg)
+        say(f"  learner {k}: {surv} survivors, {total} bytes")
+        msgs.append(msg[:total].clone())
+        del r, msg
+    del d, msg_ws
+    torch.cuda.empty_cache()
+    host_msgs = [host(m) for m in msgs]
+    ws = plan.decode_workspace(len(msgs), DEV)
+    for accumulate in (False, True):
+        start = np.full(n, 0.5, np.float32)
+        start[::7] = -0.0
+        out = torch.from_numpy(start).to(DEV)
+        say(f"  decode 2^28 elements at L_T 50, accumulate={accumulate}")
+        A.decode_accumulate(plan, msgs, out, accumulate, ws)
+        got = host(out)
+        del out
+        oracle.decode_accumulate(segs, host_msgs, start, accumulate)
+        np.testing.assert_array_equal(bits(got), bits(start))
+        assert int(host(ws[:4]).view(np.uint32)[0]) == 0
+        del got, start
+    plan.close()
+    del msgs, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("flags", FLAGS)
 @pytest.mark.parametrize("lt", [1, 3, 7, 50, 64, 500, 1021, 4093, 4094, 9000, 18432, 18433, 32768])
 def test_decode_edge_tables(lt, flags):
     """Every decode tile shape: LDS tiles (L_T <= 4093), long bins with at
