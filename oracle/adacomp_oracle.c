@@ -30,7 +30,7 @@
  *   s = (1/B) * sum_i g_max(i);  G_q = sign(G) * s for transmitted indices;
  *   residue <- G - G_q for transmitted indices, residue <- G otherwise.
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *   - fp32 arithmetic, round-to-nearest-even, no contraction: H is
  *     fl(fl(residue + dW) + dW), never residue + 2*dW rounded once.
  *   - bins are consecutive runs of L_T elements of the flattened (C-order)
