@@ -54,6 +54,9 @@ struct adacomp_plan {
     // 1.07e9 elements at L_T 50, decode 2.114 -> 2.055 ms; the conv-stack and ResNet-50 tables
     // (fewer tiles) 36.3 -> 38.0 us and 107.3 -> 109.1 us, so they keep one block at a time.
     bool count_batched = false;
+    // Some layer's decode tiles (LDS tiles) hold 8-bit entry words: k_decode_tiles then
+    // reserves its per-entry bin table.
+    bool dense_words = false;
 };
 constexpr uint32_t kCountBatchMinBytes = 48;
 constexpr uint64_t kSumKernelMinTiles = 65536;
@@ -387,9 +390,11 @@ int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t 
             if (sg.dt.variant == 0u && sg.wb != 2u) p->sum_kernel = false;
         if (plan_flags & ADACOMP_PLAN_DECODE_RECORDS) p->sum_kernel = true;
         if (L.dt.by_variant[0].empty()) p->sum_kernel = false;
-        for (const SegDev& sg : L.segs)
+        for (const SegDev& sg : L.segs) {
             if (uint64_t(sg.dt.bpt) * sg.wb > kCountBatchMinBytes && L.dt.ntiles >= kSumKernelMinTiles)
                 p->count_batched = true;
+            if (sg.dt.variant == 0u && sg.wb == 1u) p->dense_words = true;
+        }
         *out = p;
         return ADACOMP_OK;
     } catch (...) {
@@ -746,12 +751,18 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
                 const uint32_t acc_words = L.dt.max_span_vecs[0] * 4;
                 const uint32_t kg = adacomp::decode_tiles_group(K, ps);
                 const bool sep = kg < K || (accumulate != 0 && !fused);
-                const uint32_t lds = adacomp::decode_tiles_lds_bytes(acc_words, K, kg, ps, sep);
+                // The bin-start table: on tables of 8-bit words only; on smaller tables (fewer
+                // than kSumKernelMinTiles LDS decode tiles) with kTblBytes of its own, on larger
+                // ones in the place of the bin prefixes alone (no LDS beyond them).
+                const uint32_t tblw = !plan->dense_words ? 0u
+                                      : n < kSumKernelMinTiles ? std::max(adacomp::kTblBytes / 4u, kg * ps)
+                                                               : kg * ps;
+                const uint32_t lds = adacomp::decode_tiles_lds_bytes(acc_words, K, kg, ps, sep, tblw);
                 float* dst = fused ? nullptr : out;
                 const int acc = fused ? 0 : accumulate;
 #define ADACOMP_TILES(SEP, OPT)                                                                    \
     hipLaunchKernelGGL((adacomp::k_decode_tiles<SEP, OPT>), dim3(n), dim3(256), lds, stream, mp, K, \
-                       kg, ps, plan->ddesc[0], DT, DC, L.nseg, dw, dst, acc, acc_words, op)
+                       kg, ps, plan->ddesc[0], DT, DC, L.nseg, dw, dst, acc, acc_words, op, tblw)
                 if (plain_sum) {
                     hipLaunchKernelGGL(adacomp::k_decode_tiles_sum, dim3(n), dim3(256),
                                        adacomp::decode_sum_lds_bytes(acc_words, K, ps), stream, mp, K,

@@ -737,12 +737,125 @@ __device__ __forceinline__ void place_window4(const u32x4& v, int i0, uint32_t w
 }
 
 
+// The same two placements with the bins read from a table of bin starts: the
+// byte of a message's run position holds b + 1 where bin b's words begin, 0
+// elsewhere (the run's first position always holds a start).  An entry's bin
+// is the last start at or before it, so no entry waits on a search of the
+// count prefixes.
+//
+// The start at or before table byte P (P >= at, the run's first byte), as b + 1:
+// the aligned word holding P, then, rarely, the words before it.
+__device__ __forceinline__ uint32_t tbl_start_at(const uint32_t* tb32, uint32_t at, uint32_t P) {
+    int q = int(P >> 2);
+    uint32_t x = tb32[q] & ((P & 3u) == 3u ? ~0u : (1u << (8u * ((P & 3u) + 1u))) - 1u);
+    while (true) {
+        if (uint32_t(4 * q) < at) x &= ~0u << (8u * (at - uint32_t(4 * q)));   // bytes of an earlier run
+        if (x != 0u || uint32_t(4 * q) <= at) break;
+        --q;
+        x = tb32[q];
+    }
+    return (x >> (8u * ((31u - __builtin_clz(x | 1u)) >> 3))) & 0xFFu;
+}
+
+__device__ __forceinline__ void place_window_tbl(const u32x4& v, int i0, uint32_t wlo, uint32_t whi,
+                                                 uint32_t n, const uint32_t* tb32, uint32_t tblw, uint32_t at,
+                                                 uint32_t lt, uint32_t tlen, uint32_t lead, uint32_t wb,
+                                                 uint32_t hit, uint32_t* mask) {
+    const int first = max(i0 + int(wlo), 0);
+    const int last = min(i0 + int(whi), int(n));
+    if (first >= last) return;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    // The block's start bytes: table bytes at + i0 .. at + i0 + 16 / wb - 1, read as the
+    // aligned words covering them, the word indices clamped to the table (a clamped word
+    // only holds bytes of words that are not placed: before the run or past its end).
+    const int q0 = int(at) + i0;
+    const int wq = q0 >> 2;   // floor
+    const uint32_t rs = 8u * uint32_t(q0 & 3);
+    uint32_t run = tbl_start_at(tb32, at, at + uint32_t(first));
+    if (wb == 1u) {
+        uint32_t W[5];
+#pragma unroll
+        for (int t = 0; t < 5; ++t) W[t] = tb32[min(max(wq + t, 0), int(tblw) - 1)];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t st = uint32_t(((uint64_t(W[g + 1]) << 32) | W[g]) >> rs);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * g + e;
+                const uint32_t m = (st >> (8 * e)) & 0xFFu;
+                if (i0 + j > first && m != 0u) run = m;
+                const uint32_t word = (w[g] >> (8 * e)) & 0xFFu;
+                const uint32_t idx = word & 0x7Fu;
+                const uint32_t x = (run - 1u) * lt + idx;
+                if (i0 + j >= first && i0 + j < last && idx < lt && x < tlen)
+                    atomicOr(&mask[x + lead], (word >> 7) ? hit | (hit << 16) : hit);
+            }
+        }
+    } else {
+        uint32_t W[3];
+#pragma unroll
+        for (int t = 0; t < 3; ++t) W[t] = tb32[min(max(wq + t, 0), int(tblw) - 1)];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const uint32_t st = uint32_t(((uint64_t(W[g + 1]) << 32) | W[g]) >> rs);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * g + e;
+                const uint32_t m = (st >> (8 * e)) & 0xFFu;
+                if (i0 + j > first && m != 0u) run = m;
+                const uint32_t word = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+                const uint32_t idx = word & 0x7FFFu;
+                const uint32_t x = (run - 1u) * lt + idx;
+                if (i0 + j >= first && i0 + j < last && idx < lt && x < tlen)
+                    atomicOr(&mask[x + lead], (word >> 15) ? hit | (hit << 16) : hit);
+            }
+        }
+    }
+}
+
+// A window of at most 4 words, keeping each placed entry's LDS slot in xs.
+__device__ __forceinline__ void place_window4_tbl(const u32x4& v, int i0, uint32_t wlo, uint32_t whi,
+                                                  uint32_t n, const uint32_t* tb32, uint32_t at,
+                                                  uint32_t lt, uint32_t tlen, uint32_t lead, uint32_t wb,
+                                                  uint32_t hit, uint32_t* mask, uint32_t (&xs)[4]) {
+    const uint32_t wbits = 8u * wb, top = wbits - 1u;
+    const uint32_t wmask = (1u << wbits) - 1u, imask = (1u << top) - 1u;
+    const int first = max(i0 + int(wlo), 0);
+    const int last = min(i0 + int(whi), int(n));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xs[e] = kNoSlot;
+    if (first >= last) return;
+    uint64_t w0 = uint64_t(v.x) | (uint64_t(v.y) << 32), w1 = uint64_t(v.z) | (uint64_t(v.w) << 32);
+    const uint32_t sbits = uint32_t(first - i0) * wbits;   // 0 .. 120
+    if (sbits >= 64u) {
+        w0 = w1 >> (sbits - 64u);
+    } else if (sbits != 0u) {
+        w0 = (w0 >> sbits) | (w1 << (64u - sbits));
+    }
+    const uint8_t* tb = reinterpret_cast<const uint8_t*>(tb32) + at;
+    uint32_t st[4];
+#pragma unroll
+    for (int e = 1; e < 4; ++e) st[e] = tb[min(first + e, last - 1)];
+    uint32_t run = tbl_start_at(tb32, at, at + uint32_t(first));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (e > 0 && st[e] != 0u) run = st[e];
+        const uint32_t word = uint32_t(w0 >> (uint32_t(e) * wbits)) & wmask;
+        const uint32_t idx = word & imask;
+        const uint32_t x = (run - 1u) * lt + idx;
+        if (first + e < last && idx < lt && x < tlen) {
+            atomicOr(&mask[x + lead], (word >> top) ? hit | (hit << 16) : hit);
+            xs[e] = x + lead;
+        }
+    }
+}
+
 template <bool SEP, int OPT>
 __global__ void __launch_bounds__(256)
 k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                const DecDesc* __restrict__ descs, uint32_t DT, uint32_t DC, uint32_t nseg,
                DecodeWs ws, float* __restrict__ out, int accumulate, uint32_t acc_words,
-               OptParams op) {
+               OptParams op, uint32_t tblw) {
     constexpr int THREADS = 256, NW = THREADS / 64;
     constexpr uint32_t NS = kDecCap / 4 / THREADS;   // float4 slots per thread
     constexpr bool FUSED = OPT != kOptNone;
@@ -755,6 +868,9 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
     uint32_t* nent = reinterpret_cast<uint32_t*>(abase + KG);    // [KG]
     float* ks = reinterpret_cast<float*>(nent + KG);             // [KG]
     uint32_t* pref = reinterpret_cast<uint32_t*>(ks + KG);       // [KG][pstride]
+    // In the same place, when a group's table is used: the bin starts of the group's runs,
+    // run after run ([4 tblw] bytes, zero before the starts are written).
+    uint32_t* tbl32 = pref;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const DecDesc dd = descs[blockIdx.x];
@@ -800,6 +916,8 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
         }
         if (vi < accw / 4u) reinterpret_cast<u32x4*>(mask)[vi] = u32x4{0u, 0u, 0u, 0u};
     }
+    for (uint32_t q = uint32_t(tid); q < tblw / 4u; q += THREADS)
+        reinterpret_cast<u32x4*>(tbl32)[q] = u32x4{0u, 0u, 0u, 0u};
 
     f32x4 a4[SEP ? 1 : NS];   // without SEP: this thread's sums
     bool owned = false;       // entry-owned sums (sparse tiles, without SEP)
@@ -827,6 +945,15 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                 a_s = ws.dseg_s[uint64_t(k) * nseg + dd.si];
             }
         }
+        // Every wavefront: the length of each message's run for this tile (lane kk) and where
+        // it starts in the bin table.  The table is used for tiles of at most 128 bins whose
+        // runs fit it; then no bin prefix is stored.
+        uint32_t t_n = 0;
+        if (tblw != 0u && uint32_t(lane) < kn && mptr[k0 + uint32_t(lane)] != 0u)
+            t_n = ws.dcnt[uint64_t(k0 + uint32_t(lane)) * DT + dd.tile];
+        const uint32_t t_incl = wave_incl_add(t_n);
+        const uint32_t t_at = t_incl - t_n;   // lane kk: first table byte of message kk
+        const bool use_tbl = tblw != 0u && nb <= 128u && __builtin_amdgcn_readlane(t_incl, 63) <= 4u * tblw;
         // Count words into registers, one lane per bin, then per-message prefixes by DPP scans.
         // Every load is issued without a branch (unused lanes read `dummy`), so that all of a
         // wavefront's loads are in flight together.
@@ -843,11 +970,19 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                 if (b == 0u) pref[kk * pstride] = 0u;
             }
         };
+        // Table: the start of bin b of message kk (count c, inclusive prefix inc) in the zeroed
+        // table, at = the message's first table byte.
+        auto put_bins = [&](uint32_t b, uint32_t c, uint32_t inc, uint32_t at) {
+            if (c != 0u && at + inc - c < 4u * tblw) reinterpret_cast<uint8_t*>(tbl32)[at + inc - c] = uint8_t(b + 1u);
+        };
         if (nb <= 16u) {
             // one message per row of 16 lanes: wavefront wv, row q holds message 4 wv + q
             const uint32_t kk = 4u * uint32_t(wv) + (uint32_t(lane) >> 4), b = uint32_t(lane) & 15u;
             const uint32_t w = count_word(kk, b);
-            put_prefix(kk, b, row_incl_add(w));
+            const uint32_t inc = row_incl_add(w);
+            const uint32_t at = __shfl(t_at, int(min(kk, kMaskMsgs - 1u)));
+            if (use_tbl) put_bins(b, w, inc, at);
+            else put_prefix(kk, b, inc);
         } else if (nb <= 128u) {
             // wavefront wv: messages wv + 4 m (m < 4), bins lane and 64 + lane
             uint32_t cw[8];
@@ -859,8 +994,14 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                 const uint32_t kk = uint32_t(wv) + NW * uint32_t(m);
                 const uint32_t lo = wave_incl_add(cw[2 * m]);
                 const uint32_t hi = wave_incl_add(cw[2 * m + 1]) + __builtin_amdgcn_readlane(lo, 63);
-                put_prefix(kk, uint32_t(lane), lo);
-                put_prefix(kk, 64u + uint32_t(lane), hi);
+                if (use_tbl) {
+                    const uint32_t at = __builtin_amdgcn_readlane(t_at, int(min(kk, kMaskMsgs - 1u)));
+                    put_bins(uint32_t(lane), cw[2 * m], lo, at);
+                    put_bins(64u + uint32_t(lane), cw[2 * m + 1], hi, at);
+                } else {
+                    put_prefix(kk, uint32_t(lane), lo);
+                    put_prefix(kk, 64u + uint32_t(lane), hi);
+                }
             }
         } else {
             // long runs of short bins: per message, 8 rounds of 64 bins at a time
@@ -929,16 +1070,21 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                 const uint32_t nq = __shfl(ne, int(kk));
                 const int iq = int(int64_t(blk) - int64_t(a));
                 const uint32_t sq = (u & ((1u << sh) - 1u)) * wbytes;
+                const uint32_t at = __shfl(t_at, int(kk));
                 own_hit = 1u << kk;
                 if (uint32_t(tid) < NU) {
                     const uint32_t wsh = wb == 1u ? 0u : 1u;
-                    place_window4(v, iq >> wsh, sq >> wsh, (sq + wbytes) >> wsh, nq, pref + kk * pstride, nb,
-                                  lt, tlen, lead, wb, own_hit, mask, own_x);
+                    if (use_tbl)
+                        place_window4_tbl(v, iq >> wsh, sq >> wsh, (sq + wbytes) >> wsh, nq, tbl32, at, lt,
+                                          tlen, lead, wb, own_hit, mask, own_x);
+                    else
+                        place_window4(v, iq >> wsh, sq >> wsh, (sq + wbytes) >> wsh, nq, pref + kk * pstride, nb,
+                                      lt, tlen, lead, wb, own_hit, mask, own_x);
                 }
             }
             for (uint32_t u0 = owned ? NU : 0u; u0 < NU; u0 += THREADS * kBlkBatch) {   // workgroup-uniform
                 u32x4 v[kBlkBatch];
-                uint32_t kq[kBlkBatch], nq[kBlkBatch], sq[kBlkBatch];
+                uint32_t kq[kBlkBatch], nq[kBlkBatch], sq[kBlkBatch], aq[kBlkBatch];
                 int iq[kBlkBatch];
 #pragma unroll
                 for (int r = 0; r < kBlkBatch; ++r) {
@@ -968,6 +1114,7 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                     v[r] = *(global_u32x4_ptr)blk;
                     kq[r] = kk;
                     nq[r] = __shfl(ne, int(kk));
+                    aq[r] = __shfl(t_at, int(kk));
                     iq[r] = int(int64_t(blk) - int64_t(a));
                     sq[r] = (u & ((1u << sh) - 1u)) * wbytes;   // the window's first byte
                 }
@@ -977,12 +1124,19 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                     if (u0 + THREADS * uint32_t(r) + uint32_t(tid) >= NU) continue;
                     const uint32_t kk = kq[r];
                     const uint32_t wsh = wb == 1u ? 0u : 1u;
-                    place_window(v[r], iq[r] >> wsh, sq[r] >> wsh, (sq[r] + wbytes) >> wsh, nq[r],
-                                 pref + kk * pstride, nb, lt, tlen, lead, wb, 1u << kk, mask);
+                    if (use_tbl)
+                        place_window_tbl(v[r], iq[r] >> wsh, sq[r] >> wsh, (sq[r] + wbytes) >> wsh, nq[r],
+                                         tbl32, tblw, aq[r], lt, tlen, lead, wb, 1u << kk, mask);
+                    else
+                        place_window(v[r], iq[r] >> wsh, sq[r] >> wsh, (sq[r] + wbytes) >> wsh, nq[r],
+                                     pref + kk * pstride, nb, lt, tlen, lead, wb, 1u << kk, mask);
                 }
             }
         }
         __syncthreads();   // every bit of the group is set
+        if (SEP && tblw != 0u)   // the next group's table starts from zero (nothing reads it past the barrier)
+            for (uint32_t q = uint32_t(tid); q < tblw / 4u; q += THREADS)
+                reinterpret_cast<u32x4*>(tbl32)[q] = u32x4{0u, 0u, 0u, 0u};
 
         // ---- sums: each thread its own elements, hits in message order ----
         if (!SEP && owned) {

@@ -204,10 +204,15 @@ ADACOMP_HD constexpr uint32_t xcd_grouped(uint32_t b, uint32_t n) {
 // Dynamic LDS bytes of k_decode_tiles: acc_words mask words (and as many sum
 // words with SEP), per message its address, per group message its first
 // entry's address, entry count and s, and the group's bin prefixes.
+// k_decode_tiles can keep, for a group whose runs hold at most 4 tblw entry
+// words, the start of each bin (one byte, tiles of at most 128 bins) in the
+// place of the bin prefixes (tblw words, at least the prefixes' own).
+constexpr uint32_t kTblBytes = 10240;
 inline uint32_t decode_tiles_lds_bytes(uint32_t acc_words, uint32_t K, uint32_t KG,
-                                       uint32_t pstride, bool sep) {
+                                       uint32_t pstride, bool sep, uint32_t tblw) {
     const uint32_t accw = (acc_words + 3u) & ~3u;
-    return 4u * (accw * (sep ? 2u : 1u) + 2u * K + 2u * KG + 2u * KG + KG * pstride);
+    const uint32_t pw = KG * pstride > tblw ? KG * pstride : tblw;
+    return 4u * (accw * (sep ? 2u : 1u) + 2u * K + 2u * KG + 2u * KG + pw);
 }
 
 // Dynamic LDS bytes of k_decode_tiles_sum (K <= kMaskMsgs messages): the mask
