@@ -751,18 +751,21 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
                 const uint32_t acc_words = L.dt.max_span_vecs[0] * 4;
                 const uint32_t kg = adacomp::decode_tiles_group(K, ps);
                 const bool sep = kg < K || (accumulate != 0 && !fused);
-                // The bin-start table: on tables of 8-bit words only; on smaller tables (fewer
+                // The bin-start table: plain decodes of tables of 8-bit words only; on smaller tables (fewer
                 // than kSumKernelMinTiles LDS decode tiles) with kTblBytes of its own, on larger
                 // ones in the place of the bin prefixes alone (no LDS beyond them).
-                const uint32_t tblw = !plan->dense_words ? 0u
+                const uint32_t tblw = !plan->dense_words || opt != adacomp::kOptNone ? 0u
                                       : n < kSumKernelMinTiles ? std::max(adacomp::kTblBytes / 4u, kg * ps)
                                                                : kg * ps;
                 const uint32_t lds = adacomp::decode_tiles_lds_bytes(acc_words, K, kg, ps, sep, tblw);
                 float* dst = fused ? nullptr : out;
                 const int acc = fused ? 0 : accumulate;
 #define ADACOMP_TILES(SEP, OPT)                                                                    \
-    hipLaunchKernelGGL((adacomp::k_decode_tiles<SEP, OPT>), dim3(n), dim3(256), lds, stream, mp, K, \
-                       kg, ps, plan->ddesc[0], DT, DC, L.nseg, dw, dst, acc, acc_words, op, tblw)
+    hipLaunchKernelGGL((adacomp::k_decode_tiles<SEP, OPT, false>), dim3(n), dim3(256), lds, stream, mp, \
+                       K, kg, ps, plan->ddesc[0], DT, DC, L.nseg, dw, dst, acc, acc_words, op, 0u)
+#define ADACOMP_TILES_TBL(SEP)                                                                     \
+    hipLaunchKernelGGL((adacomp::k_decode_tiles<SEP, adacomp::kOptNone, true>), dim3(n), dim3(256), lds, \
+                       stream, mp, K, kg, ps, plan->ddesc[0], DT, DC, L.nseg, dw, dst, acc, acc_words, op, tblw)
                 if (plain_sum) {
                     hipLaunchKernelGGL(adacomp::k_decode_tiles_sum, dim3(n), dim3(256),
                                        adacomp::decode_sum_lds_bytes(acc_words, K, ps), stream, mp, K,
@@ -773,11 +776,15 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
                 } else if (opt == adacomp::kOptAdam) {
                     if (sep) ADACOMP_TILES(true, adacomp::kOptAdam);
                     else ADACOMP_TILES(false, adacomp::kOptAdam);
+                } else if (tblw != 0u) {
+                    if (sep) ADACOMP_TILES_TBL(true);
+                    else ADACOMP_TILES_TBL(false);
                 } else {
                     if (sep) ADACOMP_TILES(true, adacomp::kOptNone);
                     else ADACOMP_TILES(false, adacomp::kOptNone);
                 }
 #undef ADACOMP_TILES
+#undef ADACOMP_TILES_TBL
             } else if (long_decode_in_lds(L, K, KG, ps, opt)) {
                 // long bins, the whole tile accumulated in LDS (one 1024-thread workgroup per
                 // CU) and written once, or stepped by the optimizer

@@ -146,6 +146,7 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
     const bool ok = header_matches(m, geo);
     const SegDev sg = segs[chunk_seg[c]];
     const uint32_t tb = chunk_tile_begin[c], n = chunk_tile_begin[c + 1] - tb;
+    __syncthreads();   // bad is cleared before any thread sets it
     uint32_t cnt[4];
     bool over = false;
 #pragma unroll
@@ -172,6 +173,7 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
     uint32_t base = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        if (uint32_t(i) * 256u >= n) break;   // workgroup-uniform: no tile left in the chunk
         const uint32_t t = uint32_t(i) * 256u + threadIdx.x;
         uint32_t total;
         const uint32_t ex = block_exclusive_scan<256>(cnt[i], lw, &total);
@@ -850,7 +852,7 @@ __device__ __forceinline__ void place_window4_tbl(const u32x4& v, int i0, uint32
     }
 }
 
-template <bool SEP, int OPT>
+template <bool SEP, int OPT, bool TBL>
 __global__ void __launch_bounds__(256)
 k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                const DecDesc* __restrict__ descs, uint32_t DT, uint32_t DC, uint32_t nseg,
@@ -916,8 +918,9 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
         }
         if (vi < accw / 4u) reinterpret_cast<u32x4*>(mask)[vi] = u32x4{0u, 0u, 0u, 0u};
     }
-    for (uint32_t q = uint32_t(tid); q < tblw / 4u; q += THREADS)
-        reinterpret_cast<u32x4*>(tbl32)[q] = u32x4{0u, 0u, 0u, 0u};
+    if (TBL)
+        for (uint32_t q = uint32_t(tid); q < tblw / 4u; q += THREADS)
+            reinterpret_cast<u32x4*>(tbl32)[q] = u32x4{0u, 0u, 0u, 0u};
 
     f32x4 a4[SEP ? 1 : NS];   // without SEP: this thread's sums
     bool owned = false;       // entry-owned sums (sparse tiles, without SEP)
@@ -948,12 +951,16 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
         // Every wavefront: the length of each message's run for this tile (lane kk) and where
         // it starts in the bin table.  The table is used for tiles of at most 128 bins whose
         // runs fit it; then no bin prefix is stored.
-        uint32_t t_n = 0;
-        if (tblw != 0u && uint32_t(lane) < kn && mptr[k0 + uint32_t(lane)] != 0u)
-            t_n = ws.dcnt[uint64_t(k0 + uint32_t(lane)) * DT + dd.tile];
-        const uint32_t t_incl = wave_incl_add(t_n);
-        const uint32_t t_at = t_incl - t_n;   // lane kk: first table byte of message kk
-        const bool use_tbl = tblw != 0u && nb <= 128u && __builtin_amdgcn_readlane(t_incl, 63) <= 4u * tblw;
+        uint32_t t_at = 0;   // lane kk: first table byte of message kk
+        bool use_tbl = false;
+        if (TBL && tblw != 0u && nb <= 128u) {   // uniform
+            uint32_t t_n = 0;
+            if (uint32_t(lane) < kn && mptr[k0 + uint32_t(lane)] != 0u)
+                t_n = ws.dcnt[uint64_t(k0 + uint32_t(lane)) * DT + dd.tile];
+            const uint32_t t_incl = wave_incl_add(t_n);
+            t_at = t_incl - t_n;
+            use_tbl = __builtin_amdgcn_readlane(t_incl, 63) <= 4u * tblw;
+        }
         // Count words into registers, one lane per bin, then per-message prefixes by DPP scans.
         // Every load is issued without a branch (unused lanes read `dummy`), so that all of a
         // wavefront's loads are in flight together.
@@ -980,8 +987,7 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
             const uint32_t kk = 4u * uint32_t(wv) + (uint32_t(lane) >> 4), b = uint32_t(lane) & 15u;
             const uint32_t w = count_word(kk, b);
             const uint32_t inc = row_incl_add(w);
-            const uint32_t at = __shfl(t_at, int(min(kk, kMaskMsgs - 1u)));
-            if (use_tbl) put_bins(b, w, inc, at);
+            if (TBL && use_tbl) put_bins(b, w, inc, __shfl(t_at, int(min(kk, kMaskMsgs - 1u))));   // uniform branch
             else put_prefix(kk, b, inc);
         } else if (nb <= 128u) {
             // wavefront wv: messages wv + 4 m (m < 4), bins lane and 64 + lane
@@ -994,7 +1000,7 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                 const uint32_t kk = uint32_t(wv) + NW * uint32_t(m);
                 const uint32_t lo = wave_incl_add(cw[2 * m]);
                 const uint32_t hi = wave_incl_add(cw[2 * m + 1]) + __builtin_amdgcn_readlane(lo, 63);
-                if (use_tbl) {
+                if (TBL && use_tbl) {
                     const uint32_t at = __builtin_amdgcn_readlane(t_at, int(min(kk, kMaskMsgs - 1u)));
                     put_bins(uint32_t(lane), cw[2 * m], lo, at);
                     put_bins(64u + uint32_t(lane), cw[2 * m + 1], hi, at);
@@ -1070,11 +1076,11 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                 const uint32_t nq = __shfl(ne, int(kk));
                 const int iq = int(int64_t(blk) - int64_t(a));
                 const uint32_t sq = (u & ((1u << sh) - 1u)) * wbytes;
-                const uint32_t at = __shfl(t_at, int(kk));
+                const uint32_t at = TBL && use_tbl ? __shfl(t_at, int(kk)) : 0u;
                 own_hit = 1u << kk;
                 if (uint32_t(tid) < NU) {
                     const uint32_t wsh = wb == 1u ? 0u : 1u;
-                    if (use_tbl)
+                    if (TBL && use_tbl)
                         place_window4_tbl(v, iq >> wsh, sq >> wsh, (sq + wbytes) >> wsh, nq, tbl32, at, lt,
                                           tlen, lead, wb, own_hit, mask, own_x);
                     else
@@ -1082,59 +1088,67 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
                                       lt, tlen, lead, wb, own_hit, mask, own_x);
                 }
             }
-            for (uint32_t u0 = owned ? NU : 0u; u0 < NU; u0 += THREADS * kBlkBatch) {   // workgroup-uniform
-                u32x4 v[kBlkBatch];
-                uint32_t kq[kBlkBatch], nq[kBlkBatch], sq[kBlkBatch], aq[kBlkBatch];
-                int iq[kBlkBatch];
+            // The blocks left (all of them unless owned), kBlkBatch per thread requested
+            // together; TB: bins from the bin-start table (a separate copy of the loop, so
+            // that the prefix-search path keeps its own registers).
+            auto blocks = [&](auto tb_tag) {
+                constexpr bool TB = decltype(tb_tag)::value;
+                for (uint32_t u0 = owned ? NU : 0u; u0 < NU; u0 += THREADS * kBlkBatch) {   // workgroup-uniform
+                    u32x4 v[kBlkBatch];
+                    uint32_t kq[kBlkBatch], nq[kBlkBatch], sq[kBlkBatch], aq[kBlkBatch];
+                    int iq[kBlkBatch];
 #pragma unroll
-                for (int r = 0; r < kBlkBatch; ++r) {
-                    if (u0 + THREADS * uint32_t(r) >= NU) break;   // workgroup-uniform
-                    const uint32_t u = min(u0 + THREADS * uint32_t(r) + uint32_t(tid), NU - 1u);
-                    const uint32_t q = u >> sh;
-                    // The last message whose first block is at or before q (empty messages
-                    // share their successor's start, so the one found holds block q): fixed
-                    // steps 8, 4, 2, 1 with every lane active.  A lane shuffle reads 0 from
-                    // an inactive lane, so it must not sit in a loop whose trip count differs
-                    // between lanes.
-                    uint32_t kk = 0;
+                    for (int r = 0; r < kBlkBatch; ++r) {
+                        if (u0 + THREADS * uint32_t(r) >= NU) break;   // workgroup-uniform
+                        const uint32_t u = min(u0 + THREADS * uint32_t(r) + uint32_t(tid), NU - 1u);
+                        const uint32_t q = u >> sh;
+                        // The last message whose first block is at or before q (empty messages
+                        // share their successor's start, so the one found holds block q): fixed
+                        // steps 8, 4, 2, 1 with every lane active.  A lane shuffle reads 0 from
+                        // an inactive lane, so it must not sit in a loop whose trip count differs
+                        // between lanes.
+                        uint32_t kk = 0;
 #pragma unroll
-                    for (uint32_t step = kMaskMsgs / 2u; step >= 1u; step >>= 1) {
-                        const uint32_t c = kk + step;
-                        const uint32_t bc = __shfl(bs, int(min(c, kMaskMsgs - 1u)));
-                        if (c < kn && bc <= q) kk = c;
+                        for (uint32_t step = kMaskMsgs / 2u; step >= 1u; step >>= 1) {
+                            const uint32_t c = kk + step;
+                            const uint32_t bc = __shfl(bs, int(min(c, kMaskMsgs - 1u)));
+                            if (c < kn && bc <= q) kk = c;
+                        }
+                        const uint64_t a = (uint64_t(__shfl(uint32_t(ab >> 32), int(kk))) << 32) |
+                                           __shfl(uint32_t(ab), int(kk));
+                        // kept inside message kk's blocks whatever q (a message without blocks is
+                        // never found; if it were, the always readable dummy word is read instead)
+                        const uint32_t nbk = __shfl(nblk, int(kk));
+                        const uint32_t rel = min(q - __shfl(bs, int(kk)), nbk - 1u);
+                        const uint64_t blk = nbk != 0u ? (a & ~uint64_t(15)) + 16u * uint64_t(rel)
+                                                       : dummy & ~uint64_t(15);
+                        v[r] = *(global_u32x4_ptr)blk;
+                        kq[r] = kk;
+                        nq[r] = __shfl(ne, int(kk));
+                        if (TB) aq[r] = __shfl(t_at, int(kk));
+                        iq[r] = int(int64_t(blk) - int64_t(a));
+                        sq[r] = (u & ((1u << sh) - 1u)) * wbytes;   // the window's first byte
                     }
-                    const uint64_t a = (uint64_t(__shfl(uint32_t(ab >> 32), int(kk))) << 32) |
-                                       __shfl(uint32_t(ab), int(kk));
-                    // kept inside message kk's blocks whatever q (a message without blocks is
-                    // never found; if it were, the always readable dummy word is read instead)
-                    const uint32_t nbk = __shfl(nblk, int(kk));
-                    const uint32_t rel = min(q - __shfl(bs, int(kk)), nbk - 1u);
-                    const uint64_t blk = nbk != 0u ? (a & ~uint64_t(15)) + 16u * uint64_t(rel)
-                                                   : dummy & ~uint64_t(15);
-                    v[r] = *(global_u32x4_ptr)blk;
-                    kq[r] = kk;
-                    nq[r] = __shfl(ne, int(kk));
-                    aq[r] = __shfl(t_at, int(kk));
-                    iq[r] = int(int64_t(blk) - int64_t(a));
-                    sq[r] = (u & ((1u << sh) - 1u)) * wbytes;   // the window's first byte
-                }
 #pragma unroll
-                for (int r = 0; r < kBlkBatch; ++r) {
-                    if (u0 + THREADS * uint32_t(r) >= NU) break;   // workgroup-uniform
-                    if (u0 + THREADS * uint32_t(r) + uint32_t(tid) >= NU) continue;
-                    const uint32_t kk = kq[r];
-                    const uint32_t wsh = wb == 1u ? 0u : 1u;
-                    if (use_tbl)
-                        place_window_tbl(v[r], iq[r] >> wsh, sq[r] >> wsh, (sq[r] + wbytes) >> wsh, nq[r],
-                                         tbl32, tblw, aq[r], lt, tlen, lead, wb, 1u << kk, mask);
-                    else
-                        place_window(v[r], iq[r] >> wsh, sq[r] >> wsh, (sq[r] + wbytes) >> wsh, nq[r],
-                                     pref + kk * pstride, nb, lt, tlen, lead, wb, 1u << kk, mask);
+                    for (int r = 0; r < kBlkBatch; ++r) {
+                        if (u0 + THREADS * uint32_t(r) >= NU) break;   // workgroup-uniform
+                        if (u0 + THREADS * uint32_t(r) + uint32_t(tid) >= NU) continue;
+                        const uint32_t kk = kq[r];
+                        const uint32_t wsh = wb == 1u ? 0u : 1u;
+                        if (TB)
+                            place_window_tbl(v[r], iq[r] >> wsh, sq[r] >> wsh, (sq[r] + wbytes) >> wsh, nq[r],
+                                             tbl32, tblw, aq[r], lt, tlen, lead, wb, 1u << kk, mask);
+                        else
+                            place_window(v[r], iq[r] >> wsh, sq[r] >> wsh, (sq[r] + wbytes) >> wsh, nq[r],
+                                         pref + kk * pstride, nb, lt, tlen, lead, wb, 1u << kk, mask);
+                    }
                 }
-            }
+            };
+            if (TBL && use_tbl) blocks(std::integral_constant<bool, TBL>{});
+            else blocks(std::false_type{});
         }
         __syncthreads();   // every bit of the group is set
-        if (SEP && tblw != 0u)   // the next group's table starts from zero (nothing reads it past the barrier)
+        if (TBL && SEP && tblw != 0u)   // the next group's table starts from zero (nothing reads it past the barrier)
             for (uint32_t q = uint32_t(tid); q < tblw / 4u; q += THREADS)
                 reinterpret_cast<u32x4*>(tbl32)[q] = u32x4{0u, 0u, 0u, 0u};
 

@@ -18,12 +18,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* l
                                                          uint32_t* total) {
     constexpr int NW = THREADS / 64;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    uint32_t inc = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t t = __shfl_up(inc, d);
-        if (lane >= d) inc += t;
-    }
+    const uint32_t inc = wave_incl_add(v);
     if (lane == 63) lds_w[wv] = inc;
     __syncthreads();
     uint32_t before = 0, all = 0;

@@ -115,7 +115,8 @@ static std::string check(const std::vector<adacomp_segment>& segs, int expect_st
             return "FAIL decode LDS";
         if (v == 0) {
             const uint32_t tg = decode_tiles_group(ADACOMP_MAX_MESSAGES, ps);
-            if (decode_tiles_lds_bytes(acc, ADACOMP_MAX_MESSAGES, tg, ps, true) > 65536)
+            // with the largest bin-start table a plain decode reserves
+            if (decode_tiles_lds_bytes(acc, ADACOMP_MAX_MESSAGES, tg, ps, true, kTblBytes / 4) > 65536)
                 return "FAIL decode tiles LDS";
             // the plain sum of up to kMaskMsgs messages, where they fit one group
             if (decode_tiles_group(kMaskMsgs, ps) == kMaskMsgs &&
