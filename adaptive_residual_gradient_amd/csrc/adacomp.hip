@@ -755,8 +755,9 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
                 // than kSumKernelMinTiles LDS decode tiles) with kTblBytes of its own, on larger
                 // ones in the place of the bin prefixes alone (no LDS beyond them).
                 const uint32_t tblw = !plan->dense_words || opt != adacomp::kOptNone ? 0u
-                                      : n < kSumKernelMinTiles ? std::max(adacomp::kTblBytes / 4u, kg * ps)
-                                                               : kg * ps;
+                                      : n < kSumKernelMinTiles
+                                          ? std::max(adacomp::kTblBytes / 4u, adacomp::decode_tiles_pref_words(kg, ps))
+                                          : adacomp::decode_tiles_pref_words(kg, ps);
                 const uint32_t lds = adacomp::decode_tiles_lds_bytes(acc_words, K, kg, ps, sep, tblw);
                 float* dst = fused ? nullptr : out;
                 const int acc = fused ? 0 : accumulate;

@@ -869,10 +869,11 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
     uint64_t* abase = mptr + K;                                  // [KG]
     uint32_t* nent = reinterpret_cast<uint32_t*>(abase + KG);    // [KG]
     float* ks = reinterpret_cast<float*>(nent + KG);             // [KG]
-    uint32_t* pref = reinterpret_cast<uint32_t*>(ks + KG);       // [KG][pstride]
+    // [KG][pstride], 16 bits each (a prefix counts at most a tile's 4096 elements)
+    uint16_t* pref = reinterpret_cast<uint16_t*>(ks + KG);
     // In the same place, when a group's table is used: the bin starts of the group's runs,
     // run after run ([4 tblw] bytes, zero before the starts are written).
-    uint32_t* tbl32 = pref;
+    uint32_t* tbl32 = reinterpret_cast<uint32_t*>(pref);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const DecDesc dd = descs[blockIdx.x];
@@ -973,7 +974,7 @@ k_decode_tiles(MsgPtrs msgs, uint32_t K, uint32_t KG, uint32_t pstride,
         };
         auto put_prefix = [&](uint32_t kk, uint32_t b, uint32_t inc) {
             if (kk < kn && b < nb) {
-                pref[kk * pstride + b + 1u] = inc;
+                pref[kk * pstride + b + 1u] = uint16_t(inc);
                 if (b == 0u) pref[kk * pstride] = 0u;
             }
         };

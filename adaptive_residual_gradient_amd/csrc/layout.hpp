@@ -208,10 +208,12 @@ ADACOMP_HD constexpr uint32_t xcd_grouped(uint32_t b, uint32_t n) {
 // words, the start of each bin (one byte, tiles of at most 128 bins) in the
 // place of the bin prefixes (tblw words, at least the prefixes' own).
 constexpr uint32_t kTblBytes = 10240;
+// LDS words of k_decode_tiles' bin prefixes (16 bits each).
+inline uint32_t decode_tiles_pref_words(uint32_t KG, uint32_t pstride) { return (KG * pstride + 1u) / 2u; }
 inline uint32_t decode_tiles_lds_bytes(uint32_t acc_words, uint32_t K, uint32_t KG,
                                        uint32_t pstride, bool sep, uint32_t tblw) {
     const uint32_t accw = (acc_words + 3u) & ~3u;
-    const uint32_t pw = KG * pstride > tblw ? KG * pstride : tblw;
+    const uint32_t pw = decode_tiles_pref_words(KG, pstride) > tblw ? decode_tiles_pref_words(KG, pstride) : tblw;
     return 4u * (accw * (sep ? 2u : 1u) + 2u * K + 2u * KG + 2u * KG + pw);
 }
 
