@@ -124,7 +124,8 @@ __device__ __forceinline__ uint32_t sum_count_words_batched(const uint8_t* m, ui
 
 // Per (chunk of decode tiles, message): survivors of each decode tile from
 // the count words, offsets within the chunk, chunk totals.  Thread t takes
-// tiles t, t + 256, t + 512, t + 768, so the lanes of a wavefront read
+// tiles t, t + 256, t + 512, t + 768 (decode chunks hold at most
+// kDecChunkTiles = 256 tiles: one round), so the lanes of a wavefront read
 // neighbouring tiles' count words together; one block scan per round of
 // 256 tiles gives the offsets in tile order.  NB > 0: a tile's count blocks
 // are requested together when they are at most NB (tables whose decode
@@ -226,14 +227,14 @@ k_decode_base(MsgPtrs msgs, uint32_t K, const SegDev* __restrict__ segs, MsgGeom
         ws.dseg_eoff[i] = eoff;
         const uint64_t c0 = uint64_t(k) * DC + sg.dt.chunk_begin;
         uint64_t run = 0;
-        // Chunk totals eight at a time, all requested before any is used.
-        for (uint32_t c = 0; c < sg.dt.nchunks; c += 8) {
-            uint32_t v[8];
+        // Chunk totals sixteen at a time, all requested before any is used.
+        for (uint32_t c = 0; c < sg.dt.nchunks; c += 16) {
+            uint32_t v[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < 16; ++u)
                 v[u] = c + u < sg.dt.nchunks ? ws.dchunk_cnt[c0 + c + u] : 0u;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 16; ++u) {
                 if (c + u < sg.dt.nchunks) ws.dchunk_base[c0 + c + u] = uint32_t(run);
                 bad |= (v[u] & kChunkBad) != 0u;
                 run += v[u] & ~kChunkBad;

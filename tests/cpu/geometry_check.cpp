@@ -62,9 +62,9 @@ static std::string check_tiling(const Layout& L, const Tiling& T, bool decode, c
         for (uint32_t c = ts.chunk_begin; c < ts.chunk_begin + ts.nchunks; ++c) {
             if (T.chunk_seg[c] != s) return "FAIL chunk_seg";
             const uint32_t a = T.chunk_tile_begin[c], b = T.chunk_tile_begin[c + 1];
-            if (b <= a || b - a > kChunkTiles) return "FAIL chunk size";
+            if (b <= a || b - a > T.chunk_tiles || T.chunk_tiles > kChunkTiles) return "FAIL chunk size";
             if (a < ts.tile_begin || b > ts.tile_begin + ts.ntiles) return "FAIL chunk crosses segment";
-            if ((a - ts.tile_begin) / kChunkTiles != c - ts.chunk_begin) return "FAIL chunk index";
+            if ((a - ts.tile_begin) / T.chunk_tiles != c - ts.chunk_begin) return "FAIL chunk index";
         }
     }
     if (seen != T.ntiles || T.chunk_tile_begin.back() != T.ntiles) return "FAIL tile count";
