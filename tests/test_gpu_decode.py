@@ -158,6 +158,46 @@ def test_decode_edge_tables(lt, flags):
     plan.close()
 
 
+@pytest.mark.parametrize("K,dense", [(2, True), (3, True), (16, False), (5, "mixed")])
+def test_decode_bin_table_limits(K, dense):
+    """Plain decodes of a small table of 8-bit words (L_T 50), where entry
+    bins come from the LDS bin-start table when a tile's runs fit it: every
+    element sent by every message (all values of a bin equal in magnitude),
+    with K = 2 (runs of 8100 words per tile: inside the table) and K = 3
+    (12150: past it, so the tiles take the prefix search); sparse messages;
+    and a mix of both, in both accumulate modes."""
+    segs = [(0, 1000050, 50), (1000052, 123457, 50)]
+    span = 1000052 + 123460
+    plan = A.Plan(segs)
+    rng = np.random.default_rng(1000 + K)
+    cws = plan.compress_workspace(DEV)
+    msgs, host_msgs = [], []
+    for k in range(K):
+        full = dense is True or (dense == "mixed" and k % 2 == 0)
+        if full:   # r = 0, |dW| equal: |H| = 2|dW| >= g_max = |dW| everywhere
+            d = (np.where(rng.random(span) < 0.5, -1.0, 1.0) * 1e-3).astype(np.float32)
+        else:
+            d = (rng.standard_normal(span) * 1e-3).astype(np.float32)
+        r = torch.zeros(span, dtype=torch.float32, device=DEV)
+        m = plan.message_buffer(DEV)
+        A.compress(plan, r, torch.from_numpy(d).to(DEV), m, cws)
+        total, surv, _ = A.message_header(plan, m)
+        if full:
+            assert surv == 1000050 + 123457
+        msgs.append(m)
+        host_msgs.append(host(m[:total]))
+    ws = plan.decode_workspace(K, DEV)
+    for accumulate in (False, True):
+        start = rng.standard_normal(span).astype(np.float32)
+        out = torch.from_numpy(start.copy()).to(DEV)
+        say(f"  decode K={K} dense={dense} accumulate={accumulate}")
+        A.decode_accumulate(plan, msgs, out, accumulate, ws)
+        want = start.copy()
+        oracle.decode_accumulate(segs, host_msgs, want, accumulate)
+        np.testing.assert_array_equal(bits(host(out)), bits(want))
+    plan.close()
+
+
 @pytest.mark.parametrize("flags", FLAGS)
 def test_decode_skips_foreign_messages(flags):
     """A message made for another segment table contributes nothing and is
