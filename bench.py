@@ -202,7 +202,8 @@ def measure_decode_sgd(A, plan, msgs, n_alloc, N, K, dev):
 def measure_small_table(A, W, dev):
     """The 100 x 1000 layer (L_T 500), launch-latency bound: one compress call
     per step over its 10 seeded gradients, timed per call with events
-    (median of 100 calls) and back to back (mean of 500), for each finish:
+    (median of 100 calls), back to back (mean of 500) and replayed from a HIP
+    graph of the 10 calls (mean of 20 replays), for each finish:
     the default small-table finish (tile pass + one finish kernel), the
     three-kernel finish and the single launch."""
     import time
@@ -233,8 +234,29 @@ def measure_small_table(A, W, dev):
             A.compress(plan, r, dws[i % len(dws)], msg, ws)
         torch.cuda.synchronize()
         b2b = (time.perf_counter() - t0) * 1e6 / 500
+        # The 10 steps captured once in a HIP graph and replayed 20 times (no host
+        # launch per kernel): events around the replays, per call.
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for d in dws:
+                    A.compress(plan, r, d, msg, ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(20):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        graph_us = a.elapsed_time(b) * 1e3 / (20 * len(dws))
+        del g
         out[label] = {"launches": int(plan.info.compress_launches), "call_us": round(per[50], 2),
-                      "back_to_back_us": round(b2b, 2)}
+                      "back_to_back_us": round(b2b, 2), "graph_replay_us": round(graph_us, 2)}
         plan.close()
     return out
 
