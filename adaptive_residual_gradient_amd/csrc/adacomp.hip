@@ -34,6 +34,7 @@ struct adacomp_plan {
     int device = -1;
     void* dmem = nullptr;
     SegDev* d_segs = nullptr;
+    adacomp::CountChunk* d_cchunks = nullptr;   // decode count chunks
     DevTiling dct, ddt;                                        // compress and decode tiles
     adacomp::DecDesc* ddesc[adacomp::kDecVariants] = {nullptr, nullptr};   // decode tiles in launch order
     uint32_t tile_lds_words[adacomp::kVariants] = {0, 0, 0};  // one tile's LDS words
@@ -333,6 +334,24 @@ int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t 
         };
         const uint64_t o_segs = put(L.segs.data(), sizeof(SegDev) * L.nseg);
         const TilingOffsets oc = put_tiling(L.ct), od = put_tiling(L.dt);
+        uint64_t o_cchunks = 0;
+        {
+            std::vector<adacomp::CountChunk> cc(L.dt.nchunks);
+            for (uint64_t c = 0; c < L.dt.nchunks; ++c) {
+                const SegDev& sg = L.segs[L.dt.chunk_seg[c]];
+                adacomp::CountChunk& x = cc[c];
+                x.count_off = sg.count_off;
+                x.numel = sg.numel;
+                x.tile0 = L.dt.chunk_tile_begin[c];
+                x.ntiles = L.dt.chunk_tile_begin[c + 1] - x.tile0;
+                x.first_bin = (x.tile0 - sg.dt.tile_begin) * sg.dt.bpt;
+                x.bpt = sg.dt.bpt;
+                x.nbins = sg.nbins;
+                x.wb = sg.wb;
+                x.lt = sg.lt;
+            }
+            o_cchunks = put(cc.data(), sizeof(adacomp::CountChunk) * cc.size());
+        }
         uint64_t o_desc[adacomp::kDecVariants];
         for (int v = 0; v < adacomp::kDecVariants; ++v) {
             const std::vector<adacomp::DecDesc> d = adacomp::decode_descs(L, v);
@@ -360,6 +379,7 @@ int adacomp_plan_create_ex(const adacomp_segment* segs, uint32_t nseg, uint32_t 
         }
         uint8_t* base = static_cast<uint8_t*>(p->dmem);
         p->d_segs = reinterpret_cast<SegDev*>(base + o_segs);
+        p->d_cchunks = reinterpret_cast<adacomp::CountChunk*>(base + o_cchunks);
         auto bind = [base](DevTiling& d, const TilingOffsets& o) {
             d.tile_seg = reinterpret_cast<uint32_t*>(base + o.ts);
             for (int v = 0; v < adacomp::kVariants; ++v)
@@ -720,12 +740,10 @@ int decode_impl(const adacomp_plan* plan, const void* const* msgs, uint32_t K, f
     {
         if (plan->count_batched)
             hipLaunchKernelGGL(adacomp::k_decode_count<8>, dim3(DC, K), dim3(256), 0, stream, mp,
-                               plan->d_segs, plan->ddt.chunk_tile_begin, plan->ddt.chunk_seg, DT, DC,
-                               geo, dw);
+                               plan->d_cchunks, DT, DC, geo, dw);
         else
             hipLaunchKernelGGL(adacomp::k_decode_count<0>, dim3(DC, K), dim3(256), 0, stream, mp,
-                               plan->d_segs, plan->ddt.chunk_tile_begin, plan->ddt.chunk_seg, DT, DC,
-                               geo, dw);
+                               plan->d_cchunks, DT, DC, geo, dw);
         if ((st = launch_status()) != ADACOMP_OK) return st;
         tm.mark(ADACOMP_STAGE_DECODE_COUNT);
     }

@@ -132,9 +132,8 @@ __device__ __forceinline__ uint32_t sum_count_words_batched(const uint8_t* m, ui
 // tiles hold many count words: dense short bins); NB = 0: one at a time.
 template <int NB>
 __global__ void __launch_bounds__(256)
-k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
-               const uint32_t* __restrict__ chunk_tile_begin, const uint32_t* __restrict__ chunk_seg,
-               uint32_t DT, uint32_t DC, MsgGeom geo, DecodeWs ws) {
+k_decode_count(MsgPtrs msgs, const CountChunk* __restrict__ chunks, uint32_t DT, uint32_t DC,
+               MsgGeom geo, DecodeWs ws) {
     __shared__ uint32_t lw[4];
     __shared__ uint32_t bad;
     const uint32_t c = blockIdx.x, k = blockIdx.y;
@@ -145,8 +144,8 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
     }
     // A message made for another table is never read past its header.
     const bool ok = header_matches(m, geo);
-    const SegDev sg = segs[chunk_seg[c]];
-    const uint32_t tb = chunk_tile_begin[c], n = chunk_tile_begin[c + 1] - tb;
+    const CountChunk cc = chunks[c];
+    const uint32_t tb = cc.tile0, n = cc.ntiles;
     __syncthreads();   // bad is cleared before any thread sets it
     uint32_t cnt[4];
     bool over = false;
@@ -155,14 +154,14 @@ k_decode_count(MsgPtrs msgs, const SegDev* __restrict__ segs,
         const uint32_t t = uint32_t(i) * 256u + threadIdx.x;
         uint32_t s = 0;
         if (ok && t < n) {
-            const uint32_t first_bin = (tb + t - sg.dt.tile_begin) * sg.dt.bpt;
-            const uint32_t nb = min(sg.dt.bpt, sg.nbins - first_bin);
-            const uint64_t a0 = sg.count_off + uint64_t(first_bin) * sg.wb;
-            s = NB > 0 ? sum_count_words_batched<(NB > 0 ? NB : 1)>(m, a0, a0 + uint64_t(nb) * sg.wb, sg.wb)
-                       : sum_count_words(m, a0, a0 + uint64_t(nb) * sg.wb, sg.wb);
+            const uint32_t first_bin = cc.first_bin + t * cc.bpt;
+            const uint32_t nb = min(cc.bpt, cc.nbins - first_bin);
+            const uint64_t a0 = cc.count_off + uint64_t(first_bin) * cc.wb;
+            s = NB > 0 ? sum_count_words_batched<(NB > 0 ? NB : 1)>(m, a0, a0 + uint64_t(nb) * cc.wb, cc.wb)
+                       : sum_count_words(m, a0, a0 + uint64_t(nb) * cc.wb, cc.wb);
             // A tile never sends more elements than it holds.
-            const uint64_t e0 = uint64_t(first_bin) * sg.lt;
-            const uint64_t elems = min(uint64_t(nb) * sg.lt, sg.numel - e0);
+            const uint64_t e0 = uint64_t(first_bin) * cc.lt;
+            const uint64_t elems = min(uint64_t(nb) * cc.lt, cc.numel - e0);
             if (s > elems) {
                 over = true;
                 s = 0;

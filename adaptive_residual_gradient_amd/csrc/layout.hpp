@@ -145,6 +145,22 @@ struct Tiling {
 
 // Everything the decode apply kernel needs about one decode tile, built at
 // plan time in launch order so that a workgroup starts with a single load.
+// What k_decode_count needs of one decode count chunk, read with one load
+// (instead of the chunk's layer index and then the layer's record).
+struct CountChunk {
+    uint64_t count_off;   // message byte offset of the layer's first count word
+    uint64_t numel;       // elements of the layer
+    uint32_t tile0;       // global index of the chunk's first decode tile
+    uint32_t ntiles;      // decode tiles in the chunk
+    uint32_t first_bin;   // the layer's bin index of the chunk's first bin
+    uint32_t bpt;         // bins per decode tile
+    uint32_t nbins;       // bins of the layer
+    uint32_t wb;          // bytes per word
+    uint32_t lt;          // bin length
+    uint32_t pad;
+};
+static_assert(sizeof(CountChunk) == 48, "CountChunk layout");
+
 struct DecDesc {
     uint64_t t0;        // flat index of the tile's first element
     uint64_t count_at;  // message byte offset of the tile's first count word
